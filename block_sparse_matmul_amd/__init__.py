@@ -1,0 +1,225 @@
+"""Block-sparse multi-head attention for AMD MI355X (gfx950).
+
+Python binding of libbsattn.so (include/bsattn.h): argument checks and
+marshalling only; every step runs in the library's HIP kernels. PyTorch
+supplies device memory and the current stream.
+
+    L = Layout(layout_uint8[H, nbr, nbc], block)        # or Layout.acsr(...)
+    S = sdd(L, q, k)                  # [Z, nnz, b, b] float32, S = Q K^T on blocks
+    P = softmax(L, S, scale, causal)  # block-sparse row softmax
+    O = dsd(L, P, v)                  # O = P V
+    C = dds(L, a, S)                  # C = A S
+    O = attention(L, q, k, v, scale, causal)   # fused SDD -> softmax -> DSD
+
+Operation semantics follow the three block-sparse modes and the softmax of
+Triton issue 117 ("question on blocksparse"); see include/bsattn.h.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import math
+from typing import Dict, Optional, Sequence, Tuple
+
+import numpy as np
+
+from . import _lib
+from ._lib import AcsrTerm, BsError, BS_BF16, BS_CAUSAL, BS_F32, check, lib
+
+__all__ = ["Layout", "sdd", "softmax", "dsd", "dds", "attention", "BsError", "lib"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(device) -> C.c_void_p:
+    torch = _torch()
+    return C.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return BS_F32
+    if t.dtype == torch.bfloat16:
+        return BS_BF16
+    raise TypeError(f"dense operands must be float32 or bfloat16, got {t.dtype}")
+
+
+def _check_dense(name, t, ndim=4):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got {tuple(t.shape)}")
+
+
+def _ptr(t) -> C.c_void_p:
+    return C.c_void_p(t.data_ptr() if t is not None and t.numel() > 0 else 0)
+
+
+class Layout:
+    """A built block layout: device block-CSR/CSC tables (owned by the library)."""
+
+    def __init__(self, layout, block: int, device=None, _handle=None):
+        torch = _torch()
+        if _handle is not None:
+            self._h = _handle
+        else:
+            if not torch.cuda.is_available():
+                raise RuntimeError("Layout needs a visible GPU (HIP device)")
+            lay = torch.as_tensor(np.asarray(layout) if not isinstance(layout, torch.Tensor) else layout)
+            if lay.dim() != 3:
+                raise ValueError("layout must be [H, nbr, nbc]")
+            dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+            lay = lay.to(device=dev, dtype=torch.uint8).contiguous()
+            H, nbr, nbc = lay.shape
+            h = C.c_void_p()
+            with torch.cuda.device(dev):
+                check(lib().bs_layout_build(_ptr(lay), H, nbr, nbc, block, _stream(dev), C.byref(h)))
+            self._h = h
+        self._read_info()
+
+    @classmethod
+    def acsr(cls, terms: Sequence[Tuple[int, int, int, int, int, int]], H: int, nbr: int, nbc: int,
+             block: int, device=None) -> "Layout":
+        """Layout from affine row terms (row_begin, row_end, slope, offset,
+        stride, count), the same for every head."""
+        torch = _torch()
+        if not torch.cuda.is_available():
+            raise RuntimeError("Layout needs a visible GPU (HIP device)")
+        arr = (AcsrTerm * max(1, len(terms)))()
+        for i, t in enumerate(terms):
+            arr[i] = AcsrTerm(*[int(v) for v in t])
+        dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+        h = C.c_void_p()
+        with torch.cuda.device(dev):
+            check(lib().bs_layout_build_acsr(arr, len(terms), H, nbr, nbc, block, _stream(dev), C.byref(h)))
+        return cls(None, block, _handle=h)
+
+    def _read_info(self):
+        H, nbr, nbc, b = C.c_int(), C.c_int(), C.c_int(), C.c_int()
+        nnz = C.c_int64()
+        check(lib().bs_layout_info(self._h, C.byref(H), C.byref(nbr), C.byref(nbc), C.byref(b), C.byref(nnz)))
+        self.H, self.nbr, self.nbc, self.block, self.nnz = H.value, nbr.value, nbc.value, b.value, nnz.value
+
+    @property
+    def handle(self) -> C.c_void_p:
+        if self._h is None:
+            raise RuntimeError("layout was freed")
+        return self._h
+
+    def export(self) -> Dict[str, np.ndarray]:
+        """Copy the tables to host numpy int32 arrays."""
+        n = self.nnz
+        out = {
+            "row_ptr": np.zeros(self.H * self.nbr + 1, np.int32),
+            "col_idx": np.zeros(n, np.int32),
+            "col_ptr": np.zeros(self.H * self.nbc + 1, np.int32),
+            "row_idx": np.zeros(n, np.int32),
+            "blk_id": np.zeros(n, np.int32),
+        }
+        ptrs = [a.ctypes.data_as(C.POINTER(C.c_int32)) for a in out.values()]
+        check(lib().bs_layout_export(self.handle, *ptrs))
+        return out
+
+    def free(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib().bs_layout_free(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def _empty(shape, dtype, device):
+    return _torch().empty(shape, dtype=dtype, device=device)
+
+
+def sdd(L: Layout, a, b, out=None):
+    """S[z, k] = a[z, h, r-block, :] @ b[z, h, c-block, :]^T for each stored block."""
+    torch = _torch()
+    _check_dense("a", a)
+    _check_dense("b", b)
+    Z, H, Na, K = a.shape
+    if a.dtype != b.dtype or b.shape != (Z, H, L.nbc * L.block, K) or (H, Na) != (L.H, L.nbr * L.block):
+        raise ValueError("a must be [Z, H, nbr*b, K] and b [Z, H, nbc*b, K] of one dtype")
+    if out is None:
+        out = _empty((Z, L.nnz, L.block, L.block), torch.float32, a.device)
+    elif out.shape != (Z, L.nnz, L.block, L.block) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [Z, nnz, b, b] tensor")
+    check(lib().bs_sdd(L.handle, _ptr(a), _ptr(b), _ptr(out), Z, K, _dtype_code(a), _stream(a.device)))
+    return out
+
+
+def softmax(L: Layout, s, scale: float, causal: bool = False, out=None, inplace: bool = False):
+    """Block-sparse row softmax of SDD output (scale, then causal mask)."""
+    torch = _torch()
+    _check_dense("s", s)
+    if s.dtype != torch.float32 or s.shape[1:] != (L.nnz, L.block, L.block):
+        raise ValueError("s must be float32 [Z, nnz, b, b]")
+    if inplace:
+        out = s
+    elif out is None:
+        out = torch.empty_like(s)
+    check(lib().bs_softmax(L.handle, _ptr(s), _ptr(out), s.shape[0], float(scale),
+                           BS_CAUSAL if causal else 0, _stream(s.device)))
+    return out
+
+
+def dsd(L: Layout, p, b, out=None):
+    """C[z, h, r-block, :] = sum over stored (h, r, c) of p[z, k] @ b[z, h, c-block, :]."""
+    torch = _torch()
+    _check_dense("p", p)
+    _check_dense("b", b)
+    Z, H, Nb, Nd = b.shape
+    if p.dtype != torch.float32 or p.shape != (Z, L.nnz, L.block, L.block):
+        raise ValueError("p must be float32 [Z, nnz, b, b]")
+    if (H, Nb) != (L.H, L.nbc * L.block):
+        raise ValueError("b must be [Z, H, nbc*b, Nd]")
+    if out is None:
+        out = _empty((Z, H, L.nbr * L.block, Nd), b.dtype, b.device)
+    check(lib().bs_dsd(L.handle, _ptr(p), _ptr(b), _ptr(out), Z, Nd, _dtype_code(b), _stream(b.device)))
+    return out
+
+
+def dds(L: Layout, a, s, out=None):
+    """C[z, h, :, c-block] = sum over stored (h, r, c) of a[z, h, :, r-block] @ s[z, k]."""
+    torch = _torch()
+    _check_dense("a", a)
+    _check_dense("s", s)
+    Z, H, M, Na = a.shape
+    if s.dtype != torch.float32 or s.shape != (Z, L.nnz, L.block, L.block):
+        raise ValueError("s must be float32 [Z, nnz, b, b]")
+    if (H, Na) != (L.H, L.nbr * L.block):
+        raise ValueError("a must be [Z, H, M, nbr*b]")
+    if out is None:
+        out = _empty((Z, H, M, L.nbc * L.block), a.dtype, a.device)
+    check(lib().bs_dds(L.handle, _ptr(a), _ptr(s), _ptr(out), Z, M, _dtype_code(a), _stream(a.device)))
+    return out
+
+
+def attention(L: Layout, q, k, v, scale: Optional[float] = None, causal: bool = False, out=None):
+    """Fused block-sparse attention O = softmax(scale q k^T + mask) v."""
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check_dense(n, t)
+    Z, H, Nq, d = q.shape
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share a dtype")
+    if (H, Nq) != (L.H, L.nbr * L.block) or k.shape != (Z, H, L.nbc * L.block, d) or v.shape != k.shape:
+        raise ValueError("q must be [Z, H, nbr*b, d]; k, v [Z, H, nbc*b, d]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = _empty(q.shape, q.dtype, q.device)
+    check(lib().bs_attention(L.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(out), Z, d, float(scale),
+                             BS_CAUSAL if causal else 0, _dtype_code(q), _stream(q.device)))
+    return out

@@ -1,0 +1,288 @@
+// C-ABI entry points: argument validation (before any HIP call), handle
+// management, and dispatch to the kernel launchers. The operations and their
+// meaning are documented in include/bsattn.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <limits>
+#include <string>
+
+#include "internal.h"
+
+namespace bsa {
+
+static thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  if (log_enabled()) fprintf(stderr, "[bsattn] error %d: %s\n", code, msg.c_str());
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  const bool oom = (e == hipErrorOutOfMemory);
+  return fail(oom ? BS_ERR_OOM : BS_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool log_enabled() {
+  static const bool on = [] {
+    const char* v = getenv("BS_LOG");
+    return v && v[0] && v[0] != '0';
+  }();
+  return on;
+}
+
+}  // namespace bsa
+
+using bsa::fail;
+
+namespace {
+
+bool block_ok(int b) { return b == 16 || b == 32 || b == 64 || b == 128; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_handle(bs_layout_t L) {
+  if (!L) return fail(BS_ERR_INVALID_ARG, "layout handle is NULL");
+  return BS_OK;
+}
+
+int check_dims(int H, int nbr, int nbc, int block) {
+  if (!block_ok(block)) return fail(BS_ERR_UNSUPPORTED, "block must be 16, 32, 64 or 128");
+  if (H <= 0 || nbr <= 0 || nbc <= 0) return fail(BS_ERR_INVALID_ARG, "H, nbr and nbc must be positive");
+  const int64_t cells = (int64_t)H * nbr * nbc;
+  if (cells > std::numeric_limits<int32_t>::max() || (int64_t)nbr * block > std::numeric_limits<int32_t>::max() ||
+      (int64_t)nbc * block > std::numeric_limits<int32_t>::max())
+    return fail(BS_ERR_SHAPE, "layout too large for 32-bit block indices");
+  return BS_OK;
+}
+
+int check_dtype(bs_dtype dt) {
+  if (dt != BS_F32 && dt != BS_BF16) return fail(BS_ERR_INVALID_ARG, "dtype must be BS_F32 or BS_BF16");
+  return BS_OK;
+}
+
+int current_device_ok() {
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n == 0) {
+    (void)hipGetLastError();
+    return fail(BS_ERR_NO_DEVICE, "no HIP device is visible");
+  }
+  return BS_OK;
+}
+
+// Tensor pointers used by a compute call: non-NULL and 16-byte aligned
+// whenever there is work to do.
+int check_ptrs(bool work, std::initializer_list<const void*> ptrs) {
+  if (!work) return BS_OK;
+  for (const void* p : ptrs) {
+    if (!p) return fail(BS_ERR_INVALID_ARG, "tensor pointer is NULL");
+    if (!aligned16(p)) return fail(BS_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  }
+  return BS_OK;
+}
+
+void log_call(const char* name, const bs_layout* L, int Z, int x) {
+  if (bsa::log_enabled())
+    fprintf(stderr, "[bsattn] %s H=%d nbr=%d nbc=%d b=%d nnz=%lld Z=%d dim=%d\n", name, L->H, L->nbr, L->nbc,
+            L->block, (long long)L->nnz, Z, x);
+}
+
+int finish_build(bs_layout* L, const uint8_t* layout, hipStream_t s, bs_layout_t* out) {
+  const int rc = bsa::build_tables(L, layout, s);
+  if (rc != BS_OK) {
+    delete L;
+    return rc;
+  }
+  *out = L;
+  return BS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bs_version(void) { return 100; }
+
+const char* bs_last_error(void) { return bsa::g_last_error.c_str(); }
+
+int bs_layout_build(const uint8_t* layout, int H, int nbr, int nbc, int block, void* stream, bs_layout_t* out) {
+  if (!out) return fail(BS_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  int rc = check_dims(H, nbr, nbc, block);
+  if (rc) return rc;
+  if (!layout) return fail(BS_ERR_INVALID_ARG, "layout pointer is NULL");
+  if ((rc = current_device_ok())) return rc;
+  bs_layout* L = new bs_layout();
+  L->H = H;
+  L->nbr = nbr;
+  L->nbc = nbc;
+  L->block = block;
+  if (hipGetDevice(&L->device) != hipSuccess) {
+    delete L;
+    return fail(BS_ERR_HIP, "hipGetDevice failed");
+  }
+  if (bsa::log_enabled()) fprintf(stderr, "[bsattn] layout_build H=%d nbr=%d nbc=%d b=%d\n", H, nbr, nbc, block);
+  return finish_build(L, layout, (hipStream_t)stream, out);
+}
+
+int bs_layout_build_acsr(const bs_acsr_term* terms, int n_terms, int H, int nbr, int nbc, int block, void* stream,
+                         bs_layout_t* out) {
+  if (!out) return fail(BS_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  int rc = check_dims(H, nbr, nbc, block);
+  if (rc) return rc;
+  if (n_terms < 0 || (n_terms > 0 && !terms)) return fail(BS_ERR_INVALID_ARG, "terms pointer is NULL");
+  for (int t = 0; t < n_terms; ++t) {
+    if (terms[t].row_begin > terms[t].row_end || terms[t].count < 0)
+      return fail(BS_ERR_INVALID_ARG, "ACSR term needs row_begin <= row_end and count >= 0");
+  }
+  if ((rc = current_device_ok())) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  const size_t cells = (size_t)H * nbr * nbc;
+  uint8_t* lay = nullptr;
+  bs_acsr_term* dterms = nullptr;
+  if (hipMalloc(&lay, cells) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(BS_ERR_OOM, "hipMalloc of the expanded layout failed");
+  }
+  if (n_terms > 0 && hipMalloc(&dterms, sizeof(bs_acsr_term) * n_terms) != hipSuccess) {
+    (void)hipGetLastError();
+    (void)hipFree(lay);
+    return fail(BS_ERR_OOM, "hipMalloc of the ACSR terms failed");
+  }
+  hipError_t e = hipSuccess;
+  if (n_terms > 0)
+    e = hipMemcpyAsync(dterms, terms, sizeof(bs_acsr_term) * n_terms, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) rc = bsa::expand_acsr(dterms, n_terms, H, nbr, nbc, lay, s);
+  else rc = bsa::hip_fail(e, "hipMemcpyAsync(ACSR terms)");
+  if (rc == BS_OK) {
+    bs_layout* L = new bs_layout();
+    L->H = H;
+    L->nbr = nbr;
+    L->nbc = nbc;
+    L->block = block;
+    (void)hipGetDevice(&L->device);
+    rc = finish_build(L, lay, s, out);  // synchronises s before returning
+  } else {
+    (void)hipStreamSynchronize(s);
+  }
+  (void)hipFree(dterms);
+  (void)hipFree(lay);
+  return rc;
+}
+
+int bs_layout_info(bs_layout_t L, int* H, int* nbr, int* nbc, int* block, int64_t* nnz) {
+  if (int rc = check_handle(L)) return rc;
+  if (H) *H = L->H;
+  if (nbr) *nbr = L->nbr;
+  if (nbc) *nbc = L->nbc;
+  if (block) *block = L->block;
+  if (nnz) *nnz = L->nnz;
+  return BS_OK;
+}
+
+int bs_layout_export(bs_layout_t L, int32_t* row_ptr, int32_t* col_idx, int32_t* col_ptr, int32_t* row_idx,
+                     int32_t* blk_id) {
+  if (int rc = check_handle(L)) return rc;
+  struct Item {
+    int32_t* dst;
+    const int32_t* src;
+    int64_t n;
+  } items[] = {{row_ptr, L->row_ptr, (int64_t)L->H * L->nbr + 1},
+               {col_idx, L->col_idx, L->nnz},
+               {col_ptr, L->col_ptr, (int64_t)L->H * L->nbc + 1},
+               {row_idx, L->row_idx, L->nnz},
+               {blk_id, L->blk_id, L->nnz}};
+  for (const Item& it : items) {
+    if (!it.dst || it.n == 0) continue;
+    BSA_HIP(hipMemcpy(it.dst, it.src, sizeof(int32_t) * it.n, hipMemcpyDeviceToHost));
+  }
+  return BS_OK;
+}
+
+void bs_layout_free(bs_layout_t L) {
+  if (!L) return;
+  if (L->col_idx) (void)hipFree(L->col_idx);  // start of the nnz allocation
+  if (L->mem) (void)hipFree(L->mem);
+  delete L;
+}
+
+int bs_sdd(bs_layout_t L, const void* A, const void* B, float* S, int Z, int K, bs_dtype dt, void* stream) {
+  if (int rc = check_handle(L)) return rc;
+  if (int rc = check_dtype(dt)) return rc;
+  if (Z < 0 || K <= 0) return fail(BS_ERR_INVALID_ARG, "Z must be >= 0 and K > 0");
+  if (K % 16) return fail(BS_ERR_UNSUPPORTED, "K must be a multiple of 16");
+  const bool work = Z > 0 && L->nnz > 0;
+  if (int rc = check_ptrs(work, {A, B, S})) return rc;
+  if (!work) return BS_OK;
+  if ((int64_t)Z * L->nnz * L->block * L->block > ((int64_t)1 << 46))
+    return fail(BS_ERR_SHAPE, "block-sparse tensor too large");
+  log_call("sdd", L, Z, K);
+  return bsa::launch_sdd(L, A, B, S, Z, K, dt, (hipStream_t)stream);
+}
+
+int bs_softmax(bs_layout_t L, const float* S, float* P, int Z, float scale, int flags, void* stream) {
+  if (int rc = check_handle(L)) return rc;
+  if (flags & ~BS_CAUSAL) return fail(BS_ERR_INVALID_ARG, "unknown flag");
+  if (Z < 0) return fail(BS_ERR_INVALID_ARG, "Z must be >= 0");
+  const bool causal = flags & BS_CAUSAL;
+  if (causal && L->nbr != L->nbc) return fail(BS_ERR_INVALID_ARG, "causal softmax needs a square layout");
+  const bool work = Z > 0 && L->nnz > 0;
+  if (int rc = check_ptrs(work, {S, P})) return rc;
+  if (!work) return BS_OK;
+  if ((int64_t)L->H * L->nbr * L->block > std::numeric_limits<int32_t>::max() - 4)
+    return fail(BS_ERR_SHAPE, "too many query rows");
+  log_call("softmax", L, Z, flags);
+  return bsa::launch_softmax(L, S, P, Z, scale, causal, (hipStream_t)stream);
+}
+
+int bs_dsd(bs_layout_t L, const float* P, const void* B, void* C, int Z, int Nd, bs_dtype dt, void* stream) {
+  if (int rc = check_handle(L)) return rc;
+  if (int rc = check_dtype(dt)) return rc;
+  if (Z < 0 || Nd <= 0) return fail(BS_ERR_INVALID_ARG, "Z must be >= 0 and Nd > 0");
+  if (Nd % 16) return fail(BS_ERR_UNSUPPORTED, "Nd must be a multiple of 16");
+  const bool work = Z > 0;
+  if (int rc = check_ptrs(work, {B, C})) return rc;
+  if (work && L->nnz > 0) {
+    if (int rc = check_ptrs(true, {P})) return rc;
+  }
+  if (!work) return BS_OK;
+  log_call("dsd", L, Z, Nd);
+  return bsa::launch_dsd(L, P, B, C, Z, Nd, dt, (hipStream_t)stream);
+}
+
+int bs_dds(bs_layout_t L, const void* A, const float* S, void* C, int Z, int M, bs_dtype dt, void* stream) {
+  if (int rc = check_handle(L)) return rc;
+  if (int rc = check_dtype(dt)) return rc;
+  if (Z < 0 || M <= 0) return fail(BS_ERR_INVALID_ARG, "Z must be >= 0 and M > 0");
+  if (M % 16) return fail(BS_ERR_UNSUPPORTED, "M must be a multiple of 16");
+  const bool work = Z > 0;
+  if (int rc = check_ptrs(work, {A, C})) return rc;
+  if (work && L->nnz > 0) {
+    if (int rc = check_ptrs(true, {S})) return rc;
+  }
+  if (!work) return BS_OK;
+  log_call("dds", L, Z, M);
+  return bsa::launch_dds(L, A, S, C, Z, M, dt, (hipStream_t)stream);
+}
+
+int bs_attention(bs_layout_t L, const void* Q, const void* K, const void* V, void* O, int Z, int d, float scale,
+                 int flags, bs_dtype dt, void* stream) {
+  if (int rc = check_handle(L)) return rc;
+  if (int rc = check_dtype(dt)) return rc;
+  if (flags & ~BS_CAUSAL) return fail(BS_ERR_INVALID_ARG, "unknown flag");
+  if (Z < 0) return fail(BS_ERR_INVALID_ARG, "Z must be >= 0");
+  if (d != 64 && d != 128) return fail(BS_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  const bool causal = flags & BS_CAUSAL;
+  if (causal && L->nbr != L->nbc) return fail(BS_ERR_INVALID_ARG, "causal attention needs a square layout");
+  const bool work = Z > 0;
+  if (int rc = check_ptrs(work, {Q, K, V, O})) return rc;
+  if (!work) return BS_OK;
+  log_call("attention", L, Z, d);
+  return bsa::launch_attention(L, Q, K, V, O, Z, d, scale, causal, dt, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// Internal declarations shared by the C-ABI layer (api.cpp) and the kernel
+// translation units. Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "../../include/bsattn.h"
+
+// Device-resident tables of one layout. One allocation (`mem`) holds every
+// array; all are int32.
+struct bs_layout {
+  int device = 0;
+  int H = 0, nbr = 0, nbc = 0, block = 0;
+  int64_t nnz = 0;
+  int max_row_len = 0;  // longest block row (blocks)
+  int max_col_len = 0;  // longest block column (blocks)
+  void* mem = nullptr;
+  int32_t* row_ptr = nullptr;    // [H*nbr + 1]
+  int32_t* col_idx = nullptr;    // [nnz]
+  int32_t* col_ptr = nullptr;    // [H*nbc + 1]
+  int32_t* row_idx = nullptr;    // [nnz]
+  int32_t* blk_id = nullptr;     // [nnz]
+  int32_t* row_order = nullptr;  // [H*nbr] block rows, longest first
+  int32_t* col_order = nullptr;  // [H*nbc] block columns, longest first
+};
+
+namespace bsa {
+
+// error reporting (thread-local message, see bs_last_error)
+int fail(int code, const std::string& msg);
+int hip_fail(hipError_t e, const char* what);
+
+#define BSA_HIP(call)                                   \
+  do {                                                  \
+    hipError_t e_ = (call);                             \
+    if (e_ != hipSuccess) return ::bsa::hip_fail(e_, #call); \
+  } while (0)
+
+// ---- LUT builder (lut.hip) ----
+// Builds every table of `L` from a device 0/1 layout. L's sizes are set by
+// the caller; on success L->mem and the table pointers are set.
+int build_tables(bs_layout* L, const uint8_t* layout_dev, hipStream_t s);
+// Expands ACSR terms (device array) into a dense device layout.
+int expand_acsr(const bs_acsr_term* terms_dev, int n_terms, int H, int nbr,
+                int nbc, uint8_t* layout_dev, hipStream_t s);
+
+// ---- operator launchers (one per translation unit) ----
+int launch_sdd(const bs_layout* L, const void* A, const void* B, float* S,
+               int Z, int K, bs_dtype dt, hipStream_t s);
+int launch_softmax(const bs_layout* L, const float* S, float* P, int Z,
+                   float scale, bool causal, hipStream_t s);
+int launch_dsd(const bs_layout* L, const float* P, const void* B, void* C,
+               int Z, int Nd, bs_dtype dt, hipStream_t s);
+int launch_dds(const bs_layout* L, const void* A, const float* S, void* C,
+               int Z, int M, bs_dtype dt, hipStream_t s);
+int launch_attention(const bs_layout* L, const void* Q, const void* K,
+                     const void* V, void* O, int Z, int d, float scale,
+                     bool causal, bs_dtype dt, hipStream_t s);
+
+bool log_enabled();
+
+}  // namespace bsa

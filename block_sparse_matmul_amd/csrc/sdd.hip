@@ -1,0 +1,88 @@
+// SDD: sampled dense-dense product (Triton issue 117, "question on
+// blocksparse": sparse = dense x dense, the first of the three modes).
+// For every stored block k = (h, r, c):
+//   S[z, k] = A[z, h, r-block, :] . B[z, h, c-block, :]^T      (fp32 out)
+//
+// One workgroup (4 waves) per (batch, block row), block rows taken longest
+// first. The row's output tiles (T x T, T = min(block, 32)) are dealt to the
+// waves; each tile is one MFMA accumulation over K with both operands read
+// as 16-byte row vectors (A rows are query rows, B rows are key rows), and
+// the tile is stored row by row (T consecutive floats per row).
+#include "internal.h"
+#include "tile.h"
+
+namespace bsa {
+namespace {
+
+template <typename E, int BLK, int T>
+__global__ __launch_bounds__(256) void k_sdd(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
+                                             const int32_t* __restrict__ row_order,
+                                             const typename Elem<E>::storage* __restrict__ A,
+                                             const typename Elem<E>::storage* __restrict__ B, float* __restrict__ S,
+                                             int H, int nbr, int nbc, int K, int64_t nnz) {
+  using St = typename Elem<E>::storage;
+  using AccT = typename Acc<T>::type;
+  constexpr int G = 64 / T, VEC = Elem<E>::VEC, KC = G * VEC, TPB = BLK / T, NR = T * T / 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int li = lane % T, g = lane / T;
+  const int hr = row_order[blockIdx.x];
+  const int z = blockIdx.y;
+  const int h = hr / nbr, r = hr % nbr;
+  const int k0 = row_ptr[hr], k1 = row_ptr[hr + 1];
+  const int items = (k1 - k0) * TPB * TPB;
+  const int64_t zh = (int64_t)z * H + h;
+  const St* a_row = A + (zh * nbr * BLK + (int64_t)r * BLK) * K + g * VEC;
+  for (int it = wave; it < items; it += 4) {
+    const int kk = k0 + it / (TPB * TPB);
+    const int t = it % (TPB * TPB);
+    const int ti = t / TPB, tj = t % TPB;
+    const int c = col_idx[kk];
+    const St* pa = a_row + (int64_t)(ti * T + li) * K;
+    const St* pb = B + (zh * nbc * BLK + (int64_t)c * BLK + tj * T + li) * K + g * VEC;
+    AccT acc = {};
+    for (int k = 0; k < K; k += KC) {
+      Frag<E> fa, fb;
+      if (k + g * VEC < K) {
+        fa.load(pa + k);
+        fb.load(pb + k);
+      } else {
+        fa.zero();
+        fb.zero();
+      }
+      mma_frag<T>(acc, fa, fb);
+    }
+    float* ps = S + ((int64_t)z * nnz + kk) * (BLK * BLK) + (ti * T) * BLK + tj * T + li;
+#pragma unroll
+    for (int q = 0; q < NR; ++q) ps[acc_row<T>(q, g) * BLK] = acc[q];
+  }
+}
+
+template <typename E, int BLK>
+int run(const bs_layout* L, const void* A, const void* B, float* S, int Z, int K, hipStream_t s) {
+  using St = typename Elem<E>::storage;
+  constexpr int T = BLK >= 32 ? 32 : 16;
+  hipLaunchKernelGGL((k_sdd<E, BLK, T>), dim3(L->H * L->nbr, Z), dim3(256), 0, s, L->row_ptr, L->col_idx,
+                     L->row_order, (const St*)A, (const St*)B, S, L->H, L->nbr, L->nbc, K, L->nnz);
+  BSA_HIP(hipGetLastError());
+  return BS_OK;
+}
+
+template <typename E>
+int run_e(const bs_layout* L, const void* A, const void* B, float* S, int Z, int K, hipStream_t s) {
+  switch (L->block) {
+    case 16: return run<E, 16>(L, A, B, S, Z, K, s);
+    case 32: return run<E, 32>(L, A, B, S, Z, K, s);
+    case 64: return run<E, 64>(L, A, B, S, Z, K, s);
+    case 128: return run<E, 128>(L, A, B, S, Z, K, s);
+  }
+  return fail(BS_ERR_UNSUPPORTED, "block must be 16, 32, 64 or 128");
+}
+
+}  // namespace
+
+int launch_sdd(const bs_layout* L, const void* A, const void* B, float* S, int Z, int K, bs_dtype dt,
+               hipStream_t s) {
+  return dt == BS_BF16 ? run_e<bf16_t>(L, A, B, S, Z, K, s) : run_e<float>(L, A, B, S, Z, K, s);
+}
+
+}  // namespace bsa

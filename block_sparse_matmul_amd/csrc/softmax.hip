@@ -1,0 +1,160 @@
+// Block-sparse row softmax on SDD output (Triton issue 117, "question on
+// blocksparse": it reduces the rows of the SDD output and is the same as
+// full-attention softmax; a dense causal mask covers the triangle inside
+// diagonal blocks).
+//
+// For query row i of block row r: x = scale * S over the stored blocks of
+// the row (causal: -inf where key c*b+j > query r*b+i), P = exp(x - max) /
+// sum exp(x - max), zeros when nothing is visible. exp is evaluated as
+// exp2(x * log2(e)) on the hardware's base-2 exponential (the identity the
+// Triton tutorial's Puzzle 8 uses).
+//
+// One wave per query row. The row's stored entries (len blocks x b floats,
+// b contiguous floats per block) are read as 16-byte vectors, 256 floats per
+// wave pass, and kept in registers (up to R vectors per lane) between the
+// max/sum pass and the write pass, so an in-register row costs one read and
+// one write of HBM; longer rows are read a second time. Cross-lane max and
+// sum use butterfly shuffles. P may alias S: each vector is read before the
+// same lanes write it.
+#include <math.h>
+
+#include "internal.h"
+#include "tile.h"
+
+namespace bsa {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+template <int R, bool CAUSAL>
+__global__ __launch_bounds__(256) void k_softmax(const int32_t* __restrict__ row_ptr,
+                                                 const int32_t* __restrict__ col_idx, const float* S, float* P,
+                                                 int rows, int nbr, int b, int64_t nnz, float c) {
+  const int lane = threadIdx.x & 63;
+  const int qrow = blockIdx.x * 4 + (threadIdx.x >> 6);  // (h, r, i) flattened
+  if (qrow >= rows * b) return;
+  const int z = blockIdx.y;
+  const int hr = qrow / b, i = qrow % b;
+  const int r = hr % nbr;
+  const int k0 = row_ptr[hr], k1 = row_ptr[hr + 1];
+  const int n = (k1 - k0) * b;  // stored entries of this row
+  const int64_t zbase = (int64_t)z * nnz;
+  const int q_index = r * b + i;
+  const float NEG = -INFINITY;
+
+  auto addr = [&](int e) -> int64_t {  // element e of the row -> offset in S
+    const int kl = e / b, j = e % b;
+    return ((zbase + k0 + kl) * b + i) * (int64_t)b + j;
+  };
+  auto load = [&](int e) -> f32x4 {  // scaled, masked values of entries e..e+3
+    f32x4 x = {NEG, NEG, NEG, NEG};
+    if (e < n) {
+      x = *reinterpret_cast<const f32x4*>(S + addr(e));
+      x *= c;
+      if (CAUSAL) {
+        const int kl = e / b, j = e % b;
+        const int key = col_idx[k0 + kl] * b + j;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (key + q > q_index) x[q] = NEG;
+      }
+    }
+    return x;
+  };
+
+  f32x4 cache[R];
+  const int passes = (n + 255) / 256;
+  float m = NEG;
+#pragma unroll
+  for (int p = 0; p < R; ++p) {
+    if (p < passes) {
+      cache[p] = load(p * 256 + lane * 4);
+      m = fmaxf(m, fmaxf(fmaxf(cache[p][0], cache[p][1]), fmaxf(cache[p][2], cache[p][3])));
+    }
+  }
+  for (int p = R; p < passes; ++p) {
+    const f32x4 x = load(p * 256 + lane * 4);
+    m = fmaxf(m, fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+  }
+  m = wave_max(m);
+  if (m == NEG) {  // nothing visible (empty row, or every entry masked)
+    for (int p = 0; p < passes; ++p) {
+      const int e = p * 256 + lane * 4;
+      if (e < n) *reinterpret_cast<f32x4*>(P + addr(e)) = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    return;
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int p = 0; p < R; ++p) {
+    if (p < passes) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        cache[p][q] = exp2f(cache[p][q] - m);
+        s += cache[p][q];
+      }
+    }
+  }
+  for (int p = R; p < passes; ++p) {
+    const f32x4 x = load(p * 256 + lane * 4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s += exp2f(x[q] - m);
+  }
+  const float inv = 1.0f / wave_sum(s);
+#pragma unroll
+  for (int p = 0; p < R; ++p) {
+    const int e = p * 256 + lane * 4;
+    if (p < passes && e < n) *reinterpret_cast<f32x4*>(P + addr(e)) = cache[p] * inv;
+  }
+  for (int p = R; p < passes; ++p) {
+    const int e = p * 256 + lane * 4;
+    f32x4 x = load(e);
+    if (e < n) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) x[q] = exp2f(x[q] - m) * inv;
+      *reinterpret_cast<f32x4*>(P + addr(e)) = x;
+    }
+  }
+}
+
+template <int R>
+void launch_r(const bs_layout* L, const float* S, float* P, int Z, float c, bool causal, hipStream_t s) {
+  const int rows = L->H * L->nbr;
+  const dim3 grid((unsigned)(((int64_t)rows * L->block + 3) / 4), Z);
+  if (causal)
+    hipLaunchKernelGGL((k_softmax<R, true>), grid, dim3(256), 0, s, L->row_ptr, L->col_idx, S, P, rows, L->nbr,
+                       L->block, L->nnz, c);
+  else
+    hipLaunchKernelGGL((k_softmax<R, false>), grid, dim3(256), 0, s, L->row_ptr, L->col_idx, S, P, rows, L->nbr,
+                       L->block, L->nnz, c);
+}
+
+}  // namespace
+
+int launch_softmax(const bs_layout* L, const float* S, float* P, int Z, float scale, bool causal, hipStream_t s) {
+  const int64_t longest = (int64_t)L->max_row_len * L->block;  // floats in the longest row
+  const float c = scale * kLog2e;
+  if (longest <= 4 * 256)
+    launch_r<4>(L, S, P, Z, c, causal, s);
+  else if (longest <= 8 * 256)
+    launch_r<8>(L, S, P, Z, c, causal, s);
+  else if (longest <= 16 * 256)
+    launch_r<16>(L, S, P, Z, c, causal, s);
+  else
+    launch_r<32>(L, S, P, Z, c, causal, s);
+  BSA_HIP(hipGetLastError());
+  return BS_OK;
+}
+
+}  // namespace bsa

@@ -1,0 +1,118 @@
+// MFMA tile helpers for gfx950 (CDNA4, wave64).
+//
+// A tile is T x T with T = 32 (v_mfma_f32_32x32x2_f32 / _32x32x16_bf16) or
+// T = 16 (v_mfma_f32_16x16x4_f32 / _16x16x32_bf16). The lanes of a wave form
+// G = 64 / T groups of T lanes; lane l is "column" l % T of group l / T.
+//
+// Operand layout (both A [M x K] and B [K x N]): lane l supplies the row
+// (A) or column (B) l % T, and KL consecutive k values of group g = l / T,
+// where KL = 1 for fp32 and KL = 8 for bf16. A contraction is free to
+// permute k as long as A and B use the same permutation, so the kernels
+// pair each lane's 16-byte vector loads with the k values of several
+// instructions.
+//
+// Accumulator layout: lane l holds column l % T; register r holds row
+// acc_row<T>(r, g) = 4*G*(r/4) + 4*g + (r%4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16;
+
+struct bf16_t {};  // tag for the bf16 element type (stored as 16-bit words)
+
+template <int T>
+struct Acc;
+template <>
+struct Acc<32> { typedef f32x16 type; };
+template <>
+struct Acc<16> { typedef f32x4 type; };
+
+template <int T>
+__device__ __forceinline__ constexpr int acc_row(int r, int g) {
+  return 4 * (64 / T) * (r / 4) + 4 * g + (r % 4);
+}
+
+__device__ __forceinline__ void mma(f32x16& c, float a, float b) {
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4& c, float a, float b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x16& c, bf16x8 a, bf16x8 b) {
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4& c, bf16x8 a, bf16x8 b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// round-to-nearest-even float -> bf16 (v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
+__device__ __forceinline__ float from_bf16(u16 x) { return __uint_as_float((uint32_t)x << 16); }
+__device__ __forceinline__ u16 bf16_bits(float x) {
+  __bf16 h = (__bf16)x;
+  return __builtin_bit_cast(u16, h);
+}
+
+// element type traits: fp32 (KL = 1, 4 floats per 16-byte load) and bf16
+// (KL = 8, one 16-byte load feeds one instruction)
+template <typename E>
+struct Elem;
+template <>
+struct Elem<float> {
+  static constexpr int VEC = 4;   // elements per 16-byte lane load
+  static constexpr int KL = 1;    // k values per lane per instruction
+  typedef float storage;
+};
+template <>
+struct Elem<bf16_t> {
+  static constexpr int VEC = 8;
+  static constexpr int KL = 8;
+  typedef u16 storage;
+};
+
+// 16-byte operand fragment of one lane, as the MFMA wants it
+template <typename E>
+struct Frag;
+template <>
+struct Frag<float> {
+  f32x4 v;
+  __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const f32x4*>(p); }
+  __device__ __forceinline__ void zero() { v = f32x4{0.f, 0.f, 0.f, 0.f}; }
+};
+template <>
+struct Frag<bf16_t> {
+  bf16x8 v;
+  __device__ __forceinline__ void load(const u16* p) { v = *reinterpret_cast<const bf16x8*>(p); }
+  __device__ __forceinline__ void zero() {
+    const __bf16 z = (__bf16)0.f;
+    v = bf16x8{z, z, z, z, z, z, z, z};
+  }
+};
+
+// acc += A-frag x B-frag over the 16 bytes each lane holds
+template <int T>
+__device__ __forceinline__ void mma_frag(typename Acc<T>::type& c, const Frag<float>& a, const Frag<float>& b) {
+  mma(c, a.v[0], b.v[0]);
+  mma(c, a.v[1], b.v[1]);
+  mma(c, a.v[2], b.v[2]);
+  mma(c, a.v[3], b.v[3]);
+}
+template <int T>
+__device__ __forceinline__ void mma_frag(typename Acc<T>::type& c, const Frag<bf16_t>& a, const Frag<bf16_t>& b) {
+  mma(c, a.v, b.v);
+}
+
+// store one output element of type E from a float accumulator value
+__device__ __forceinline__ void store_elem(float* p, float x) { *p = x; }
+__device__ __forceinline__ void store_elem(u16* p, float x) { *p = bf16_bits(x); }
+
+}  // namespace bsa

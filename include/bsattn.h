@@ -1,0 +1,168 @@
+/*
+ * bsattn.h -- block-sparse multi-head attention for AMD MI355X (gfx950).
+ *
+ * The operations are the ones the Triton issue "question on blocksparse"
+ * (openai/triton #117) names for block-sparse matrix products:
+ *   SDD  sparse = dense x dense   (sampled dense-dense product)
+ *   DSD  dense  = sparse x dense  (left operand sparse)
+ *   DDS  dense  = dense x sparse  (right operand sparse)
+ * plus the block-sparse row softmax that runs on the SDD output, and the
+ * attention those three compose (SDD -> softmax -> DSD), here fused into one
+ * kernel. The sparsity layout is a tensor of 0s and 1s, one entry per
+ * non-overlapping square block of 16, 32, 64 or 128 (same answer). Regular
+ * layouts may instead be given in the affine-compressed row form (ACSR) of
+ * the SPLAT abstract (NSF-PAR, Jain).
+ *
+ * Conventions for every call
+ *  - Tensor pointers are DEVICE pointers to contiguous row-major memory on
+ *    the current HIP device, unless a parameter says "host".
+ *  - The caller owns and pre-allocates every tensor. The library allocates
+ *    device memory only inside bs_layout_build*, and frees it in
+ *    bs_layout_free.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Compute calls are asynchronous on it; pointers must stay valid until
+ *    the work completes. bs_layout_build*, bs_layout_export synchronise
+ *    the stream.
+ *  - Every call returns BS_OK (0) or a negative bs_status. Arguments are
+ *    validated before any HIP call is made; bs_last_error() gives the
+ *    message of the last failure on the calling thread.
+ *  - A layout handle is immutable after it is built and may be used from
+ *    several streams and threads at once.
+ *
+ * Shapes (b = block, nnz = number of stored blocks over all heads)
+ *  - layout                 uint8 [H][nbr][nbc], values 0 or 1, one layout
+ *                           per head, shared across the batch Z.
+ *  - block ids              stored blocks enumerated in (head, block-row,
+ *                           block-col) lexicographic order; the k-th gets k.
+ *  - block-sparse tensor    float32 [Z][nnz][b][b]; block k row-major.
+ */
+#ifndef BSATTN_H
+#define BSATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct bs_layout* bs_layout_t;
+
+/* element type of the dense operands (block-sparse tensors are always
+   float32) */
+typedef enum { BS_F32 = 0, BS_BF16 = 1 } bs_dtype;
+
+/* flags for bs_softmax / bs_attention */
+enum { BS_CAUSAL = 1 };
+
+typedef enum {
+  BS_OK = 0,
+  BS_ERR_INVALID_ARG = -1, /* null pointer with work to do, negative size,
+                              causal on a non-square layout, unknown flag */
+  BS_ERR_UNSUPPORTED = -2, /* block not in {16,32,64,128}; head_dim not in
+                              {64,128}; a dimension not a multiple of 16 */
+  BS_ERR_LAYOUT = -3,      /* a layout value other than 0 or 1 */
+  BS_ERR_SHAPE = -4,       /* sizes overflow the 32/64-bit index ranges */
+  BS_ERR_HIP = -5,         /* a HIP runtime call failed */
+  BS_ERR_OOM = -6,         /* device allocation failed */
+  BS_ERR_NO_DEVICE = -7    /* no HIP device is visible */
+} bs_status;
+
+/* One affine row term of an ACSR layout: every block row r in
+   [row_begin, row_end) stores the block columns
+   slope*r + offset + stride*k, k = 0 .. count-1, that fall in [0, nbc).
+   A layout is the union of its terms (SPLAT abstract: affine-compressed
+   sparse rows for the regular geometry of sparse-MHSA patterns). */
+typedef struct {
+  int32_t row_begin, row_end, slope, offset, stride, count;
+} bs_acsr_term;
+
+/* Build a layout handle from a 0/1 layout.
+   layout: DEVICE uint8 [H][nbr][nbc]. block in {16,32,64,128}.
+   On success *out owns device tables: block-CSR (row_ptr, col_idx) over
+   (h, r, c) and CSC (col_ptr, row_idx, blk_id) over (h, c, r), built on the
+   GPU. Errors: BS_ERR_UNSUPPORTED (block), BS_ERR_LAYOUT (a value not 0/1),
+   BS_ERR_INVALID_ARG, BS_ERR_SHAPE, BS_ERR_OOM, BS_ERR_HIP. Synchronises
+   `stream`. *out is NULL on failure. */
+int bs_layout_build(const uint8_t* layout, int H, int nbr, int nbc, int block,
+                    void* stream, bs_layout_t* out);
+
+/* Build a layout handle from ACSR terms (HOST array of n_terms entries),
+   the same pattern for every head. The terms are expanded on the GPU, then
+   the same tables as bs_layout_build are built. Errors as bs_layout_build;
+   a term with row_begin > row_end or count < 0 is BS_ERR_INVALID_ARG. */
+int bs_layout_build_acsr(const bs_acsr_term* terms, int n_terms, int H,
+                         int nbr, int nbc, int block, void* stream,
+                         bs_layout_t* out);
+
+/* Sizes of a handle (any output pointer may be NULL). */
+int bs_layout_info(bs_layout_t L, int* H, int* nbr, int* nbc, int* block,
+                   int64_t* nnz);
+
+/* Copy the tables to HOST buffers (any may be NULL): row_ptr[H*nbr+1],
+   col_idx[nnz], col_ptr[H*nbc+1], row_idx[nnz], blk_id[nnz]. Synchronous. */
+int bs_layout_export(bs_layout_t L, int32_t* row_ptr, int32_t* col_idx,
+                     int32_t* col_ptr, int32_t* row_idx, int32_t* blk_id);
+
+/* Release a handle (NULL is ignored). Call it when no queued work still
+   uses the handle. */
+void bs_layout_free(bs_layout_t L);
+
+/* SDD: S[z,k] = A[z,h,r-block,:] . B[z,h,c-block,:]^T for every stored block
+   k = (h, r, c); the sampled dense-dense product of the issue's first mode,
+   in attention S = Q K^T.
+   A: [Z][H][nbr*b][K], B: [Z][H][nbc*b][K] of dtype dt; S: float32
+   [Z][nnz][b][b]. K > 0 and a multiple of 16. */
+int bs_sdd(bs_layout_t L, const void* A, const void* B, float* S, int Z,
+           int K, bs_dtype dt, void* stream);
+
+/* Block-sparse row softmax (the issue's softmax on SDD output; the same as
+   full-attention softmax over the stored entries). For query row i of
+   block row r of head h, x = scale * S over every stored block (h, r, c);
+   with BS_CAUSAL, entries whose key index c*b+j exceeds the query index
+   r*b+i are -inf (the dense mask inside diagonal blocks). P = exp(x - max) /
+   sum exp(x - max); a row with no visible entry is all zeros.
+   S, P: float32 [Z][nnz][b][b]; P may equal S (in place). BS_CAUSAL needs
+   nbr == nbc. */
+int bs_softmax(bs_layout_t L, const float* S, float* P, int Z, float scale,
+               int flags, void* stream);
+
+/* DSD: C[z,h,r-block,:] = sum over stored (h,r,c) of P[z,k] . B[z,h,c-block,:]
+   (the issue's second mode; in attention O = P V).
+   P: float32 [Z][nnz][b][b]; B: [Z][H][nbc*b][Nd], C: [Z][H][nbr*b][Nd] of
+   dtype dt (bf16: P is rounded to bf16 for the product, C is rounded from
+   the float32 accumulator). Rows with no stored block are written as zero.
+   Nd > 0 and a multiple of 16. */
+int bs_dsd(bs_layout_t L, const float* P, const void* B, void* C, int Z,
+           int Nd, bs_dtype dt, void* stream);
+
+/* DDS: C[z,h,:,c-block] = sum over stored (h,r,c) of A[z,h,:,r-block] . S[z,k]
+   (the issue's third mode; in attention's backward dV^T = dO^T P).
+   A: [Z][H][M][nbr*b], C: [Z][H][M][nbc*b] of dtype dt; S: float32
+   [Z][nnz][b][b]. Columns with no stored block are written as zero.
+   M > 0 and a multiple of 16. */
+int bs_dds(bs_layout_t L, const void* A, const float* S, void* C, int Z,
+           int M, bs_dtype dt, void* stream);
+
+/* Fused block-sparse attention: O = softmax(scale Q K^T + mask) V with the
+   mask of the layout (and BS_CAUSAL), i.e. SDD -> softmax -> DSD in one
+   kernel (the issue's attention composition) with a streaming row softmax
+   (running max and sum, Triton tutorial Puzzles 8 and 9); P never leaves
+   the chip. Q: [Z][H][nbr*b][d], K, V: [Z][H][nbc*b][d], O: [Z][H][nbr*b][d],
+   all of dtype dt; d in {64, 128}. bf16: scores and softmax in float32, P
+   rounded to bf16 for the P.V product, O rounded from float32. Rows with
+   no visible key are zero. */
+int bs_attention(bs_layout_t L, const void* Q, const void* K, const void* V,
+                 void* O, int Z, int d, float scale, int flags, bs_dtype dt,
+                 void* stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* bs_last_error(void);
+
+/* Library ABI version (major*10000 + minor*100 + patch). */
+int bs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSATTN_H */
