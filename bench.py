@@ -1,0 +1,274 @@
+"""Benchmark: block-sparse attention throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one fused block-sparse attention call (SDD -> block-sparse
+softmax -> DSD in the fused kernel) over the whole workload, inputs already
+resident in HBM and the layout tables built once beforehand. The value is
+TFLOP/s over the stored blocks only (4 b^2 d flops per stored block per batch
+element). Rank 0 prints one JSON line with, besides the contract fields:
+  roofline      the fused kernel's achieved TFLOP/s against the MFMA peak of
+                its dtype, timed with HIP events on the stream it runs on;
+                `traffic` is the HBM bytes per launch from rocprofv3 counters
+                (profiles/traffic_<workload>.txt), null if that file is
+                missing or the kernel source changed since it was taken
+  cpu_baseline  the oracle (float64 numpy, per-block route) timed on this
+                host's cores on a bounded sample of block rows
+  ops           the unfused three-call path (SDD, softmax, DSD), the
+                standalone DDS where the workload has one, and the one-time
+                layout build, each timed on its own
+Other modes:
+  --calibrate-copy   a plain 1 GiB device copy (for scaling HBM counters)
+  --all              also print one line per workload to stderr
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "block-sparse attention TFLOP/s on nnz blocks + % of MFMA peak, 1 MI355X"
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}   # MI355X dense MFMA
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "causal_b64"
+
+
+def _events_time(fn, n, stream):
+    """Run fn n times on `stream`; mean ms per call from HIP events recorded
+    on that stream."""
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(n):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / n
+
+
+def _source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+ATTN_SOURCES = ["block_sparse_matmul_amd/csrc/attention.hip", "block_sparse_matmul_amd/csrc/tile.h"]
+
+
+def _traffic(workload, launches_flops):
+    """HBM bytes per launch of the fused kernel from committed counters."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_hash") != _source_hash(ATTN_SOURCES):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, lay, q, k, v, budget_s=12.0, seed=0):
+    """The oracle's per-block route on a seeded random sample of block rows,
+    for about budget_s seconds of CPU time; TFLOP/s over the sampled rows'
+    stored blocks."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    rng = np.random.default_rng(seed)
+    rows = [(z, h, r) for z in range(w.Z) for h in range(w.H) for r in range(w.nb)]
+    order = rng.permutation(len(rows))
+    lens = lay.sum(axis=2)
+    # the oracle converts its inputs to float64 once per call; hand it the
+    # per-head slices it needs so the sample measures the arithmetic
+    done_blocks, n_rows = 0, 0
+    t0 = time.perf_counter()
+    for i in order:
+        z, h, r = rows[i]
+        oracle.attention_blockrow(q[z:z + 1, h:h + 1], k[z:z + 1, h:h + 1], v[z:z + 1, h:h + 1],
+                                  lay[h:h + 1], w.block, w.scale, w.causal, 0, 0, r)
+        done_blocks += int(lens[h, r])
+        n_rows += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    flops = 4 * w.block * w.block * w.d * done_blocks
+    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n_rows} of {len(rows)} block rows of {w.name} ({done_blocks} stored blocks), "
+                      f"oracle per-block route in float64 numpy, {el:.1f} s"}
+
+
+def run_workload(w, steps, warmup, with_ops=True, with_cpu=True):
+    import numpy as np
+    import torch
+
+    import block_sparse_matmul_amd as bsa
+    import workloads as W
+    import oracle
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    lay = W.make_layout(w)
+    qh, kh, vh = W.make_qkv(w)
+    q, k, v = qh.to(dev), kh.to(dev), vh.to(dev)
+
+    t0 = time.perf_counter()
+    if w.pattern == "strided_acsr":
+        L = bsa.Layout.acsr(W.make_acsr(w), w.H, w.nb, w.nb, w.block)
+    else:
+        L = bsa.Layout(torch.from_numpy(lay), w.block)
+    lut_ms = (time.perf_counter() - t0) * 1e3
+    out = torch.empty_like(q)
+    flops = oracle.nnz_flops_attention(L.nnz, w.Z, w.block, w.d)
+
+    def step():
+        bsa.attention(L, q, k, v, w.scale, w.causal, out=out)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    kern_ms = _events_time(step, steps, stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    tflops = flops / (wall_ms * 1e-3) / 1e12
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    traffic = _traffic(w.name, flops)
+    res = {
+        "wall_ms": wall_ms, "kernel_ms": kern_ms, "tflops": tflops, "nnz": L.nnz,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": traffic},
+        "lut_build_ms": round(lut_ms, 3),
+    }
+    if with_ops:
+        ops = {}
+        if True:
+            S = torch.empty((w.Z, L.nnz, w.block, w.block), dtype=torch.float32, device=dev)
+            O2 = torch.empty_like(q)
+            n = max(3, steps // 2)
+            bsa.sdd(L, q, k, out=S)
+            t_sdd = _events_time(lambda: bsa.sdd(L, q, k, out=S), n, stream)
+            t_sm = _events_time(lambda: bsa.softmax(L, S, w.scale, w.causal, out=S), n, stream)
+            t_dsd = _events_time(lambda: bsa.dsd(L, S, v, out=O2), n, stream)
+            sbytes = 4 * w.block * w.block * L.nnz * w.Z
+            ops["unfused"] = {
+                "sdd_ms": round(t_sdd, 4), "softmax_ms": round(t_sm, 4), "dsd_ms": round(t_dsd, 4),
+                "total_ms": round(t_sdd + t_sm + t_dsd, 4),
+                "tflops": round(flops / ((t_sdd + t_sm + t_dsd) * 1e-3) / 1e12, 3),
+                "softmax_gbs": round(2 * sbytes / (t_sm * 1e-3) / 1e9, 1),
+                "softmax_hbm_frac": round(2 * sbytes / (t_sm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            }
+            del S, O2
+        if w.dds_m:
+            A, Sd = W.make_dds_operands(w, L.nnz)
+            A, Sd = A.to(dev), Sd.to(dev)
+            C = torch.empty((w.Z, w.H, w.dds_m, w.N), dtype=A.dtype, device=dev)
+            n = max(3, steps // 2)
+            bsa.dds(L, A, Sd, out=C)
+            t_dds = _events_time(lambda: bsa.dds(L, A, Sd, out=C), n, stream)
+            fd = oracle.nnz_flops_dds(L.nnz, w.Z, w.block, w.dds_m)
+            ops["dds"] = {"ms": round(t_dds, 4), "tflops": round(fd / (t_dds * 1e-3) / 1e12, 3),
+                          "frac": round(fd / (t_dds * 1e-3) / 1e12 / PEAK_TFLOPS[w.dtype], 4), "M": w.dds_m}
+            del A, Sd, C
+        res["ops"] = ops
+    if with_cpu:
+        res["cpu_baseline"] = cpu_baseline(w, lay, qh, kh, vh)
+    return res
+
+
+def calibrate_copy():
+    """A plain device-to-device copy of 1 GiB, 5 times: the reference point
+    for HBM byte counters (expect 1 GiB read + 1 GiB written per copy)."""
+    import torch
+    n = (1 << 30) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n * 4, "copies": 5}))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--all", action="store_true", help="also run every workload (lines on stderr)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
+    ap.add_argument("--no-ops", action="store_true", help="skip the per-op breakdown")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build runs the block-sparse attention kernel on a "
+              "single MI355X (multi-GPU sharding is a design note, not implemented); use --gpus 1",
+              file=sys.stderr)
+        return 2
+    if args.calibrate_copy:
+        calibrate_copy()
+        return 0
+
+    import torch
+    import workloads as W
+    if not torch.cuda.is_available():
+        print("bench.py needs a visible GPU", file=sys.stderr)
+        return 1
+
+    w = W.workload(args.workload)
+    if args.all:
+        for other in W.WORKLOADS:
+            r = run_workload(other, max(5, args.steps // 2), args.warmup, with_ops=not args.no_ops, with_cpu=False)
+            print(json.dumps({"workload": other.name, **{k: r[k] for k in ("kernel_ms", "tflops", "nnz", "roofline",
+                                                                          "ops") if k in r}}),
+                  file=sys.stderr, flush=True)
+    r = run_workload(w, args.steps, args.warmup, with_ops=not args.no_ops, with_cpu=not args.no_cpu)
+    line = {
+        "metric": METRIC,
+        "value": round(r["tflops"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["wall_ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded layouts and N(0,1) Q/K/V, see workloads/)",
+        "config": {"workload": w.name, "Z": w.Z, "H": w.H, "N": w.N, "d": w.d, "block": w.block,
+                   "causal": w.causal, "nnz": r["nnz"], "density": round(r["nnz"] / (w.H * w.nb * w.nb), 4),
+                   "global_batch": w.Z, "seq_len": w.N, "parallelism": "single GPU"},
+        "roofline": r["roofline"],
+        "mfma_peak_frac": r["roofline"]["frac"],
+        "cpu_baseline": r.get("cpu_baseline"),
+        "ops": r.get("ops"),
+        "lut_build_ms": r["lut_build_ms"],
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
