@@ -2,29 +2,41 @@
 // kernel (the composition of Triton issue 117, "question on blocksparse"),
 // with the streaming softmax of the Triton tutorial (Puzzle 8, online
 // softmax; Puzzle 9, simple FlashAttention): a running row max m and sum l,
-// the old partial output rescaled by exp(m_old - m_new) when the max grows,
-// and one division by l at the end (the same value as normalising at every
-// step).
+// the partial output rescaled by exp(m_old - m_new) when the reference max
+// moves, and one division by l at the end (the same value as normalising at
+// every step).
 //
-// Work decomposition: one workgroup per (batch, head, block row), block
-// rows longest first; one wave per T query rows of the block (T = 32, or 16
-// for 16-blocks). Per stored block c of the row:
-//   S^T = K_c Q^T          MFMA, K rows as A, the wave's Q rows (held in
-//                          registers for the whole row) as B. In the
-//                          accumulator layout every lane then owns ONE query
-//                          row (its column) and a slice of the keys, so the
-//                          row max and sum need only in-lane work plus a
-//                          butterfly across the G = 64/T lane groups.
-//   online softmax         scale*log2(e) folded into one multiply, causal
-//                          mask on blocks that reach the diagonal, exp2.
-//   O^T += V_c^T P^T       MFMA with P^T straight from the score registers
-//                          (B operand, no transpose through LDS) and V read
-//                          down its columns; O^T also keeps one query row per
-//                          lane, so the rescale by exp(m_old - m_new) is a
-//                          per-lane scalar.
-// bf16: scores, softmax and O accumulate in fp32; P is rounded to bf16
-// (round-to-nearest-even) for the P.V product; O is rounded once at the end.
+// Work decomposition. One workgroup per (batch, head, block row), rows
+// taken longest first; b/16 waves, wave w owning query rows 16w..16w+15 of
+// the block. The stored blocks of the row are visited in order; each is
+// staged once into LDS for all waves (K row-major, V transposed, rows padded
+// by 16 bytes so the operand reads below are bank-conflict free), and the
+// next block is already in flight into registers while the current one is
+// computed.
+//
+// Per block and wave, with 16x16 MFMA tiles (fp32 16x16x4, bf16 16x16x32):
+//   S^T = K_c Q^T     A = K rows from LDS, B = the wave's Q rows (registers,
+//                     loaded once). In the accumulator every lane then owns
+//                     ONE query row (its column) and 4 keys per 16-key tile,
+//                     so row max / sum are in-lane plus one butterfly over
+//                     the 4 lane groups.
+//   softmax           log2 domain (scale*log2(e) folded into Q for fp32, into
+//                     one fma for bf16); causal mask only on blocks that
+//                     reach the diagonal; raw v_exp_f32. The reference max
+//                     moves only when a block's max exceeds it by more than
+//                     TAU (so p <= 2^TAU): numerator and denominator share it,
+//                     so the result is exact, and most blocks skip the
+//                     rescale of O.
+//   O^T += V_c^T P^T  A = V^T rows from LDS, B = P^T straight from the score
+//                     registers (no transpose); O^T also keeps one query row
+//                     per lane, so the rescale is a per-lane scalar.
+// bf16: the key order inside each 32-key span is permuted in the S^T
+// product (which K row a lane feeds) so that a lane's 8 P values of one
+// 16x16x32 P.V instruction are 8 consecutive keys, read from V^T with one
+// 16-byte LDS load. P is rounded to bf16 (RNE) for P.V, O once at the end.
 #include <math.h>
+
+#include <type_traits>
 
 #include "internal.h"
 #include "tile.h"
@@ -33,192 +45,274 @@ namespace bsa {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kTau = 8.0f;  // lazy-rescale headroom, log2 units
 
-// V^T operand for one P.V instruction: the V entries (key rows, column n)
-// that pair with the k values this lane's P^T fragment holds.
-template <typename E, int T, int BLK>
-struct PV;
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <int T, int BLK>
-struct PV<float, T, BLK> {
-  using AccT = typename Acc<T>::type;
-  static constexpr int NR = T * T / 64;
-  // o[n-tile] += V^T[n][keys of reg q] * P^T[keys of reg q][query]
-  static __device__ __forceinline__ void run(AccT& o, const AccT (&p)[BLK / T], const float* pv, int D, int g) {
-#pragma unroll
-    for (int jt = 0; jt < BLK / T; ++jt)
-#pragma unroll
-      for (int q = 0; q < NR; ++q) mma(o, pv[(jt * T + acc_row<T>(q, g)) * D], p[jt][q]);
-  }
+template <typename E>
+struct Cfg;
+template <>
+struct Cfg<float> {
+  static constexpr int VEC = 4;   // elements per 16-byte vector
+  static constexpr int KC = 16;   // contraction values per 16-byte lane vector group (4 groups x 4)
+  typedef f32x4 Vec;
+};
+template <>
+struct Cfg<bf16_t> {
+  static constexpr int VEC = 8;
+  static constexpr int KC = 32;
+  typedef bf16x8 Vec;
 };
 
-template <int BLK>
-struct PV<bf16_t, 32, BLK> {
-  using AccT = f32x16;
-  // each instruction takes 8 consecutive score registers (16 keys per pair of
-  // instructions per 32-key tile)
-  static __device__ __forceinline__ void run(AccT& o, const AccT (&p)[BLK / 32], const u16* pv, int D, int g) {
-#pragma unroll
-    for (int jt = 0; jt < BLK / 32; ++jt)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        bf16x8 a, b;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          b[q] = to_bf16(p[jt][8 * u + q]);
-          a[q] = __builtin_bit_cast(__bf16, pv[(jt * 32 + acc_row<32>(8 * u + q, g)) * D]);
-        }
-        mma(o, a, b);
-      }
+// key of score register r of lane group g in 16-key tile jt
+template <typename E, int BLK>
+__device__ __forceinline__ constexpr int key_of(int jt, int m) {
+  // m = accumulator row (4g + r) or, for the A operand, the lane's row li
+  if constexpr (std::is_same<E, bf16_t>::value && BLK % 32 == 0) {
+    return 32 * (jt / 2) + 8 * (m / 4) + 4 * (jt % 2) + (m % 4);
+  } else {
+    return 16 * jt + m;
   }
-};
+}
 
-template <int BLK>
-struct PV<bf16_t, 16, BLK> {
-  using AccT = f32x4;
-  // each instruction takes the 4 score registers of two 16-key tiles
-  static __device__ __forceinline__ void run(AccT& o, const AccT (&p)[BLK / 16], const u16* pv, int D, int g) {
-    constexpr int NJT = BLK / 16;
-#pragma unroll
-    for (int jt = 0; jt < NJT; jt += 2) {
-      bf16x8 a, b;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int t = jt + q / 4;
-        if (t < NJT) {
-          b[q] = to_bf16(p[t][q % 4]);
-          a[q] = __builtin_bit_cast(__bf16, pv[(t * 16 + acc_row<16>(q % 4, g)) * D]);
-        } else {
-          b[q] = (__bf16)0.f;
-          a[q] = (__bf16)0.f;
-        }
-      }
-      mma(o, a, b);
-    }
-  }
-};
-
-template <typename E, int BLK, int T, int D, bool CAUSAL>
-__global__ __launch_bounds__(64 * (BLK / T)) void k_attn(
+template <typename E, int BLK, int D, bool CAUSAL>
+__global__ __launch_bounds__(BLK * 4) void k_attn(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, const int32_t* __restrict__ row_order,
     const typename Elem<E>::storage* __restrict__ Q, const typename Elem<E>::storage* __restrict__ K,
     const typename Elem<E>::storage* __restrict__ V, typename Elem<E>::storage* __restrict__ O, int H, int nbr,
     int nbc, float c) {
   using St = typename Elem<E>::storage;
-  using AccT = typename Acc<T>::type;
-  constexpr int G = 64 / T, VEC = Elem<E>::VEC, KC = G * VEC, NQ = D / KC, NR = T * T / 64;
-  constexpr int NJT = BLK / T, NNT = D / T;
-  const float NEG = -INFINITY;
+  using Vec = typename Cfg<E>::Vec;
+  constexpr bool BF = std::is_same<E, bf16_t>::value;
+  constexpr int VEC = Cfg<E>::VEC, KC = Cfg<E>::KC;
+  constexpr int NW = BLK / 16, NT = 64 * NW;
+  constexpr int NQ = D / KC;          // Q fragments per lane
+  constexpr int NJT = BLK / 16;       // 16-key tiles per block
+  constexpr int NNT = D / 16;         // 16-column tiles of O
+  constexpr int KSTR = D + VEC;       // padded LDS row strides (elements)
+  constexpr int VSTR = BLK + VEC;
+  constexpr int CPR = D / VEC;        // 16-byte chunks per K row
+  constexpr int KCH = BLK * CPR / NT; // K chunks per thread (D / (4 VEC))
+  // V micro-blocks: 4 keys x VEC columns, transposed on the way to LDS
+  constexpr int VMB = BLK * D / (4 * VEC);
+  constexpr int VPT = (VMB + NT - 1) / NT;
+  static_assert(KCH >= 1 && BLK * CPR % NT == 0, "K staging");
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int li = lane % T, g = lane / T;
+  __shared__ __attribute__((aligned(16))) St Ks[BLK * KSTR];
+  __shared__ __attribute__((aligned(16))) St Vt[D * VSTR];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int li = lane & 15, g = lane >> 4;
   const int hr = row_order[blockIdx.x];
   const int z = blockIdx.y;
   const int h = hr / nbr, r = hr % nbr;
   const int k0 = row_ptr[hr], k1 = row_ptr[hr + 1];
   const int64_t zh = (int64_t)z * H + h;
   const int64_t Nq = (int64_t)nbr * BLK, Nk = (int64_t)nbc * BLK;
-  const int q_index = r * BLK + wave * T + li;  // this lane's query row
+  const int q_lo = r * BLK + wave * 16;  // first query row of this wave
+  const int q_index = q_lo + li;         // this lane's query row
+  const St* Kz = K + zh * Nk * D;
+  const St* Vz = V + zh * Nk * D;
 
-  // the wave's Q rows as B fragments (k values permuted per 16-byte vector)
-  Frag<E> qf[NQ];
+  // ---- Q as B fragments; fp32 folds scale*log2(e) in, bf16 only its sign
+  Vec qf[NQ];
+  float cs;
   {
     const St* pq = Q + (zh * Nq + q_index) * D + g * VEC;
 #pragma unroll
-    for (int u = 0; u < NQ; ++u) qf[u].load(pq + u * KC);
+    for (int u = 0; u < NQ; ++u) qf[u] = *reinterpret_cast<const Vec*>(pq + u * KC);
+    if constexpr (BF) {
+      const float sgn = c > 0.f ? 1.f : (c < 0.f ? -1.f : 0.f);
+      if (sgn != 1.f) {
+#pragma unroll
+        for (int u = 0; u < NQ; ++u)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qf[u][e] = to_bf16((float)qf[u][e] * sgn);  // exact
+      }
+      cs = (c == 0.f) ? 1.f : fabsf(c);
+    } else {
+#pragma unroll
+      for (int u = 0; u < NQ; ++u) qf[u] *= c;
+      cs = 1.f;
+    }
   }
 
-  float m_run = NEG, l_run = 0.f;
-  AccT o[NNT];
+  // ---- staging registers for one block
+  Vec kst[KCH];
+  Vec vst[VPT][4];
+  auto stage_load = [&](int cb) {
+    const St* kb = Kz + (int64_t)cb * BLK * D;
 #pragma unroll
-  for (int nt = 0; nt < NNT; ++nt) o[nt] = AccT{};
+    for (int i = 0; i < KCH; ++i) {
+      const int ch = tid + i * NT;
+      kst[i] = *reinterpret_cast<const Vec*>(kb + (ch / CPR) * D + (ch % CPR) * VEC);
+    }
+    const St* vb = Vz + (int64_t)cb * BLK * D;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int mb = tid + i * NT;
+      if (mb < VMB) {
+        const int n0 = (mb % CPR) * VEC, key0 = (mb / CPR) * 4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vst[i][j] = *reinterpret_cast<const Vec*>(vb + (key0 + j) * D + n0);
+      }
+    }
+  };
+  auto stage_store = [&]() {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int ch = tid + i * NT;
+      *reinterpret_cast<Vec*>(&Ks[(ch / CPR) * KSTR + (ch % CPR) * VEC]) = kst[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int mb = tid + i * NT;
+      if (mb < VMB) {
+        const int n0 = (mb % CPR) * VEC, key0 = (mb / CPR) * 4;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          if constexpr (BF) {
+            bf16x4 t = {vst[i][0][e], vst[i][1][e], vst[i][2][e], vst[i][3][e]};
+            *reinterpret_cast<bf16x4*>(&Vt[(n0 + e) * VSTR + key0]) = t;
+          } else {
+            f32x4 t = {vst[i][0][e], vst[i][1][e], vst[i][2][e], vst[i][3][e]};
+            *reinterpret_cast<f32x4*>(&Vt[(n0 + e) * VSTR + key0]) = t;
+          }
+        }
+      }
+    }
+  };
 
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 o[NNT];
+#pragma unroll
+  for (int nt = 0; nt < NNT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (k0 < k1) stage_load(col_idx[k0]);
   for (int kk = k0; kk < k1; ++kk) {
     const int cb = col_idx[kk];
-    const St* pk = K + (zh * Nk + (int64_t)cb * BLK + li) * D + g * VEC;
-    const St* pv = V + (zh * Nk + (int64_t)cb * BLK) * D;
+    __syncthreads();  // every wave is done with the previous block in LDS
+    stage_store();
+    __syncthreads();
+    if (kk + 1 < k1) stage_load(col_idx[kk + 1]);  // in flight during compute
 
-    // S^T tiles: s[jt][q] = score(query li, key jt*T + acc_row(q, g))
-    AccT s[NJT];
+    if (CAUSAL && cb * BLK > q_lo + 15) continue;  // every key after every query of this wave
+    const bool mask_block = CAUSAL && (cb * BLK + BLK - 1 > q_lo);
+
+    // S^T tiles: s[jt][rr] = score(query li, key key_of(jt, 4g + rr))
+    f32x4 s[NJT];
 #pragma unroll
     for (int jt = 0; jt < NJT; ++jt) {
-      s[jt] = AccT{};
+      s[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const St* ka = &Ks[key_of<E, BLK>(jt, li) * KSTR + g * VEC];
 #pragma unroll
       for (int u = 0; u < NQ; ++u) {
-        Frag<E> kf;
-        kf.load(pk + (int64_t)jt * T * D + u * KC);
-        mma_frag<T>(s[jt], kf, qf[u]);
+        const Vec a = *reinterpret_cast<const Vec*>(ka + u * KC);
+        if constexpr (BF) {
+          s[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[u], s[jt], 0, 0, 0);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], qf[u][e], s[jt], 0, 0, 0);
+        }
       }
     }
 
-    // scale (log2 domain), mask, running max
-    const bool mask_block = CAUSAL && (cb * BLK + BLK - 1 > r * BLK + wave * T);
-    float mx = NEG;
+    // mask and block max (raw scores; cs > 0)
+    float mx = -INFINITY;
 #pragma unroll
     for (int jt = 0; jt < NJT; ++jt)
 #pragma unroll
-      for (int q = 0; q < NR; ++q) {
-        float x = s[jt][q] * c;
-        if (mask_block && cb * BLK + jt * T + acc_row<T>(q, g) > q_index) x = NEG;
-        s[jt][q] = x;
-        mx = fmaxf(mx, x);
+      for (int rr = 0; rr < 4; ++rr) {
+        if (mask_block && cb * BLK + key_of<E, BLK>(jt, 4 * g + rr) > q_index) s[jt][rr] = -INFINITY;
+        mx = fmaxf(mx, s[jt][rr]);
       }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_blk = mx * cs;
+    const bool upd = m_blk > m_run + kTau;
+    if (__builtin_amdgcn_ballot_w64(upd) != 0) {  // wave-uniform
+      const float m_new = upd ? m_blk : m_run;
+      const float alpha = fast_exp2(m_run - m_new);  // 0 when m_run = -inf
+      l_run *= alpha;
 #pragma unroll
-    for (int off = T; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = (m_new == NEG) ? 1.f : exp2f(m_run - m_new);
-    const float m_sub = (m_new == NEG) ? 0.f : m_new;
+      for (int nt = 0; nt < NNT; ++nt) o[nt] *= alpha;
+      m_run = m_new;
+    }
+    const float m_sub = (m_run == -INFINITY) ? 0.f : m_run;
     float ls = 0.f;
 #pragma unroll
     for (int jt = 0; jt < NJT; ++jt)
 #pragma unroll
-      for (int q = 0; q < NR; ++q) {
-        const float pr = exp2f(s[jt][q] - m_sub);
-        s[jt][q] = pr;
-        ls += pr;
+      for (int rr = 0; rr < 4; ++rr) {
+        const float p = fast_exp2(fmaf(s[jt][rr], cs, -m_sub));
+        s[jt][rr] = p;
+        ls += p;
       }
-    l_run = l_run * alpha + ls;
-    m_run = m_new;
+    l_run += ls;
 
-    // O^T[n][query] = alpha * O^T + V^T[n][keys] P^T[keys][query]
+    // O^T[n][query] += V^T[n][keys] P^T[keys][query]
+    if constexpr (BF) {
+      if constexpr (BLK % 32 == 0) {
 #pragma unroll
-    for (int nt = 0; nt < NNT; ++nt) {
-      o[nt] *= alpha;
-      PV<E, T, BLK>::run(o[nt], s, pv + nt * T + li, D, g);
+        for (int jp = 0; jp < NJT / 2; ++jp) {
+          const bf16x8 pb = {to_bf16(s[2 * jp][0]),     to_bf16(s[2 * jp][1]),     to_bf16(s[2 * jp][2]),
+                             to_bf16(s[2 * jp][3]),     to_bf16(s[2 * jp + 1][0]), to_bf16(s[2 * jp + 1][1]),
+                             to_bf16(s[2 * jp + 1][2]), to_bf16(s[2 * jp + 1][3])};
+#pragma unroll
+          for (int nt = 0; nt < NNT; ++nt) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Vt[(nt * 16 + li) * VSTR + 32 * jp + 8 * g]);
+            o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[nt], 0, 0, 0);
+          }
+        }
+      } else {  // a single 16-key tile: the other half of the k range is zero
+        const __bf16 zb = (__bf16)0.f;
+        const bf16x8 pb = {to_bf16(s[0][0]), to_bf16(s[0][1]), to_bf16(s[0][2]), to_bf16(s[0][3]), zb, zb, zb, zb};
+#pragma unroll
+        for (int nt = 0; nt < NNT; ++nt) {
+          const bf16x4 a4 = *reinterpret_cast<const bf16x4*>(&Vt[(nt * 16 + li) * VSTR + 4 * g]);
+          const bf16x8 a = {a4[0], a4[1], a4[2], a4[3], zb, zb, zb, zb};
+          o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[nt], 0, 0, 0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+        for (int nt = 0; nt < NNT; ++nt) {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(&Vt[(nt * 16 + li) * VSTR + 16 * jt + 4 * g]);
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) o[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[rr], s[jt][rr], o[nt], 0, 0, 0);
+        }
     }
   }
 
-  // finish: l over the lane groups, O = O^T / l, written row-wise
-#pragma unroll
-  for (int off = T; off < 64; off <<= 1) l_run += __shfl_xor(l_run, off);
+  // ---- finish: l over the 4 lane groups, O = O^T / l, 4 columns per store
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
   const float inv = (l_run > 0.f) ? 1.0f / l_run : 0.f;
-  St* po = O + (zh * Nq + q_index) * D;
+  St* po = O + (zh * Nq + q_index) * D + 4 * g;
 #pragma unroll
-  for (int nt = 0; nt < NNT; ++nt)
-#pragma unroll
-    for (int q = 0; q < NR; q += 4) {
-      const int n = nt * T + acc_row<T>(q, g);  // 4 consecutive columns
-      if constexpr (sizeof(St) == 4) {
-        *reinterpret_cast<f32x4*>(po + n) =
-            f32x4{o[nt][q] * inv, o[nt][q + 1] * inv, o[nt][q + 2] * inv, o[nt][q + 3] * inv};
-      } else {
-        *reinterpret_cast<bf16x4*>(po + n) = bf16x4{to_bf16(o[nt][q] * inv), to_bf16(o[nt][q + 1] * inv),
-                                                    to_bf16(o[nt][q + 2] * inv), to_bf16(o[nt][q + 3] * inv)};
-      }
+  for (int nt = 0; nt < NNT; ++nt) {
+    if constexpr (BF) {
+      *reinterpret_cast<bf16x4*>(po + nt * 16) =
+          bf16x4{to_bf16(o[nt][0] * inv), to_bf16(o[nt][1] * inv), to_bf16(o[nt][2] * inv), to_bf16(o[nt][3] * inv)};
+    } else {
+      *reinterpret_cast<f32x4*>(po + nt * 16) = o[nt] * inv;
     }
+  }
 }
 
 template <typename E, int BLK, int D>
 int run(const bs_layout* L, const void* Q, const void* K, const void* V, void* O, int Z, float c, bool causal,
         hipStream_t s) {
   using St = typename Elem<E>::storage;
-  constexpr int T = BLK >= 32 ? 32 : 16;
-  const dim3 grid(L->H * L->nbr, Z), block(64 * (BLK / T));
+  const dim3 grid(L->H * L->nbr, Z), block(BLK * 4);
   if (causal)
-    hipLaunchKernelGGL((k_attn<E, BLK, T, D, true>), grid, block, 0, s, L->row_ptr, L->col_idx, L->row_order,
+    hipLaunchKernelGGL((k_attn<E, BLK, D, true>), grid, block, 0, s, L->row_ptr, L->col_idx, L->row_order,
                        (const St*)Q, (const St*)K, (const St*)V, (St*)O, L->H, L->nbr, L->nbc, c);
   else
-    hipLaunchKernelGGL((k_attn<E, BLK, T, D, false>), grid, block, 0, s, L->row_ptr, L->col_idx, L->row_order,
+    hipLaunchKernelGGL((k_attn<E, BLK, D, false>), grid, block, 0, s, L->row_ptr, L->col_idx, L->row_order,
                        (const St*)Q, (const St*)K, (const St*)V, (St*)O, L->H, L->nbr, L->nbc, c);
   BSA_HIP(hipGetLastError());
   return BS_OK;
