@@ -9,10 +9,12 @@
 // Work decomposition. One workgroup per (batch, head, block row), rows
 // taken longest first; b/16 waves, wave w owning query rows 16w..16w+15 of
 // the block. The stored blocks of the row are visited in order; each is
-// staged once into LDS for all waves (K row-major, V transposed, rows padded
-// by 16 bytes so the operand reads below are bank-conflict free), and the
-// next block is already in flight into registers while the current one is
-// computed.
+// staged once into LDS for all waves, K and V both row-major (contiguous
+// 16-byte writes), and the next block is already in flight into registers
+// while the current one is computed. Row strides were chosen by measuring
+// the operand read patterns on gfx950: K rows padded to 32 mod 256 bytes,
+// fp32 V rows to 16 mod 64 bytes, bf16 V rows to 32 mod 256 bytes; every
+// operand read below is then free of bank conflicts.
 //
 // Per block and wave, with 16x16 MFMA tiles (fp32 16x16x4, bf16 16x16x32):
 //   S^T = K_c Q^T     A = K rows from LDS, B = the wave's Q rows (registers,
@@ -27,13 +29,15 @@
 //                     TAU (so p <= 2^TAU): numerator and denominator share it,
 //                     so the result is exact, and most blocks skip the
 //                     rescale of O.
-//   O^T += V_c^T P^T  A = V^T rows from LDS, B = P^T straight from the score
-//                     registers (no transpose); O^T also keeps one query row
-//                     per lane, so the rescale is a per-lane scalar.
-// bf16: the key order inside each 32-key span is permuted in the S^T
-// product (which K row a lane feeds) so that a lane's 8 P values of one
-// 16x16x32 P.V instruction are 8 consecutive keys, read from V^T with one
-// 16-byte LDS load. P is rounded to bf16 (RNE) for P.V, O once at the end.
+//   O^T += V_c^T P^T  A = V^T, B = P^T straight from the score registers (no
+//                     transpose); O^T also keeps one query row per lane, so
+//                     the rescale is a per-lane scalar. fp32 takes one V
+//                     element per lane and instruction (one 4-byte LDS read);
+//                     bf16 takes 8 keys of one column per lane from two
+//                     ds_read_b64_tr_b16 (each 16-lane group reads a 4-key x
+//                     16-column patch and every lane receives the 4 keys of
+//                     its own column), so V never needs a transposed copy.
+// bf16: P is rounded to bf16 (RNE) for P.V, O once at the end.
 #include <math.h>
 
 #include <type_traits>
@@ -64,15 +68,15 @@ struct Cfg<bf16_t> {
   typedef bf16x8 Vec;
 };
 
-// key of score register r of lane group g in 16-key tile jt
-template <typename E, int BLK>
-__device__ __forceinline__ constexpr int key_of(int jt, int m) {
-  // m = accumulator row (4g + r) or, for the A operand, the lane's row li
-  if constexpr (std::is_same<E, bf16_t>::value && BLK % 32 == 0) {
-    return 32 * (jt / 2) + 8 * (m / 4) + 4 * (jt % 2) + (m % 4);
-  } else {
-    return 16 * jt + m;
-  }
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// 4 keys of one V column per lane, from a row-major bf16 tile in LDS: the
+// 16 lanes of a group pass the addresses of a 4-row x 16-column patch (lane
+// 4k + m: row k, columns 4m..4m+3) and lane i receives column i of the 4 rows
+__device__ __forceinline__ bf16x4 lds_read_tr16(const u16* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((__attribute__((address_space(3))) u16*)p));
+  return __builtin_bit_cast(bf16x4, v);
 }
 
 template <typename E, int BLK, int D, bool CAUSAL>
@@ -89,17 +93,16 @@ __global__ __launch_bounds__(BLK * 4) void k_attn(
   constexpr int NQ = D / KC;          // Q fragments per lane
   constexpr int NJT = BLK / 16;       // 16-key tiles per block
   constexpr int NNT = D / 16;         // 16-column tiles of O
-  constexpr int KSTR = D + VEC;       // padded LDS row strides (elements)
-  constexpr int VSTR = BLK + VEC;
-  constexpr int CPR = D / VEC;        // 16-byte chunks per K row
-  constexpr int KCH = BLK * CPR / NT; // K chunks per thread (D / (4 VEC))
-  // V micro-blocks: 4 keys x VEC columns, transposed on the way to LDS
-  constexpr int VMB = BLK * D / (4 * VEC);
-  constexpr int VPT = (VMB + NT - 1) / NT;
-  static_assert(KCH >= 1 && BLK * CPR % NT == 0, "K staging");
+  // padded LDS row strides (elements): K 32 mod 256 bytes; V 16 mod 64
+  // bytes (fp32) or 32 mod 256 bytes (bf16)
+  constexpr int KSTR = D + 32 / (int)sizeof(St);
+  constexpr int VSTR = BF ? D + 16 : D + 4;
+  constexpr int CPR = D / VEC;        // 16-byte chunks per row
+  constexpr int KCH = BLK * CPR / NT; // chunks per thread and matrix (D / (4 VEC))
+  static_assert(KCH >= 1 && BLK * CPR % NT == 0, "staging");
 
   __shared__ __attribute__((aligned(16))) St Ks[BLK * KSTR];
-  __shared__ __attribute__((aligned(16))) St Vt[D * VSTR];
+  __shared__ __attribute__((aligned(16))) St Vs[BLK * VSTR];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -138,25 +141,16 @@ __global__ __launch_bounds__(BLK * 4) void k_attn(
     }
   }
 
-  // ---- staging registers for one block
-  Vec kst[KCH];
-  Vec vst[VPT][4];
+  // ---- staging registers for one block (K and V, same chunk mapping)
+  Vec kst[KCH], vst[KCH];
   auto stage_load = [&](int cb) {
-    const St* kb = Kz + (int64_t)cb * BLK * D;
+    const int64_t off = (int64_t)cb * BLK * D;
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const int ch = tid + i * NT;
-      kst[i] = *reinterpret_cast<const Vec*>(kb + (ch / CPR) * D + (ch % CPR) * VEC);
-    }
-    const St* vb = Vz + (int64_t)cb * BLK * D;
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int mb = tid + i * NT;
-      if (mb < VMB) {
-        const int n0 = (mb % CPR) * VEC, key0 = (mb / CPR) * 4;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) vst[i][j] = *reinterpret_cast<const Vec*>(vb + (key0 + j) * D + n0);
-      }
+      const int e = (ch / CPR) * D + (ch % CPR) * VEC;
+      kst[i] = *reinterpret_cast<const Vec*>(Kz + off + e);
+      vst[i] = *reinterpret_cast<const Vec*>(Vz + off + e);
     }
   };
   auto stage_store = [&]() {
@@ -164,23 +158,7 @@ __global__ __launch_bounds__(BLK * 4) void k_attn(
     for (int i = 0; i < KCH; ++i) {
       const int ch = tid + i * NT;
       *reinterpret_cast<Vec*>(&Ks[(ch / CPR) * KSTR + (ch % CPR) * VEC]) = kst[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int mb = tid + i * NT;
-      if (mb < VMB) {
-        const int n0 = (mb % CPR) * VEC, key0 = (mb / CPR) * 4;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          if constexpr (BF) {
-            bf16x4 t = {vst[i][0][e], vst[i][1][e], vst[i][2][e], vst[i][3][e]};
-            *reinterpret_cast<bf16x4*>(&Vt[(n0 + e) * VSTR + key0]) = t;
-          } else {
-            f32x4 t = {vst[i][0][e], vst[i][1][e], vst[i][2][e], vst[i][3][e]};
-            *reinterpret_cast<f32x4*>(&Vt[(n0 + e) * VSTR + key0]) = t;
-          }
-        }
-      }
+      *reinterpret_cast<Vec*>(&Vs[(ch / CPR) * VSTR + (ch % CPR) * VEC]) = vst[i];
     }
   };
 
@@ -200,12 +178,12 @@ __global__ __launch_bounds__(BLK * 4) void k_attn(
     if (CAUSAL && cb * BLK > q_lo + 15) continue;  // every key after every query of this wave
     const bool mask_block = CAUSAL && (cb * BLK + BLK - 1 > q_lo);
 
-    // S^T tiles: s[jt][rr] = score(query li, key key_of(jt, 4g + rr))
+    // S^T tiles: s[jt][rr] = score(query li, key 16 jt + 4 g + rr)
     f32x4 s[NJT];
 #pragma unroll
     for (int jt = 0; jt < NJT; ++jt) {
       s[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const St* ka = &Ks[key_of<E, BLK>(jt, li) * KSTR + g * VEC];
+      const St* ka = &Ks[(16 * jt + li) * KSTR + g * VEC];
 #pragma unroll
       for (int u = 0; u < NQ; ++u) {
         const Vec a = *reinterpret_cast<const Vec*>(ka + u * KC);
@@ -224,7 +202,7 @@ __global__ __launch_bounds__(BLK * 4) void k_attn(
     for (int jt = 0; jt < NJT; ++jt)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        if (mask_block && cb * BLK + key_of<E, BLK>(jt, 4 * g + rr) > q_index) s[jt][rr] = -INFINITY;
+        if (mask_block && cb * BLK + 16 * jt + 4 * g + rr > q_index) s[jt][rr] = -INFINITY;
         mx = fmaxf(mx, s[jt][rr]);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -253,7 +231,10 @@ __global__ __launch_bounds__(BLK * 4) void k_attn(
 
     // O^T[n][query] += V^T[n][keys] P^T[keys][query]
     if constexpr (BF) {
-      if constexpr (BLK % 32 == 0) {
+      // lane (g, j = 4k + m) points at row 16h + 4g + k, columns 4m.. of
+      // the n-tile; it gets back keys 16h + 4g + 0..3 of column nt*16 + li
+      const u16* vb = &Vs[(4 * g + (li >> 2)) * VSTR + 4 * (li & 3)];
+      if constexpr (NJT >= 2) {
 #pragma unroll
         for (int jp = 0; jp < NJT / 2; ++jp) {
           const bf16x8 pb = {to_bf16(s[2 * jp][0]),     to_bf16(s[2 * jp][1]),     to_bf16(s[2 * jp][2]),
@@ -261,7 +242,9 @@ __global__ __launch_bounds__(BLK * 4) void k_attn(
                              to_bf16(s[2 * jp + 1][2]), to_bf16(s[2 * jp + 1][3])};
 #pragma unroll
           for (int nt = 0; nt < NNT; ++nt) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Vt[(nt * 16 + li) * VSTR + 32 * jp + 8 * g]);
+            const bf16x4 a0 = lds_read_tr16(vb + (32 * jp) * VSTR + nt * 16);
+            const bf16x4 a1 = lds_read_tr16(vb + (32 * jp + 16) * VSTR + nt * 16);
+            const bf16x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
             o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[nt], 0, 0, 0);
           }
         }
@@ -270,8 +253,8 @@ __global__ __launch_bounds__(BLK * 4) void k_attn(
         const bf16x8 pb = {to_bf16(s[0][0]), to_bf16(s[0][1]), to_bf16(s[0][2]), to_bf16(s[0][3]), zb, zb, zb, zb};
 #pragma unroll
         for (int nt = 0; nt < NNT; ++nt) {
-          const bf16x4 a4 = *reinterpret_cast<const bf16x4*>(&Vt[(nt * 16 + li) * VSTR + 4 * g]);
-          const bf16x8 a = {a4[0], a4[1], a4[2], a4[3], zb, zb, zb, zb};
+          const bf16x4 a0 = lds_read_tr16(vb + nt * 16);
+          const bf16x8 a = {a0[0], a0[1], a0[2], a0[3], zb, zb, zb, zb};
           o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[nt], 0, 0, 0);
         }
       }
@@ -279,10 +262,10 @@ __global__ __launch_bounds__(BLK * 4) void k_attn(
 #pragma unroll
       for (int jt = 0; jt < NJT; ++jt)
 #pragma unroll
-        for (int nt = 0; nt < NNT; ++nt) {
-          const f32x4 a = *reinterpret_cast<const f32x4*>(&Vt[(nt * 16 + li) * VSTR + 16 * jt + 4 * g]);
+        for (int rr = 0; rr < 4; ++rr) {
+          const float* vr = &Vs[(16 * jt + 4 * g + rr) * VSTR + li];
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) o[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[rr], s[jt][rr], o[nt], 0, 0, 0);
+          for (int nt = 0; nt < NNT; ++nt) o[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vr[nt * 16], s[jt][rr], o[nt], 0, 0, 0);
         }
     }
   }
