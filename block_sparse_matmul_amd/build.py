@@ -25,9 +25,13 @@ ARCH = "gfx950"
 SOURCES = ["api.cpp", "lut.hip", "sdd.hip", "softmax.hip", "dsd.hip", "dds.hip", "attention.hip"]
 
 # Packed fp32 VALU forms are kept off (the compiler would otherwise fuse
-# pairs of fp32 ops into v_pk_* instructions).
+# pairs of fp32 ops into v_pk_* instructions). MFMA results are kept in
+# ordinary VGPRs: the softmax reads the score accumulators and rescales the
+# output accumulators with VALU ops, which would otherwise copy them out of
+# and back into AGPRs on every block.
 COMMON = ["-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form",
           "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
 
 

@@ -105,7 +105,8 @@ __global__ __launch_bounds__(BLK * 4) void k_attn(
   __shared__ __attribute__((aligned(16))) St Vs[BLK * VSTR];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps mask tests scalar
+  const int lane = tid & 63;
   const int li = lane & 15, g = lane >> 4;
   const int hr = row_order[blockIdx.x];
   const int z = blockIdx.y;
@@ -178,33 +179,46 @@ __global__ __launch_bounds__(BLK * 4) void k_attn(
     if (CAUSAL && cb * BLK > q_lo + 15) continue;  // every key after every query of this wave
     const bool mask_block = CAUSAL && (cb * BLK + BLK - 1 > q_lo);
 
-    // S^T tiles: s[jt][rr] = score(query li, key 16 jt + 4 g + rr)
+    // S^T tiles: s[jt][rr] = score(query li, key 16 jt + 4 g + rr). The K
+    // operands of tile jt+1 are read from LDS while tile jt is multiplied.
     f32x4 s[NJT];
+    Vec ka[2][NQ];
+    const St* kbase = &Ks[li * KSTR + g * VEC];
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) ka[0][u] = *reinterpret_cast<const Vec*>(kbase + u * KC);
 #pragma unroll
     for (int jt = 0; jt < NJT; ++jt) {
+      if (jt + 1 < NJT) {
+#pragma unroll
+        for (int u = 0; u < NQ; ++u)
+          ka[(jt + 1) & 1][u] = *reinterpret_cast<const Vec*>(kbase + 16 * (jt + 1) * KSTR + u * KC);
+      }
       s[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const St* ka = &Ks[(16 * jt + li) * KSTR + g * VEC];
 #pragma unroll
       for (int u = 0; u < NQ; ++u) {
-        const Vec a = *reinterpret_cast<const Vec*>(ka + u * KC);
         if constexpr (BF) {
-          s[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[u], s[jt], 0, 0, 0);
+          s[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[jt & 1][u], qf[u], s[jt], 0, 0, 0);
         } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) s[jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], qf[u][e], s[jt], 0, 0, 0);
+          for (int e = 0; e < 4; ++e)
+            s[jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[jt & 1][u][e], qf[u][e], s[jt], 0, 0, 0);
         }
       }
     }
 
     // mask and block max (raw scores; cs > 0)
+    if (mask_block) {
+#pragma unroll
+      for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          if (cb * BLK + 16 * jt + 4 * g + rr > q_index) s[jt][rr] = -INFINITY;
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int jt = 0; jt < NJT; ++jt)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        if (mask_block && cb * BLK + 16 * jt + 4 * g + rr > q_index) s[jt][rr] = -INFINITY;
-        mx = fmaxf(mx, s[jt][rr]);
-      }
+      for (int rr = 0; rr < 4; ++rr) mx = fmaxf(mx, s[jt][rr]);
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_blk = mx * cs;
@@ -235,15 +249,27 @@ __global__ __launch_bounds__(BLK * 4) void k_attn(
       // the n-tile; it gets back keys 16h + 4g + 0..3 of column nt*16 + li
       const u16* vb = &Vs[(4 * g + (li >> 2)) * VSTR + 4 * (li & 3)];
       if constexpr (NJT >= 2) {
+        bf16x4 va[2][2][NNT];
+#pragma unroll
+        for (int nt = 0; nt < NNT; ++nt) {
+          va[0][0][nt] = lds_read_tr16(vb + nt * 16);
+          va[0][1][nt] = lds_read_tr16(vb + 16 * VSTR + nt * 16);
+        }
 #pragma unroll
         for (int jp = 0; jp < NJT / 2; ++jp) {
+          if (jp + 1 < NJT / 2) {
+#pragma unroll
+            for (int nt = 0; nt < NNT; ++nt) {
+              va[(jp + 1) & 1][0][nt] = lds_read_tr16(vb + (32 * (jp + 1)) * VSTR + nt * 16);
+              va[(jp + 1) & 1][1][nt] = lds_read_tr16(vb + (32 * (jp + 1) + 16) * VSTR + nt * 16);
+            }
+          }
           const bf16x8 pb = {to_bf16(s[2 * jp][0]),     to_bf16(s[2 * jp][1]),     to_bf16(s[2 * jp][2]),
                              to_bf16(s[2 * jp][3]),     to_bf16(s[2 * jp + 1][0]), to_bf16(s[2 * jp + 1][1]),
                              to_bf16(s[2 * jp + 1][2]), to_bf16(s[2 * jp + 1][3])};
 #pragma unroll
           for (int nt = 0; nt < NNT; ++nt) {
-            const bf16x4 a0 = lds_read_tr16(vb + (32 * jp) * VSTR + nt * 16);
-            const bf16x4 a1 = lds_read_tr16(vb + (32 * jp + 16) * VSTR + nt * 16);
+            const bf16x4 a0 = va[jp & 1][0][nt], a1 = va[jp & 1][1][nt];
             const bf16x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
             o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[nt], 0, 0, 0);
           }
@@ -259,14 +285,28 @@ __global__ __launch_bounds__(BLK * 4) void k_attn(
         }
       }
     } else {
+      // one V element per lane and instruction; tile jt+1 is read while
+      // tile jt is multiplied
+      float va[2][4][NNT];
+      const float* vbase = &Vs[4 * g * VSTR + li];
 #pragma unroll
-      for (int jt = 0; jt < NJT; ++jt)
+      for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const float* vr = &Vs[(16 * jt + 4 * g + rr) * VSTR + li];
+        for (int nt = 0; nt < NNT; ++nt) va[0][rr][nt] = vbase[rr * VSTR + nt * 16];
 #pragma unroll
-          for (int nt = 0; nt < NNT; ++nt) o[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vr[nt * 16], s[jt][rr], o[nt], 0, 0, 0);
+      for (int jt = 0; jt < NJT; ++jt) {
+        if (jt + 1 < NJT) {
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+            for (int nt = 0; nt < NNT; ++nt) va[(jt + 1) & 1][rr][nt] = vbase[(16 * (jt + 1) + rr) * VSTR + nt * 16];
         }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+          for (int nt = 0; nt < NNT; ++nt)
+            o[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va[jt & 1][rr][nt], s[jt][rr], o[nt], 0, 0, 0);
+      }
     }
   }
 
