@@ -59,6 +59,13 @@ int check_dims(int H, int nbr, int nbc, int block) {
   return BS_OK;
 }
 
+// one workgroup per (batch, block row / column) on a 1-D grid
+int check_grid(const bs_layout* L, int Z) {
+  const int64_t units = (int64_t)Z * L->H * (L->nbr > L->nbc ? L->nbr : L->nbc);
+  if (units > (int64_t)1 << 22) return fail(BS_ERR_SHAPE, "Z*H*blocks per side exceeds 2^22 workgroups");
+  return BS_OK;
+}
+
 int check_dtype(bs_dtype dt) {
   if (dt != BS_F32 && dt != BS_BF16) return fail(BS_ERR_INVALID_ARG, "dtype must be BS_F32 or BS_BF16");
   return BS_OK;
@@ -91,6 +98,11 @@ void log_call(const char* name, const bs_layout* L, int Z, int x) {
 }
 
 int finish_build(bs_layout* L, const uint8_t* layout, hipStream_t s, bs_layout_t* out) {
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, L->device) == hipSuccess && cus > 0)
+    L->num_cus = cus;
+  else
+    (void)hipGetLastError();
   const int rc = bsa::build_tables(L, layout, s);
   if (rc != BS_OK) {
     delete L;
@@ -218,6 +230,7 @@ int bs_sdd(bs_layout_t L, const void* A, const void* B, float* S, int Z, int K, 
   const bool work = Z > 0 && L->nnz > 0;
   if (int rc = check_ptrs(work, {A, B, S})) return rc;
   if (!work) return BS_OK;
+  if (int rc = check_grid(L, Z)) return rc;
   if ((int64_t)Z * L->nnz * L->block * L->block > ((int64_t)1 << 46))
     return fail(BS_ERR_SHAPE, "block-sparse tensor too large");
   log_call("sdd", L, Z, K);
@@ -250,6 +263,7 @@ int bs_dsd(bs_layout_t L, const float* P, const void* B, void* C, int Z, int Nd,
     if (int rc = check_ptrs(true, {P})) return rc;
   }
   if (!work) return BS_OK;
+  if (int rc = check_grid(L, Z)) return rc;
   log_call("dsd", L, Z, Nd);
   return bsa::launch_dsd(L, P, B, C, Z, Nd, dt, (hipStream_t)stream);
 }
@@ -265,6 +279,7 @@ int bs_dds(bs_layout_t L, const void* A, const float* S, void* C, int Z, int M, 
     if (int rc = check_ptrs(true, {S})) return rc;
   }
   if (!work) return BS_OK;
+  if (int rc = check_grid(L, Z)) return rc;
   log_call("dds", L, Z, M);
   return bsa::launch_dds(L, A, S, C, Z, M, dt, (hipStream_t)stream);
 }
@@ -281,6 +296,7 @@ int bs_attention(bs_layout_t L, const void* Q, const void* K, const void* V, voi
   const bool work = Z > 0;
   if (int rc = check_ptrs(work, {Q, K, V, O})) return rc;
   if (!work) return BS_OK;
+  if (int rc = check_grid(L, Z)) return rc;
   log_call("attention", L, Z, d);
   return bsa::launch_attention(L, Q, K, V, O, Z, d, scale, causal, dt, (hipStream_t)stream);
 }

@@ -68,6 +68,18 @@ struct Cfg<bf16_t> {
   typedef bf16x8 Vec;
 };
 
+// padded LDS row strides (elements), measured free of bank conflicts for the
+// operand reads of the kernel: K rows 32 mod 256 bytes; V rows 16 mod 64
+// bytes (fp32, one 4-byte read per lane) or 32 mod 256 bytes (bf16,
+// transposing 8-byte reads)
+template <typename E, int BLK, int D>
+struct Lds {
+  using St = typename Elem<E>::storage;
+  static constexpr int KSTR = D + 32 / (int)sizeof(St);
+  static constexpr int VSTR = std::is_same<E, bf16_t>::value ? D + 16 : D + 4;
+  static constexpr size_t STAGE = (size_t)BLK * (KSTR + VSTR) * sizeof(St);  // bytes per key group
+};
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -79,37 +91,45 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const u16* p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
-template <typename E, int BLK, int D, bool CAUSAL>
-__global__ __launch_bounds__(BLK * 4) void k_attn(
+template <typename E, int BLK, int D, bool CAUSAL, int NS>
+__global__ __launch_bounds__(BLK * 4 * NS) void k_attn(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, const int32_t* __restrict__ row_order,
     const typename Elem<E>::storage* __restrict__ Q, const typename Elem<E>::storage* __restrict__ K,
-    const typename Elem<E>::storage* __restrict__ V, typename Elem<E>::storage* __restrict__ O, int H, int nbr,
-    int nbc, float c) {
+    const typename Elem<E>::storage* __restrict__ V, typename Elem<E>::storage* __restrict__ O, int Z, int H,
+    int nbr, int nbc, float c) {
   using St = typename Elem<E>::storage;
   using Vec = typename Cfg<E>::Vec;
   constexpr bool BF = std::is_same<E, bf16_t>::value;
   constexpr int VEC = Cfg<E>::VEC, KC = Cfg<E>::KC;
-  constexpr int NW = BLK / 16, NT = 64 * NW;
+  constexpr int NW = BLK / 16, NT = 64 * NW;  // waves / threads of one key group
   constexpr int NQ = D / KC;          // Q fragments per lane
   constexpr int NJT = BLK / 16;       // 16-key tiles per block
   constexpr int NNT = D / 16;         // 16-column tiles of O
-  // padded LDS row strides (elements): K 32 mod 256 bytes; V 16 mod 64
-  // bytes (fp32) or 32 mod 256 bytes (bf16)
-  constexpr int KSTR = D + 32 / (int)sizeof(St);
-  constexpr int VSTR = BF ? D + 16 : D + 4;
+  constexpr int KSTR = Lds<E, BLK, D>::KSTR;
+  constexpr int VSTR = Lds<E, BLK, D>::VSTR;
   constexpr int CPR = D / VEC;        // 16-byte chunks per row
   constexpr int KCH = BLK * CPR / NT; // chunks per thread and matrix (D / (4 VEC))
   static_assert(KCH >= 1 && BLK * CPR % NT == 0, "staging");
 
-  __shared__ __attribute__((aligned(16))) St Ks[BLK * KSTR];
-  __shared__ __attribute__((aligned(16))) St Vs[BLK * VSTR];
+  constexpr int KBUF = BLK * KSTR, VBUF = BLK * VSTR;  // one stage of one key group
+  constexpr int MERGE = NS > 1 ? (NS - 1) * NW * 64 * (2 + 4 * NNT) : 0;  // floats for the final merge
+  static_assert((size_t)MERGE * 4 <= (size_t)NS * (KBUF + VBUF) * sizeof(St), "merge area");
 
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps mask tests scalar
+  __shared__ __attribute__((aligned(16))) St Ks[NS * KBUF];
+  __shared__ __attribute__((aligned(16))) St Vs[NS * VBUF];
+
+  const int tid_all = threadIdx.x;
+  const int sg = __builtin_amdgcn_readfirstlane(tid_all / NT);  // key group of this wave
+  const int tid = tid_all % NT;                                 // thread index inside the key group
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);    // query tile; uniform keeps mask tests scalar
   const int lane = tid & 63;
+  St* const Kg = Ks + sg * KBUF;
+  St* const Vg = Vs + sg * VBUF;
   const int li = lane & 15, g = lane >> 4;
-  const int hr = row_order[blockIdx.x];
-  const int z = blockIdx.y;
+  // 1-D grid, batch fastest: dispatch follows the longest-first order
+  // across the whole batch
+  const int hr = row_order[blockIdx.x / Z];
+  const int z = blockIdx.x % Z;
   const int h = hr / nbr, r = hr % nbr;
   const int k0 = row_ptr[hr], k1 = row_ptr[hr + 1];
   const int64_t zh = (int64_t)z * H + h;
@@ -158,8 +178,8 @@ __global__ __launch_bounds__(BLK * 4) void k_attn(
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const int ch = tid + i * NT;
-      *reinterpret_cast<Vec*>(&Ks[(ch / CPR) * KSTR + (ch % CPR) * VEC]) = kst[i];
-      *reinterpret_cast<Vec*>(&Vs[(ch / CPR) * VSTR + (ch % CPR) * VEC]) = vst[i];
+      *reinterpret_cast<Vec*>(&Kg[(ch / CPR) * KSTR + (ch % CPR) * VEC]) = kst[i];
+      *reinterpret_cast<Vec*>(&Vg[(ch / CPR) * VSTR + (ch % CPR) * VEC]) = vst[i];
     }
   };
 
@@ -168,13 +188,18 @@ __global__ __launch_bounds__(BLK * 4) void k_attn(
 #pragma unroll
   for (int nt = 0; nt < NNT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (k0 < k1) stage_load(col_idx[k0]);
-  for (int kk = k0; kk < k1; ++kk) {
-    const int cb = col_idx[kk];
-    __syncthreads();  // every wave is done with the previous block in LDS
-    stage_store();
+  // key group sg takes blocks k0 + sg, k0 + sg + NS, ... of the row
+  const int nsteps = (k1 - k0 + NS - 1) / NS;
+  if (k0 + sg < k1) stage_load(col_idx[k0 + sg]);
+  for (int step = 0; step < nsteps; ++step) {
+    const int kk = k0 + step * NS + sg;
+    const bool valid = kk < k1;
+    __syncthreads();  // every wave is done with the previous blocks in LDS
+    if (valid) stage_store();
     __syncthreads();
-    if (kk + 1 < k1) stage_load(col_idx[kk + 1]);  // in flight during compute
+    if (kk + NS < k1) stage_load(col_idx[kk + NS]);  // in flight during compute
+    if (!valid) continue;
+    const int cb = col_idx[kk];
 
     if (CAUSAL && cb * BLK > q_lo + 15) continue;  // every key after every query of this wave
     const bool mask_block = CAUSAL && (cb * BLK + BLK - 1 > q_lo);
@@ -183,7 +208,7 @@ __global__ __launch_bounds__(BLK * 4) void k_attn(
     // operands of tile jt+1 are read from LDS while tile jt is multiplied.
     f32x4 s[NJT];
     Vec ka[2][NQ];
-    const St* kbase = &Ks[li * KSTR + g * VEC];
+    const St* kbase = &Kg[li * KSTR + g * VEC];
 #pragma unroll
     for (int u = 0; u < NQ; ++u) ka[0][u] = *reinterpret_cast<const Vec*>(kbase + u * KC);
 #pragma unroll
@@ -247,7 +272,7 @@ __global__ __launch_bounds__(BLK * 4) void k_attn(
     if constexpr (BF) {
       // lane (g, j = 4k + m) points at row 16h + 4g + k, columns 4m.. of
       // the n-tile; it gets back keys 16h + 4g + 0..3 of column nt*16 + li
-      const u16* vb = &Vs[(4 * g + (li >> 2)) * VSTR + 4 * (li & 3)];
+      const u16* vb = &Vg[(4 * g + (li >> 2)) * VSTR + 4 * (li & 3)];
       if constexpr (NJT >= 2) {
         bf16x4 va[2][2][NNT];
 #pragma unroll
@@ -288,7 +313,7 @@ __global__ __launch_bounds__(BLK * 4) void k_attn(
       // one V element per lane and instruction; tile jt+1 is read while
       // tile jt is multiplied
       float va[2][4][NNT];
-      const float* vbase = &Vs[4 * g * VSTR + li];
+      const float* vbase = &Vg[4 * g * VSTR + li];
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
@@ -310,6 +335,39 @@ __global__ __launch_bounds__(BLK * 4) void k_attn(
     }
   }
 
+  // ---- merge the key groups: (m, l, O) of group sg > 0 through LDS into
+  // group 0, rescaling each side by exp2(m_side - m_max)
+  if constexpr (NS > 1) {
+    constexpr int SLOT = 64 * (2 + 4 * NNT);
+    float* red = reinterpret_cast<float*>(Ks);
+    __syncthreads();
+    if (sg > 0) {
+      float* slot = red + ((sg - 1) * NW + wave) * SLOT;
+      slot[lane] = m_run;
+      slot[64 + lane] = l_run;
+#pragma unroll
+      for (int nt = 0; nt < NNT; ++nt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) slot[128 + (nt * 4 + e) * 64 + lane] = o[nt][e];
+    }
+    __syncthreads();
+    if (sg > 0) return;
+#pragma unroll
+    for (int s2 = 1; s2 < NS; ++s2) {
+      const float* slot = red + ((s2 - 1) * NW + wave) * SLOT;
+      const float m2 = slot[lane], l2 = slot[64 + lane];
+      const float m_new = fmaxf(m_run, m2);
+      const float a1 = (m_new == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
+      const float a2 = (m_new == -INFINITY) ? 0.f : fast_exp2(m2 - m_new);
+      l_run = l_run * a1 + l2 * a2;
+#pragma unroll
+      for (int nt = 0; nt < NNT; ++nt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[nt][e] = o[nt][e] * a1 + slot[128 + (nt * 4 + e) * 64 + lane] * a2;
+      m_run = m_new;
+    }
+  }
+
   // ---- finish: l over the 4 lane groups, O = O^T / l, 4 columns per store
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
@@ -326,19 +384,47 @@ __global__ __launch_bounds__(BLK * 4) void k_attn(
   }
 }
 
+template <typename E, int BLK, int D, int NS>
+int launch_ns(const bs_layout* L, const void* Q, const void* K, const void* V, void* O, int Z, float c, bool causal,
+              hipStream_t s) {
+  using St = typename Elem<E>::storage;
+  const dim3 grid(L->H * L->nbr * Z), block(BLK * 4 * NS);
+  if (causal)
+    hipLaunchKernelGGL((k_attn<E, BLK, D, true, NS>), grid, block, 0, s, L->row_ptr, L->col_idx, L->row_order,
+                       (const St*)Q, (const St*)K, (const St*)V, (St*)O, Z, L->H, L->nbr, L->nbc, c);
+  else
+    hipLaunchKernelGGL((k_attn<E, BLK, D, false, NS>), grid, block, 0, s, L->row_ptr, L->col_idx, L->row_order,
+                       (const St*)Q, (const St*)K, (const St*)V, (St*)O, Z, L->H, L->nbr, L->nbc, c);
+  BSA_HIP(hipGetLastError());
+  return BS_OK;
+}
+
+// Key groups per workgroup. With one group, about four workgroups share a
+// CU, so a row of n blocks needs ~4n block-times of its CU while the CU's
+// whole share of the job is Z*nnz/CUs block-times: once the longest row
+// exceeds that, it sets the end of the kernel. NS groups cut the row's own
+// time by NS (the groups run its blocks side by side and merge at the end).
+inline int pick_key_groups(const bs_layout* L, int Z, int max_ns) {
+  const double per_cu = (double)Z * (double)L->nnz / L->num_cus;
+  int ns = 1;
+  while (ns < max_ns && 4.0 * L->max_row_len / ns > per_cu) ns *= 2;
+  return ns;
+}
+
 template <typename E, int BLK, int D>
 int run(const bs_layout* L, const void* Q, const void* K, const void* V, void* O, int Z, float c, bool causal,
         hipStream_t s) {
-  using St = typename Elem<E>::storage;
-  const dim3 grid(L->H * L->nbr, Z), block(BLK * 4);
-  if (causal)
-    hipLaunchKernelGGL((k_attn<E, BLK, D, true>), grid, block, 0, s, L->row_ptr, L->col_idx, L->row_order,
-                       (const St*)Q, (const St*)K, (const St*)V, (St*)O, L->H, L->nbr, L->nbc, c);
-  else
-    hipLaunchKernelGGL((k_attn<E, BLK, D, false>), grid, block, 0, s, L->row_ptr, L->col_idx, L->row_order,
-                       (const St*)Q, (const St*)K, (const St*)V, (St*)O, L->H, L->nbr, L->nbc, c);
-  BSA_HIP(hipGetLastError());
-  return BS_OK;
+  // largest key-group count (up to 4, and 1024 threads) whose LDS fits in 160 KiB
+  constexpr size_t stage = Lds<E, BLK, D>::STAGE;
+  constexpr int max_ns = (BLK <= 64 && 4 * stage <= 160 * 1024) ? 4 : ((BLK <= 64 && 2 * stage <= 160 * 1024) ? 2 : 1);
+  const int ns = pick_key_groups(L, Z, max_ns);
+  if constexpr (max_ns >= 4) {
+    if (ns >= 4) return launch_ns<E, BLK, D, 4>(L, Q, K, V, O, Z, c, causal, s);
+  }
+  if constexpr (max_ns >= 2) {
+    if (ns >= 2) return launch_ns<E, BLK, D, 2>(L, Q, K, V, O, Z, c, causal, s);
+  }
+  return launch_ns<E, BLK, D, 1>(L, Q, K, V, O, Z, c, causal, s);
 }
 
 template <typename E, int D>

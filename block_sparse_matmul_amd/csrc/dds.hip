@@ -43,14 +43,16 @@ __global__ __launch_bounds__(256) void k_dds(const int32_t* __restrict__ col_ptr
                                              const int32_t* __restrict__ col_order,
                                              const typename Elem<E>::storage* __restrict__ A,
                                              const float* __restrict__ S, typename Elem<E>::storage* __restrict__ C,
-                                             int H, int nbr, int nbc, int M, int64_t nnz) {
+                                             int Z, int H, int nbr, int nbc, int M, int64_t nnz) {
   using St = typename Elem<E>::storage;
   using AccT = typename Acc<T>::type;
   constexpr int G = 64 / T, VEC = Elem<E>::VEC, KC = G * VEC, TPB = BLK / T, NR = T * T / 64;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int li = lane % T, g = lane / T;
-  const int hc = col_order[blockIdx.x];
-  const int z = blockIdx.y;
+  // 1-D grid, batch fastest: dispatch follows the longest-first order
+  // across the whole batch
+  const int hc = col_order[blockIdx.x / Z];
+  const int z = blockIdx.x % Z;
   const int h = hc / nbc, c = hc % nbc;
   const int e0 = col_ptr[hc], e1 = col_ptr[hc + 1];
   const int MT = M / T;
@@ -89,11 +91,11 @@ int run(const bs_layout* L, const void* A, const float* S, void* C, int Z, int M
   using St = typename Elem<E>::storage;
   if (BLK >= 32 && M % 32 == 0) {
     constexpr int T = BLK >= 32 ? 32 : 16;
-    hipLaunchKernelGGL((k_dds<E, BLK, T>), dim3(L->H * L->nbc, Z), dim3(256), 0, s, L->col_ptr, L->row_idx,
-                       L->blk_id, L->col_order, (const St*)A, S, (St*)C, L->H, L->nbr, L->nbc, M, L->nnz);
+    hipLaunchKernelGGL((k_dds<E, BLK, T>), dim3(L->H * L->nbc * Z), dim3(256), 0, s, L->col_ptr, L->row_idx,
+                       L->blk_id, L->col_order, (const St*)A, S, (St*)C, Z, L->H, L->nbr, L->nbc, M, L->nnz);
   } else {
-    hipLaunchKernelGGL((k_dds<E, BLK, 16>), dim3(L->H * L->nbc, Z), dim3(256), 0, s, L->col_ptr, L->row_idx,
-                       L->blk_id, L->col_order, (const St*)A, S, (St*)C, L->H, L->nbr, L->nbc, M, L->nnz);
+    hipLaunchKernelGGL((k_dds<E, BLK, 16>), dim3(L->H * L->nbc * Z), dim3(256), 0, s, L->col_ptr, L->row_idx,
+                       L->blk_id, L->col_order, (const St*)A, S, (St*)C, Z, L->H, L->nbr, L->nbc, M, L->nnz);
   }
   BSA_HIP(hipGetLastError());
   return BS_OK;

@@ -54,15 +54,17 @@ template <typename E, int BLK, int T>
 __global__ __launch_bounds__(256) void k_dsd(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
                                              const int32_t* __restrict__ row_order, const float* __restrict__ P,
                                              const typename Elem<E>::storage* __restrict__ B,
-                                             typename Elem<E>::storage* __restrict__ C, int H, int nbr, int nbc,
-                                             int Nd, int64_t nnz) {
+                                             typename Elem<E>::storage* __restrict__ C, int Z, int H, int nbr,
+                                             int nbc, int Nd, int64_t nnz) {
   using St = typename Elem<E>::storage;
   using AccT = typename Acc<T>::type;
   constexpr int G = 64 / T, VEC = Elem<E>::VEC, KC = G * VEC, TPB = BLK / T, NR = T * T / 64;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int li = lane % T, g = lane / T;
-  const int hr = row_order[blockIdx.x];
-  const int z = blockIdx.y;
+  // 1-D grid, batch fastest: dispatch follows the longest-first order
+  // across the whole batch
+  const int hr = row_order[blockIdx.x / Z];
+  const int z = blockIdx.x % Z;
   const int h = hr / nbr, r = hr % nbr;
   const int k0 = row_ptr[hr], k1 = row_ptr[hr + 1];
   const int NT = Nd / T;
@@ -98,11 +100,11 @@ int run(const bs_layout* L, const float* P, const void* B, void* C, int Z, int N
   using St = typename Elem<E>::storage;
   if (BLK >= 32 && Nd % 32 == 0) {
     constexpr int T = BLK >= 32 ? 32 : 16;
-    hipLaunchKernelGGL((k_dsd<E, BLK, T>), dim3(L->H * L->nbr, Z), dim3(256), 0, s, L->row_ptr, L->col_idx,
-                       L->row_order, P, (const St*)B, (St*)C, L->H, L->nbr, L->nbc, Nd, L->nnz);
+    hipLaunchKernelGGL((k_dsd<E, BLK, T>), dim3(L->H * L->nbr * Z), dim3(256), 0, s, L->row_ptr, L->col_idx,
+                       L->row_order, P, (const St*)B, (St*)C, Z, L->H, L->nbr, L->nbc, Nd, L->nnz);
   } else {
-    hipLaunchKernelGGL((k_dsd<E, BLK, 16>), dim3(L->H * L->nbr, Z), dim3(256), 0, s, L->row_ptr, L->col_idx,
-                       L->row_order, P, (const St*)B, (St*)C, L->H, L->nbr, L->nbc, Nd, L->nnz);
+    hipLaunchKernelGGL((k_dsd<E, BLK, 16>), dim3(L->H * L->nbr * Z), dim3(256), 0, s, L->row_ptr, L->col_idx,
+                       L->row_order, P, (const St*)B, (St*)C, Z, L->H, L->nbr, L->nbc, Nd, L->nnz);
   }
   BSA_HIP(hipGetLastError());
   return BS_OK;

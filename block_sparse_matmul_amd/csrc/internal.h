@@ -13,6 +13,7 @@
 // array; all are int32.
 struct bs_layout {
   int device = 0;
+  int num_cus = 256;  // compute units of the device (scheduling heuristics)
   int H = 0, nbr = 0, nbc = 0, block = 0;
   int64_t nnz = 0;
   int max_row_len = 0;  // longest block row (blocks)

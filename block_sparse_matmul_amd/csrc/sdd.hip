@@ -19,14 +19,16 @@ __global__ __launch_bounds__(256) void k_sdd(const int32_t* __restrict__ row_ptr
                                              const int32_t* __restrict__ row_order,
                                              const typename Elem<E>::storage* __restrict__ A,
                                              const typename Elem<E>::storage* __restrict__ B, float* __restrict__ S,
-                                             int H, int nbr, int nbc, int K, int64_t nnz) {
+                                             int Z, int H, int nbr, int nbc, int K, int64_t nnz) {
   using St = typename Elem<E>::storage;
   using AccT = typename Acc<T>::type;
   constexpr int G = 64 / T, VEC = Elem<E>::VEC, KC = G * VEC, TPB = BLK / T, NR = T * T / 64;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int li = lane % T, g = lane / T;
-  const int hr = row_order[blockIdx.x];
-  const int z = blockIdx.y;
+  // 1-D grid, batch fastest: dispatch follows the longest-first order
+  // across the whole batch
+  const int hr = row_order[blockIdx.x / Z];
+  const int z = blockIdx.x % Z;
   const int h = hr / nbr, r = hr % nbr;
   const int k0 = row_ptr[hr], k1 = row_ptr[hr + 1];
   const int items = (k1 - k0) * TPB * TPB;
@@ -61,8 +63,8 @@ template <typename E, int BLK>
 int run(const bs_layout* L, const void* A, const void* B, float* S, int Z, int K, hipStream_t s) {
   using St = typename Elem<E>::storage;
   constexpr int T = BLK >= 32 ? 32 : 16;
-  hipLaunchKernelGGL((k_sdd<E, BLK, T>), dim3(L->H * L->nbr, Z), dim3(256), 0, s, L->row_ptr, L->col_idx,
-                     L->row_order, (const St*)A, (const St*)B, S, L->H, L->nbr, L->nbc, K, L->nnz);
+  hipLaunchKernelGGL((k_sdd<E, BLK, T>), dim3(L->H * L->nbr * Z), dim3(256), 0, s, L->row_ptr, L->col_idx,
+                     L->row_order, (const St*)A, (const St*)B, S, Z, L->H, L->nbr, L->nbc, K, L->nnz);
   BSA_HIP(hipGetLastError());
   return BS_OK;
 }

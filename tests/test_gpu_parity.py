@@ -276,3 +276,23 @@ def test_errors_from_python_binding():
     with pytest.raises(bsa.BsError) as e:
         bsa.attention(Lr, q, k, k, causal=True)
     assert e.value.code == -1
+
+
+@pytest.mark.parametrize("b", [16, 32, 64])
+@pytest.mark.parametrize("Z", [1, 128, 256])
+def test_attention_batch_sweep_all_key_group_schedules(b, Z):
+    """The fused kernel splits a row's blocks over 1, 2 or 4 key groups of
+    waves depending on how long the longest row is against the work per
+    CU; a batch sweep on one layout exercises every choice. Checked on
+    sampled block rows against the oracle."""
+    H, nb, d = 2, 4, 64
+    lay = W.small_random_layout(H, nb, nb, 0.5, 50 + b, force_diagonal=True)
+    announce("attention batch sweep", b, Z)
+    q, k, v = _tensors([(Z, H, nb * b, d)] * 3, 51, "f32")
+    L = bsa.Layout(torch.from_numpy(lay), b)
+    for causal in (False, True):
+        O = bsa.attention(L, to_dev(q), to_dev(k), to_dev(v), 0.125, causal)
+        rows = [(0, 0, 0), (Z - 1, 1, nb - 1), (Z // 2, 0, 2), (Z // 3, 1, 1)]
+        ref = oracle.attention_rows(q, k, v, lay, b, 0.125, causal, rows)
+        for n, (z, h, r) in enumerate(rows):
+            assert max_abs(f64(O[z, h, r * b:(r + 1) * b]), ref[n]) <= TOL["f32"], (z, h, r, causal)
