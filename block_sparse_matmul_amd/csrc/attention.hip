@@ -103,7 +103,13 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_attn(
   constexpr int VEC = Cfg<E>::VEC, KC = Cfg<E>::KC;
   constexpr int NW = BLK / 16, NT = 64 * NW;  // waves / threads of one key group
   constexpr int NQ = D / KC;          // Q fragments per lane
-  constexpr int NJT = BLK / 16;       // 16-key tiles per block
+  // Staging of the next block: split (K during the score product, V during
+  // softmax and P.V, one matrix in registers at a time) where registers are
+  // the limit, else both at the start of a step, hidden by the whole step.
+  constexpr bool SPLIT = BF && D == 128;
+  constexpr int KS = BLK < 64 ? BLK : 64;  // keys per softmax sub-step
+  constexpr int NSUB = BLK / KS;
+  constexpr int NJT = KS / 16;        // 16-key tiles per sub-step
   constexpr int NNT = D / 16;         // 16-column tiles of O
   constexpr int KSTR = Lds<E, BLK, D>::KSTR;
   constexpr int VSTR = Lds<E, BLK, D>::VSTR;
@@ -162,82 +168,132 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_attn(
     }
   }
 
-  // ---- staging registers for one block (K and V, same chunk mapping)
-  Vec kst[KCH], vst[KCH];
-  auto stage_load = [&](int cb) {
-    const int64_t off = (int64_t)cb * BLK * D;
+  // ---- staging of one block: K and V use the same chunk mapping; with
+  // SPLIT they share registers (held at different times)
+  Vec stg[KCH];
+  Vec stv[SPLIT ? 1 : KCH];
+  // per-thread chunk offsets (elements) into a global block and into the
+  // padded LDS rows, computed once
+  int goff[KCH], koff[KCH], voff[KCH];
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int ch = tid + i * NT;
-      const int e = (ch / CPR) * D + (ch % CPR) * VEC;
-      kst[i] = *reinterpret_cast<const Vec*>(Kz + off + e);
-      vst[i] = *reinterpret_cast<const Vec*>(Vz + off + e);
-    }
-  };
-  auto stage_store = [&]() {
+  for (int i = 0; i < KCH; ++i) {
+    const int ch = tid + i * NT;
+    goff[i] = (ch / CPR) * D + (ch % CPR) * VEC;
+    koff[i] = (ch / CPR) * KSTR + (ch % CPR) * VEC;
+    voff[i] = (ch / CPR) * VSTR + (ch % CPR) * VEC;
+  }
+  auto stage_load_to = [&](Vec* r, const St* base, int cb) {
+    const St* src = base + (int64_t)cb * BLK * D;  // uniform
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int ch = tid + i * NT;
-      *reinterpret_cast<Vec*>(&Kg[(ch / CPR) * KSTR + (ch % CPR) * VEC]) = kst[i];
-      *reinterpret_cast<Vec*>(&Vg[(ch / CPR) * VSTR + (ch % CPR) * VEC]) = vst[i];
-    }
+    for (int i = 0; i < KCH; ++i) r[i] = *reinterpret_cast<const Vec*>(src + goff[i]);
   };
+  auto stage_store_from = [&](const Vec* r, St* dst, const int* off) {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) *reinterpret_cast<Vec*>(&dst[off[i]]) = r[i];
+  };
+  auto stage_load = [&](const St* base, int cb) { stage_load_to(stg, base, cb); };
+  auto stage_store = [&](St* dst, const int* off) { stage_store_from(stg, dst, off); };
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 o[NNT];
 #pragma unroll
   for (int nt = 0; nt < NNT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // key group sg takes blocks k0 + sg, k0 + sg + NS, ... of the row
+  // key group sg takes blocks k0 + sg, k0 + sg + NS, ... of the row.
+  // Without SPLIT a step is: barrier, store K and V of this block, barrier,
+  // load K and V of the next block (in flight during the compute), compute.
+  // With SPLIT: K of the next block is loaded during the score product and
+  // stored once every wave is past it; V of the next block is loaded then
+  // and stored once every wave is past P.V.
   const int nsteps = (k1 - k0 + NS - 1) / NS;
-  if (k0 + sg < k1) stage_load(col_idx[k0 + sg]);
+  if (k0 + sg < k1) {
+    stage_load(Kz, col_idx[k0 + sg]);
+    if constexpr (SPLIT) {
+      stage_store(Kg, koff);
+      stage_load(Vz, col_idx[k0 + sg]);
+      stage_store(Vg, voff);
+    } else {
+      stage_load_to(stv, Vz, col_idx[k0 + sg]);
+    }
+  }
+  if constexpr (SPLIT) __syncthreads();
   for (int step = 0; step < nsteps; ++step) {
     const int kk = k0 + step * NS + sg;
     const bool valid = kk < k1;
-    __syncthreads();  // every wave is done with the previous blocks in LDS
-    if (valid) stage_store();
-    __syncthreads();
-    if (kk + NS < k1) stage_load(col_idx[kk + NS]);  // in flight during compute
-    if (!valid) continue;
-    const int cb = col_idx[kk];
-
-    if (CAUSAL && cb * BLK > q_lo + 15) continue;  // every key after every query of this wave
+    const bool has_next = kk + NS < k1;
+    const int cb_next = has_next ? col_idx[kk + NS] : 0;
+    if constexpr (!SPLIT) {
+      __syncthreads();  // every wave is done with the previous blocks in LDS
+      if (valid) {
+        stage_store(Kg, koff);
+        stage_store_from(stv, Vg, voff);
+      }
+      __syncthreads();
+      if (has_next) {
+        stage_load(Kz, cb_next);
+        stage_load_to(stv, Vz, cb_next);
+      }
+    } else {
+      if (has_next) stage_load(Kz, cb_next);
+    }
+    const int cb = valid ? col_idx[kk] : 0;
+    // blocks whose every key is after every query of this wave add nothing
+    const bool compute = valid && !(CAUSAL && cb * BLK > q_lo + 15);
     const bool mask_block = CAUSAL && (cb * BLK + BLK - 1 > q_lo);
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub) {
+    const int kofs = sub * KS;  // first key of this sub-step within the block
 
-    // S^T tiles: s[jt][rr] = score(query li, key 16 jt + 4 g + rr). The K
+    // S^T tiles: s[jt][rr] = score(query li, key kofs + 16 jt + 4 g + rr). The K
     // operands of tile jt+1 are read from LDS while tile jt is multiplied.
     f32x4 s[NJT];
-    Vec ka[2][NQ];
-    const St* kbase = &Kg[li * KSTR + g * VEC];
+    const St* kbase = &Kg[(kofs + li) * KSTR + g * VEC];
+    if (!compute) {
+    } else if constexpr (BF) {
 #pragma unroll
-    for (int u = 0; u < NQ; ++u) ka[0][u] = *reinterpret_cast<const Vec*>(kbase + u * KC);
+      for (int jt = 0; jt < NJT; ++jt) {
+        s[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int jt = 0; jt < NJT; ++jt) {
-      if (jt + 1 < NJT) {
+        for (int u = 0; u < NQ; ++u) {
+          const Vec a = *reinterpret_cast<const Vec*>(kbase + 16 * jt * KSTR + u * KC);
+          s[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[u], s[jt], 0, 0, 0);
+        }
+      }
+    } else {
+      Vec ka[2][NQ];
+#pragma unroll
+      for (int u = 0; u < NQ; ++u) ka[0][u] = *reinterpret_cast<const Vec*>(kbase + u * KC);
+#pragma unroll
+      for (int jt = 0; jt < NJT; ++jt) {
+        if (jt + 1 < NJT) {
+#pragma unroll
+          for (int u = 0; u < NQ; ++u)
+            ka[(jt + 1) & 1][u] = *reinterpret_cast<const Vec*>(kbase + 16 * (jt + 1) * KSTR + u * KC);
+        }
+        s[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < NQ; ++u)
-          ka[(jt + 1) & 1][u] = *reinterpret_cast<const Vec*>(kbase + 16 * (jt + 1) * KSTR + u * KC);
-      }
-      s[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int u = 0; u < NQ; ++u) {
-        if constexpr (BF) {
-          s[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[jt & 1][u], qf[u], s[jt], 0, 0, 0);
-        } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             s[jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[jt & 1][u][e], qf[u][e], s[jt], 0, 0, 0);
-        }
       }
     }
 
+    if (SPLIT && sub == NSUB - 1) {
+      __syncthreads();  // every wave is past the score product: K of the next block may land
+      if (has_next) {
+        stage_store(Kg, koff);
+        stage_load(Vz, cb_next);
+      }
+    }
+    if (compute) {
     // mask and block max (raw scores; cs > 0)
     if (mask_block) {
 #pragma unroll
       for (int jt = 0; jt < NJT; ++jt)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
-          if (cb * BLK + 16 * jt + 4 * g + rr > q_index) s[jt][rr] = -INFINITY;
+          if (cb * BLK + kofs + 16 * jt + 4 * g + rr > q_index) s[jt][rr] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -272,29 +328,19 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_attn(
     if constexpr (BF) {
       // lane (g, j = 4k + m) points at row 16h + 4g + k, columns 4m.. of
       // the n-tile; it gets back keys 16h + 4g + 0..3 of column nt*16 + li
-      const u16* vb = &Vg[(4 * g + (li >> 2)) * VSTR + 4 * (li & 3)];
+      const u16* vb = &Vg[(kofs + 4 * g + (li >> 2)) * VSTR + 4 * (li & 3)];
       if constexpr (NJT >= 2) {
-        bf16x4 va[2][2][NNT];
-#pragma unroll
-        for (int nt = 0; nt < NNT; ++nt) {
-          va[0][0][nt] = lds_read_tr16(vb + nt * 16);
-          va[0][1][nt] = lds_read_tr16(vb + 16 * VSTR + nt * 16);
-        }
+        // operands read right before use: the bf16 kernel is register bound
+        // (two 8-wave workgroups per CU need <= 128 VGPRs)
 #pragma unroll
         for (int jp = 0; jp < NJT / 2; ++jp) {
-          if (jp + 1 < NJT / 2) {
-#pragma unroll
-            for (int nt = 0; nt < NNT; ++nt) {
-              va[(jp + 1) & 1][0][nt] = lds_read_tr16(vb + (32 * (jp + 1)) * VSTR + nt * 16);
-              va[(jp + 1) & 1][1][nt] = lds_read_tr16(vb + (32 * (jp + 1) + 16) * VSTR + nt * 16);
-            }
-          }
           const bf16x8 pb = {to_bf16(s[2 * jp][0]),     to_bf16(s[2 * jp][1]),     to_bf16(s[2 * jp][2]),
                              to_bf16(s[2 * jp][3]),     to_bf16(s[2 * jp + 1][0]), to_bf16(s[2 * jp + 1][1]),
                              to_bf16(s[2 * jp + 1][2]), to_bf16(s[2 * jp + 1][3])};
 #pragma unroll
           for (int nt = 0; nt < NNT; ++nt) {
-            const bf16x4 a0 = va[jp & 1][0][nt], a1 = va[jp & 1][1][nt];
+            const bf16x4 a0 = lds_read_tr16(vb + (32 * jp) * VSTR + nt * 16);
+            const bf16x4 a1 = lds_read_tr16(vb + (32 * jp + 16) * VSTR + nt * 16);
             const bf16x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
             o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[nt], 0, 0, 0);
           }
@@ -313,7 +359,7 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_attn(
       // one V element per lane and instruction; tile jt+1 is read while
       // tile jt is multiplied
       float va[2][4][NNT];
-      const float* vbase = &Vg[4 * g * VSTR + li];
+      const float* vbase = &Vg[(kofs + 4 * g) * VSTR + li];
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
@@ -332,6 +378,15 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_attn(
           for (int nt = 0; nt < NNT; ++nt)
             o[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va[jt & 1][rr][nt], s[jt][rr], o[nt], 0, 0, 0);
       }
+    }
+    }  // compute
+    }  // sub-step
+    if constexpr (SPLIT) {
+      __syncthreads();  // every wave is past P.V: V of the next block may land
+      if (has_next) stage_store(Vg, voff);
+      // with sub-steps, the first P.V of the next block precedes its
+      // mid-block barrier, so V must be visible before the next step starts
+      if constexpr (NSUB > 1) __syncthreads();
     }
   }
 

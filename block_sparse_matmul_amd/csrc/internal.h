@@ -7,7 +7,7 @@
 
 #include <string>
 
-#include "../../include/bsattn.h"
+#include "bsattn.h"
 
 // Device-resident tables of one layout. One allocation (`mem`) holds every
 // array; all are int32.
