@@ -1,22 +1,27 @@
+// Row-block kernel shared by the fused attention and the fast SDD and DSD.
+//
 // Fused block-sparse attention: SDD -> block-sparse softmax -> DSD in one
 // kernel (the composition of Triton issue 117, "question on blocksparse"),
 // with the streaming softmax of the Triton tutorial (Puzzle 8, online
 // softmax; Puzzle 9, simple FlashAttention): a running row max m and sum l,
 // the partial output rescaled by exp(m_old - m_new) when the reference max
 // moves, and one division by l at the end (the same value as normalising at
-// every step).
+// every step). The same kernel, with the softmax and one of the two products
+// compiled out, is the SDD (scores written out) and the DSD (P read in).
 //
-// Work decomposition. One workgroup per (batch, head, block row), rows
-// taken longest first; b/16 waves, wave w owning query rows 16w..16w+15 of
-// the block. The stored blocks of the row are visited in order; each is
-// staged once into LDS for all waves, K and V both row-major (contiguous
-// 16-byte writes), and the next block is already in flight into registers
-// while the current one is computed. Row strides were chosen by measuring
-// the operand read patterns on gfx950: K rows padded to 32 mod 256 bytes,
-// fp32 V rows to 16 mod 64 bytes, bf16 V rows to 32 mod 256 bytes; every
-// operand read below is then free of bank conflicts.
+// Work decomposition. One workgroup per (batch, head, block row); a 1-D grid
+// with the batch index fastest, so dispatch follows the longest-first row
+// order across the whole job. b/16 waves per key group, wave w owning query
+// rows 16w..16w+15 of the block; NS key groups deal the row's blocks among
+// themselves (k0 + sg, k0 + sg + NS, ...) and merge at the end. Each stored
+// block is staged once into LDS for the waves of its group, K and V both
+// row-major (contiguous 16-byte writes), and the next block is already in
+// flight into registers while the current one is computed. Row strides were
+// chosen by measuring the operand read patterns on gfx950; every operand
+// read below is free of bank conflicts.
 //
-// Per block and wave, with 16x16 MFMA tiles (fp32 16x16x4, bf16 16x16x32):
+// Per 64-key sub-step and wave, with 16x16 MFMA tiles (fp32 16x16x4, bf16
+// 16x16x32):
 //   S^T = K_c Q^T     A = K rows from LDS, B = the wave's Q rows (registers,
 //                     loaded once). In the accumulator every lane then owns
 //                     ONE query row (its column) and 4 keys per 16-key tile,
@@ -37,6 +42,9 @@
 //                     ds_read_b64_tr_b16 (each 16-lane group reads a 4-key x
 //                     16-column patch and every lane receives the 4 keys of
 //                     its own column), so V never needs a transposed copy.
+// The S^T register layout is also the layout of a row-major b x b block read
+// with one 16-byte load per lane (row li, columns 16 jt + 4 g ..), which is
+// how the SDD stores its scores and the DSD loads its P.
 // bf16: P is rounded to bf16 (RNE) for P.V, O once at the end.
 #include <math.h>
 
@@ -50,6 +58,8 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kTau = 8.0f;  // lazy-rescale headroom, log2 units
+
+enum Mode { MODE_ATTN = 0, MODE_SDD = 1, MODE_DSD = 2 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -72,12 +82,14 @@ struct Cfg<bf16_t> {
 // operand reads of the kernel: K rows 32 mod 256 bytes; V rows 16 mod 64
 // bytes (fp32, one 4-byte read per lane) or 32 mod 256 bytes (bf16,
 // transposing 8-byte reads)
-template <typename E, int BLK, int D>
+template <typename E, int BLK, int D, int MODE>
 struct Lds {
   using St = typename Elem<E>::storage;
   static constexpr int KSTR = D + 32 / (int)sizeof(St);
   static constexpr int VSTR = std::is_same<E, bf16_t>::value ? D + 16 : D + 4;
-  static constexpr size_t STAGE = (size_t)BLK * (KSTR + VSTR) * sizeof(St);  // bytes per key group
+  static constexpr int KBUF = MODE == MODE_DSD ? 0 : BLK * KSTR;  // elements per key group
+  static constexpr int VBUF = MODE == MODE_SDD ? 0 : BLK * VSTR;
+  static constexpr size_t STAGE = (size_t)(KBUF + VBUF) * sizeof(St);  // bytes per key group
 };
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -91,38 +103,48 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const u16* p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
-template <typename E, int BLK, int D, bool CAUSAL, int NS>
-__global__ __launch_bounds__(BLK * 4 * NS) void k_attn(
+// Q, K, V, O: [Z][H][N][D] dense operands; S: [Z][nnz][BLK][BLK] fp32 block
+// values (SDD output, DSD input). MODE_ATTN uses Q, K, V -> O; MODE_SDD
+// uses Q (= A), K (= B) -> S; MODE_DSD uses S (= P), V (= B) -> O (= C).
+template <typename E, int BLK, int D, bool CAUSAL, int NS, int MODE>
+__global__ __launch_bounds__(BLK * 4 * NS) void k_rowblock(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, const int32_t* __restrict__ row_order,
     const typename Elem<E>::storage* __restrict__ Q, const typename Elem<E>::storage* __restrict__ K,
-    const typename Elem<E>::storage* __restrict__ V, typename Elem<E>::storage* __restrict__ O, int Z, int H,
-    int nbr, int nbc, float c) {
+    const typename Elem<E>::storage* __restrict__ V, typename Elem<E>::storage* __restrict__ O,
+    float* __restrict__ S, int Z, int H, int nbr, int nbc, int64_t nnz, float c) {
   using St = typename Elem<E>::storage;
   using Vec = typename Cfg<E>::Vec;
   constexpr bool BF = std::is_same<E, bf16_t>::value;
+  constexpr bool ATTN = MODE == MODE_ATTN;
+  constexpr bool HASK = MODE != MODE_DSD;  // score product (Q, K staged)
+  constexpr bool HASV = MODE != MODE_SDD;  // P.V product (V staged)
   constexpr int VEC = Cfg<E>::VEC, KC = Cfg<E>::KC;
   constexpr int NW = BLK / 16, NT = 64 * NW;  // waves / threads of one key group
-  constexpr int NQ = D / KC;          // Q fragments per lane
+  constexpr int NQ = D / KC;                  // Q fragments per lane
   // Staging of the next block: split (K during the score product, V during
   // softmax and P.V, one matrix in registers at a time) where registers are
   // the limit, else both at the start of a step, hidden by the whole step.
-  constexpr bool SPLIT = BF && D == 128;
-  constexpr int KS = BLK < 64 ? BLK : 64;  // keys per softmax sub-step
+  constexpr bool SPLIT = ATTN && BF && D == 128;
+  constexpr int KS = BLK < 64 ? BLK : 64;  // keys per sub-step
   constexpr int NSUB = BLK / KS;
-  constexpr int NJT = KS / 16;        // 16-key tiles per sub-step
-  constexpr int NNT = D / 16;         // 16-column tiles of O
-  constexpr int KSTR = Lds<E, BLK, D>::KSTR;
-  constexpr int VSTR = Lds<E, BLK, D>::VSTR;
-  constexpr int CPR = D / VEC;        // 16-byte chunks per row
-  constexpr int KCH = BLK * CPR / NT; // chunks per thread and matrix (D / (4 VEC))
+  constexpr int NJT = KS / 16;             // 16-key tiles per sub-step
+  constexpr int NNT = D / 16;              // 16-column tiles of O
+  constexpr int KSTR = Lds<E, BLK, D, MODE>::KSTR;
+  constexpr int VSTR = Lds<E, BLK, D, MODE>::VSTR;
+  constexpr int KBUF = Lds<E, BLK, D, MODE>::KBUF, VBUF = Lds<E, BLK, D, MODE>::VBUF;
+  constexpr int CPR = D / VEC;         // 16-byte chunks per row
+  constexpr int KCH = BLK * CPR / NT;  // chunks per thread and matrix (D / (4 VEC))
   static_assert(KCH >= 1 && BLK * CPR % NT == 0, "staging");
+  constexpr int SLOT = 64 * ((ATTN ? 2 : 0) + 4 * NNT);  // floats per wave for the final merge
+  // one LDS array: the K stages of the NS groups, then their V stages; the
+  // final merge of the groups reuses it from the start
+  constexpr int MERGE_ELEMS = (MODE == MODE_SDD || NS == 1) ? 0 : (NS - 1) * NW * SLOT * 4 / (int)sizeof(St);
+  constexpr int LDS_ELEMS = NS * (KBUF + VBUF) > MERGE_ELEMS ? NS * (KBUF + VBUF) : MERGE_ELEMS;
+  static_assert((KBUF * sizeof(St)) % 16 == 0, "16-byte aligned V stages");
 
-  constexpr int KBUF = BLK * KSTR, VBUF = BLK * VSTR;  // one stage of one key group
-  constexpr int MERGE = NS > 1 ? (NS - 1) * NW * 64 * (2 + 4 * NNT) : 0;  // floats for the final merge
-  static_assert((size_t)MERGE * 4 <= (size_t)NS * (KBUF + VBUF) * sizeof(St), "merge area");
-
-  __shared__ __attribute__((aligned(16))) St Ks[NS * KBUF];
-  __shared__ __attribute__((aligned(16))) St Vs[NS * VBUF];
+  __shared__ __attribute__((aligned(16))) St lds[LDS_ELEMS];
+  St* const Ks = lds;
+  St* const Vs = lds + NS * KBUF;
 
   const int tid_all = threadIdx.x;
   const int sg = __builtin_amdgcn_readfirstlane(tid_all / NT);  // key group of this wave
@@ -132,8 +154,6 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_attn(
   St* const Kg = Ks + sg * KBUF;
   St* const Vg = Vs + sg * VBUF;
   const int li = lane & 15, g = lane >> 4;
-  // 1-D grid, batch fastest: dispatch follows the longest-first order
-  // across the whole batch
   const int hr = row_order[blockIdx.x / Z];
   const int z = blockIdx.x % Z;
   const int h = hr / nbr, r = hr % nbr;
@@ -144,34 +164,36 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_attn(
   const int q_index = q_lo + li;         // this lane's query row
   const St* Kz = K + zh * Nk * D;
   const St* Vz = V + zh * Nk * D;
+  // this lane's row of a stored block in S: row wave*16 + li, columns 4g..
+  const int64_t s_lane = (int64_t)(wave * 16 + li) * BLK + 4 * g;
 
-  // ---- Q as B fragments; fp32 folds scale*log2(e) in, bf16 only its sign
-  Vec qf[NQ];
-  float cs;
-  {
+  // ---- Q as B fragments; attention folds scale*log2(e) in (fp32) or only
+  // its sign (bf16, exact); the SDD uses Q as is
+  Vec qf[HASK ? NQ : 1];
+  float cs = 1.f;
+  if constexpr (HASK) {
     const St* pq = Q + (zh * Nq + q_index) * D + g * VEC;
 #pragma unroll
     for (int u = 0; u < NQ; ++u) qf[u] = *reinterpret_cast<const Vec*>(pq + u * KC);
-    if constexpr (BF) {
+    if constexpr (ATTN && BF) {
       const float sgn = c > 0.f ? 1.f : (c < 0.f ? -1.f : 0.f);
       if (sgn != 1.f) {
 #pragma unroll
         for (int u = 0; u < NQ; ++u)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) qf[u][e] = to_bf16((float)qf[u][e] * sgn);  // exact
+          for (int e = 0; e < 8; ++e) qf[u][e] = to_bf16((float)qf[u][e] * sgn);
       }
       cs = (c == 0.f) ? 1.f : fabsf(c);
-    } else {
+    } else if constexpr (ATTN) {
 #pragma unroll
       for (int u = 0; u < NQ; ++u) qf[u] *= c;
-      cs = 1.f;
     }
   }
 
   // ---- staging of one block: K and V use the same chunk mapping; with
   // SPLIT they share registers (held at different times)
   Vec stg[KCH];
-  Vec stv[SPLIT ? 1 : KCH];
+  Vec stv[(HASK && HASV && !SPLIT) ? KCH : 1];
   // per-thread chunk offsets (elements) into a global block and into the
   // padded LDS rows, computed once
   int goff[KCH], koff[KCH], voff[KCH];
@@ -182,38 +204,45 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_attn(
     koff[i] = (ch / CPR) * KSTR + (ch % CPR) * VEC;
     voff[i] = (ch / CPR) * VSTR + (ch % CPR) * VEC;
   }
-  auto stage_load_to = [&](Vec* r, const St* base, int cb) {
+  auto stage_load_to = [&](Vec* rg, const St* base, int cb) {
     const St* src = base + (int64_t)cb * BLK * D;  // uniform
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) r[i] = *reinterpret_cast<const Vec*>(src + goff[i]);
+    for (int i = 0; i < KCH; ++i) rg[i] = *reinterpret_cast<const Vec*>(src + goff[i]);
   };
-  auto stage_store_from = [&](const Vec* r, St* dst, const int* off) {
+  auto stage_store_from = [&](const Vec* rg, St* dst, const int* off) {
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) *reinterpret_cast<Vec*>(&dst[off[i]]) = r[i];
+    for (int i = 0; i < KCH; ++i) *reinterpret_cast<Vec*>(&dst[off[i]]) = rg[i];
   };
-  auto stage_load = [&](const St* base, int cb) { stage_load_to(stg, base, cb); };
-  auto stage_store = [&](St* dst, const int* off) { stage_store_from(stg, dst, off); };
+  // the next block's matrices in registers, without SPLIT: K in stg and V
+  // in stv (attention), or the one matrix in stg (SDD: K, DSD: V)
+  auto load_next = [&](int cb) {
+    if constexpr (HASK) stage_load_to(stg, Kz, cb);
+    if constexpr (HASV) stage_load_to(HASK ? stv : stg, Vz, cb);
+  };
+  auto store_next = [&]() {
+    if constexpr (HASK) stage_store_from(stg, Kg, koff);
+    if constexpr (HASV) stage_store_from(HASK ? stv : stg, Vg, voff);
+  };
 
   float m_run = -INFINITY, l_run = 0.f;
-  f32x4 o[NNT];
+  f32x4 o[HASV ? NNT : 1];
 #pragma unroll
-  for (int nt = 0; nt < NNT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int nt = 0; nt < (HASV ? NNT : 1); ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // key group sg takes blocks k0 + sg, k0 + sg + NS, ... of the row.
-  // Without SPLIT a step is: barrier, store K and V of this block, barrier,
-  // load K and V of the next block (in flight during the compute), compute.
-  // With SPLIT: K of the next block is loaded during the score product and
-  // stored once every wave is past it; V of the next block is loaded then
-  // and stored once every wave is past P.V.
+  // Without SPLIT a step is: barrier, store the staged block, barrier, load
+  // the next block (in flight during the compute), compute. With SPLIT: K of
+  // the next block is loaded during the score product and stored once every
+  // wave is past it; V of the next block is loaded then and stored once
+  // every wave is past P.V.
   const int nsteps = (k1 - k0 + NS - 1) / NS;
   if (k0 + sg < k1) {
-    stage_load(Kz, col_idx[k0 + sg]);
     if constexpr (SPLIT) {
-      stage_store(Kg, koff);
-      stage_load(Vz, col_idx[k0 + sg]);
-      stage_store(Vg, voff);
+      stage_load_to(stg, Kz, col_idx[k0 + sg]);
+      stage_store_from(stg, Kg, koff);
+      stage_load_to(stg, Vz, col_idx[k0 + sg]);
+      stage_store_from(stg, Vg, voff);
     } else {
-      stage_load_to(stv, Vz, col_idx[k0 + sg]);
+      load_next(col_idx[k0 + sg]);
     }
   }
   if constexpr (SPLIT) __syncthreads();
@@ -224,209 +253,240 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_attn(
     const int cb_next = has_next ? col_idx[kk + NS] : 0;
     if constexpr (!SPLIT) {
       __syncthreads();  // every wave is done with the previous blocks in LDS
-      if (valid) {
-        stage_store(Kg, koff);
-        stage_store_from(stv, Vg, voff);
-      }
+      if (valid) store_next();
       __syncthreads();
-      if (has_next) {
-        stage_load(Kz, cb_next);
-        stage_load_to(stv, Vz, cb_next);
-      }
+      if (has_next) load_next(cb_next);
     } else {
-      if (has_next) stage_load(Kz, cb_next);
+      if (has_next) stage_load_to(stg, Kz, cb_next);
     }
     const int cb = valid ? col_idx[kk] : 0;
     // blocks whose every key is after every query of this wave add nothing
-    const bool compute = valid && !(CAUSAL && cb * BLK > q_lo + 15);
-    const bool mask_block = CAUSAL && (cb * BLK + BLK - 1 > q_lo);
+    const bool compute = valid && !(ATTN && CAUSAL && cb * BLK > q_lo + 15);
+    const bool mask_block = ATTN && CAUSAL && (cb * BLK + BLK - 1 > q_lo);
+    float* const s_blk = S + ((int64_t)z * nnz + kk) * (BLK * BLK) + s_lane;
+
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub) {
-    const int kofs = sub * KS;  // first key of this sub-step within the block
+      const int kofs = sub * KS;  // first key of this sub-step within the block
+      // s[jt][rr] = score of (query li, key kofs + 16 jt + 4 g + rr)
+      f32x4 s[NJT];
 
-    // S^T tiles: s[jt][rr] = score(query li, key kofs + 16 jt + 4 g + rr). The K
-    // operands of tile jt+1 are read from LDS while tile jt is multiplied.
-    f32x4 s[NJT];
-    const St* kbase = &Kg[(kofs + li) * KSTR + g * VEC];
-    if (!compute) {
-    } else if constexpr (BF) {
+      // ---- S^T = K Q^T (attention, SDD); the K operands of tile jt+1 are
+      // read from LDS while tile jt is multiplied (fp32)
+      if constexpr (HASK) {
+        const St* kbase = &Kg[(kofs + li) * KSTR + g * VEC];
+        if (!compute) {
+        } else if constexpr (BF) {
 #pragma unroll
-      for (int jt = 0; jt < NJT; ++jt) {
-        s[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int jt = 0; jt < NJT; ++jt) {
+            s[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < NQ; ++u) {
-          const Vec a = *reinterpret_cast<const Vec*>(kbase + 16 * jt * KSTR + u * KC);
-          s[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[u], s[jt], 0, 0, 0);
+            for (int u = 0; u < NQ; ++u) {
+              const Vec a = *reinterpret_cast<const Vec*>(kbase + 16 * jt * KSTR + u * KC);
+              s[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[u], s[jt], 0, 0, 0);
+            }
+          }
+        } else {
+          Vec ka[2][NQ];
+#pragma unroll
+          for (int u = 0; u < NQ; ++u) ka[0][u] = *reinterpret_cast<const Vec*>(kbase + u * KC);
+#pragma unroll
+          for (int jt = 0; jt < NJT; ++jt) {
+            if (jt + 1 < NJT) {
+#pragma unroll
+              for (int u = 0; u < NQ; ++u)
+                ka[(jt + 1) & 1][u] = *reinterpret_cast<const Vec*>(kbase + 16 * (jt + 1) * KSTR + u * KC);
+            }
+            s[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < NQ; ++u)
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                s[jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[jt & 1][u][e], qf[u][e], s[jt], 0, 0, 0);
+          }
         }
       }
-    } else {
-      Vec ka[2][NQ];
+
+      if constexpr (MODE == MODE_SDD) {
+        // the raw scores are the output
+        if (compute) {
 #pragma unroll
-      for (int u = 0; u < NQ; ++u) ka[0][u] = *reinterpret_cast<const Vec*>(kbase + u * KC);
-#pragma unroll
-      for (int jt = 0; jt < NJT; ++jt) {
-        if (jt + 1 < NJT) {
-#pragma unroll
-          for (int u = 0; u < NQ; ++u)
-            ka[(jt + 1) & 1][u] = *reinterpret_cast<const Vec*>(kbase + 16 * (jt + 1) * KSTR + u * KC);
+          for (int jt = 0; jt < NJT; ++jt) *reinterpret_cast<f32x4*>(s_blk + kofs + 16 * jt) = s[jt];
         }
-        s[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int u = 0; u < NQ; ++u)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            s[jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[jt & 1][u][e], qf[u][e], s[jt], 0, 0, 0);
+        continue;
       }
-    }
+      if constexpr (MODE == MODE_DSD) {
+        // P block rows straight into the score-register layout
+        if (compute) {
+#pragma unroll
+          for (int jt = 0; jt < NJT; ++jt) s[jt] = *reinterpret_cast<const f32x4*>(s_blk + kofs + 16 * jt);
+        }
+      }
 
-    if (SPLIT && sub == NSUB - 1) {
-      __syncthreads();  // every wave is past the score product: K of the next block may land
-      if (has_next) {
-        stage_store(Kg, koff);
-        stage_load(Vz, cb_next);
+      if (SPLIT && sub == NSUB - 1) {
+        __syncthreads();  // every wave is past the score product: K of the next block may land
+        if (has_next) {
+          stage_store_from(stg, Kg, koff);
+          stage_load_to(stg, Vz, cb_next);
+        }
       }
-    }
-    if (compute) {
-    // mask and block max (raw scores; cs > 0)
-    if (mask_block) {
-#pragma unroll
-      for (int jt = 0; jt < NJT; ++jt)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          if (cb * BLK + kofs + 16 * jt + 4 * g + rr > q_index) s[jt][rr] = -INFINITY;
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int jt = 0; jt < NJT; ++jt)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) mx = fmaxf(mx, s[jt][rr]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_blk = mx * cs;
-    const bool upd = m_blk > m_run + kTau;
-    if (__builtin_amdgcn_ballot_w64(upd) != 0) {  // wave-uniform
-      const float m_new = upd ? m_blk : m_run;
-      const float alpha = fast_exp2(m_run - m_new);  // 0 when m_run = -inf
-      l_run *= alpha;
-#pragma unroll
-      for (int nt = 0; nt < NNT; ++nt) o[nt] *= alpha;
-      m_run = m_new;
-    }
-    const float m_sub = (m_run == -INFINITY) ? 0.f : m_run;
-    float ls = 0.f;
-#pragma unroll
-    for (int jt = 0; jt < NJT; ++jt)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const float p = fast_exp2(fmaf(s[jt][rr], cs, -m_sub));
-        s[jt][rr] = p;
-        ls += p;
-      }
-    l_run += ls;
+      if (!compute) continue;
 
-    // O^T[n][query] += V^T[n][keys] P^T[keys][query]
-    if constexpr (BF) {
-      // lane (g, j = 4k + m) points at row 16h + 4g + k, columns 4m.. of
-      // the n-tile; it gets back keys 16h + 4g + 0..3 of column nt*16 + li
-      const u16* vb = &Vg[(kofs + 4 * g + (li >> 2)) * VSTR + 4 * (li & 3)];
-      if constexpr (NJT >= 2) {
-        // operands read right before use: the bf16 kernel is register bound
-        // (two 8-wave workgroups per CU need <= 128 VGPRs)
+      if constexpr (ATTN) {
+        // ---- mask, block max (raw scores; cs > 0), lazy rescale, exp2
+        if (mask_block) {
 #pragma unroll
-        for (int jp = 0; jp < NJT / 2; ++jp) {
-          const bf16x8 pb = {to_bf16(s[2 * jp][0]),     to_bf16(s[2 * jp][1]),     to_bf16(s[2 * jp][2]),
-                             to_bf16(s[2 * jp][3]),     to_bf16(s[2 * jp + 1][0]), to_bf16(s[2 * jp + 1][1]),
-                             to_bf16(s[2 * jp + 1][2]), to_bf16(s[2 * jp + 1][3])};
+          for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+              if (cb * BLK + kofs + 16 * jt + 4 * g + rr > q_index) s[jt][rr] = -INFINITY;
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) mx = fmaxf(mx, s[jt][rr]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_blk = mx * cs;
+        const bool upd = m_blk > m_run + kTau;
+        if (__builtin_amdgcn_ballot_w64(upd) != 0) {  // wave-uniform
+          const float m_new = upd ? m_blk : m_run;
+          const float alpha = fast_exp2(m_run - m_new);  // 0 when m_run = -inf
+          l_run *= alpha;
+#pragma unroll
+          for (int nt = 0; nt < NNT; ++nt) o[nt] *= alpha;
+          m_run = m_new;
+        }
+        const float m_sub = (m_run == -INFINITY) ? 0.f : m_run;
+        float ls = 0.f;
+#pragma unroll
+        for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const float p = fast_exp2(fmaf(s[jt][rr], cs, -m_sub));
+            s[jt][rr] = p;
+            ls += p;
+          }
+        l_run += ls;
+      }
+
+      // ---- O^T[n][query] += V^T[n][keys] P^T[keys][query]
+      if constexpr (BF) {
+        // lane (g, j = 4k + m) points at row 16h + 4g + k, columns 4m.. of
+        // the n-tile; it gets back keys 16h + 4g + 0..3 of column nt*16 + li
+        const u16* vb = &Vg[(kofs + 4 * g + (li >> 2)) * VSTR + 4 * (li & 3)];
+        if constexpr (NJT >= 2) {
+          // operands read right before use: the bf16 kernel is register bound
+          // (two 8-wave workgroups per CU need <= 128 VGPRs)
+#pragma unroll
+          for (int jp = 0; jp < NJT / 2; ++jp) {
+            const bf16x8 pb = {to_bf16(s[2 * jp][0]),     to_bf16(s[2 * jp][1]),     to_bf16(s[2 * jp][2]),
+                               to_bf16(s[2 * jp][3]),     to_bf16(s[2 * jp + 1][0]), to_bf16(s[2 * jp + 1][1]),
+                               to_bf16(s[2 * jp + 1][2]), to_bf16(s[2 * jp + 1][3])};
+#pragma unroll
+            for (int nt = 0; nt < NNT; ++nt) {
+              const bf16x4 a0 = lds_read_tr16(vb + (32 * jp) * VSTR + nt * 16);
+              const bf16x4 a1 = lds_read_tr16(vb + (32 * jp + 16) * VSTR + nt * 16);
+              const bf16x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+              o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[nt], 0, 0, 0);
+            }
+          }
+        } else {  // a single 16-key tile: the other half of the k range is zero
+          const __bf16 zb = (__bf16)0.f;
+          const bf16x8 pb = {to_bf16(s[0][0]), to_bf16(s[0][1]), to_bf16(s[0][2]), to_bf16(s[0][3]), zb, zb, zb, zb};
 #pragma unroll
           for (int nt = 0; nt < NNT; ++nt) {
-            const bf16x4 a0 = lds_read_tr16(vb + (32 * jp) * VSTR + nt * 16);
-            const bf16x4 a1 = lds_read_tr16(vb + (32 * jp + 16) * VSTR + nt * 16);
-            const bf16x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+            const bf16x4 a0 = lds_read_tr16(vb + nt * 16);
+            const bf16x8 a = {a0[0], a0[1], a0[2], a0[3], zb, zb, zb, zb};
             o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[nt], 0, 0, 0);
           }
         }
-      } else {  // a single 16-key tile: the other half of the k range is zero
-        const __bf16 zb = (__bf16)0.f;
-        const bf16x8 pb = {to_bf16(s[0][0]), to_bf16(s[0][1]), to_bf16(s[0][2]), to_bf16(s[0][3]), zb, zb, zb, zb};
-#pragma unroll
-        for (int nt = 0; nt < NNT; ++nt) {
-          const bf16x4 a0 = lds_read_tr16(vb + nt * 16);
-          const bf16x8 a = {a0[0], a0[1], a0[2], a0[3], zb, zb, zb, zb};
-          o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[nt], 0, 0, 0);
-        }
-      }
-    } else {
-      // one V element per lane and instruction; tile jt+1 is read while
-      // tile jt is multiplied
-      float va[2][4][NNT];
-      const float* vbase = &Vg[(kofs + 4 * g) * VSTR + li];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-#pragma unroll
-        for (int nt = 0; nt < NNT; ++nt) va[0][rr][nt] = vbase[rr * VSTR + nt * 16];
-#pragma unroll
-      for (int jt = 0; jt < NJT; ++jt) {
-        if (jt + 1 < NJT) {
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr)
-#pragma unroll
-            for (int nt = 0; nt < NNT; ++nt) va[(jt + 1) & 1][rr][nt] = vbase[(16 * (jt + 1) + rr) * VSTR + nt * 16];
-        }
+      } else {
+        // one V element per lane and instruction; tile jt+1 is read while
+        // tile jt is multiplied
+        float va[2][4][NNT];
+        const float* vbase = &Vg[(kofs + 4 * g) * VSTR + li];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
-          for (int nt = 0; nt < NNT; ++nt)
-            o[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va[jt & 1][rr][nt], s[jt][rr], o[nt], 0, 0, 0);
+          for (int nt = 0; nt < NNT; ++nt) va[0][rr][nt] = vbase[rr * VSTR + nt * 16];
+#pragma unroll
+        for (int jt = 0; jt < NJT; ++jt) {
+          if (jt + 1 < NJT) {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+              for (int nt = 0; nt < NNT; ++nt)
+                va[(jt + 1) & 1][rr][nt] = vbase[(16 * (jt + 1) + rr) * VSTR + nt * 16];
+          }
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+            for (int nt = 0; nt < NNT; ++nt)
+              o[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va[jt & 1][rr][nt], s[jt][rr], o[nt], 0, 0, 0);
+        }
       }
-    }
-    }  // compute
     }  // sub-step
     if constexpr (SPLIT) {
       __syncthreads();  // every wave is past P.V: V of the next block may land
-      if (has_next) stage_store(Vg, voff);
+      if (has_next) stage_store_from(stg, Vg, voff);
       // with sub-steps, the first P.V of the next block precedes its
       // mid-block barrier, so V must be visible before the next step starts
       if constexpr (NSUB > 1) __syncthreads();
     }
   }
+  if constexpr (MODE == MODE_SDD) return;
 
-  // ---- merge the key groups: (m, l, O) of group sg > 0 through LDS into
-  // group 0, rescaling each side by exp2(m_side - m_max)
+  // ---- merge the key groups through LDS into group 0: attention rescales
+  // each side's (l, O) by exp2(m_side - m_max); the DSD adds the partial sums
   if constexpr (NS > 1) {
-    constexpr int SLOT = 64 * (2 + 4 * NNT);
-    float* red = reinterpret_cast<float*>(Ks);
+    float* red = reinterpret_cast<float*>(lds);
     __syncthreads();
     if (sg > 0) {
       float* slot = red + ((sg - 1) * NW + wave) * SLOT;
-      slot[lane] = m_run;
-      slot[64 + lane] = l_run;
+      if constexpr (ATTN) {
+        slot[lane] = m_run;
+        slot[64 + lane] = l_run;
+      }
 #pragma unroll
       for (int nt = 0; nt < NNT; ++nt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) slot[128 + (nt * 4 + e) * 64 + lane] = o[nt][e];
+        for (int e = 0; e < 4; ++e) slot[(ATTN ? 128 : 0) + (nt * 4 + e) * 64 + lane] = o[nt][e];
     }
     __syncthreads();
     if (sg > 0) return;
 #pragma unroll
     for (int s2 = 1; s2 < NS; ++s2) {
       const float* slot = red + ((s2 - 1) * NW + wave) * SLOT;
-      const float m2 = slot[lane], l2 = slot[64 + lane];
-      const float m_new = fmaxf(m_run, m2);
-      const float a1 = (m_new == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
-      const float a2 = (m_new == -INFINITY) ? 0.f : fast_exp2(m2 - m_new);
-      l_run = l_run * a1 + l2 * a2;
+      if constexpr (ATTN) {
+        const float m2 = slot[lane], l2 = slot[64 + lane];
+        const float m_new = fmaxf(m_run, m2);
+        const float a1 = (m_new == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
+        const float a2 = (m_new == -INFINITY) ? 0.f : fast_exp2(m2 - m_new);
+        l_run = l_run * a1 + l2 * a2;
 #pragma unroll
-      for (int nt = 0; nt < NNT; ++nt)
+        for (int nt = 0; nt < NNT; ++nt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[nt][e] = o[nt][e] * a1 + slot[128 + (nt * 4 + e) * 64 + lane] * a2;
-      m_run = m_new;
+          for (int e = 0; e < 4; ++e) o[nt][e] = o[nt][e] * a1 + slot[128 + (nt * 4 + e) * 64 + lane] * a2;
+        m_run = m_new;
+      } else {
+#pragma unroll
+        for (int nt = 0; nt < NNT; ++nt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[nt][e] += slot[(nt * 4 + e) * 64 + lane];
+      }
     }
   }
 
-  // ---- finish: l over the 4 lane groups, O = O^T / l, 4 columns per store
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  const float inv = (l_run > 0.f) ? 1.0f / l_run : 0.f;
+  // ---- finish: attention divides by l (summed over the 4 lane groups);
+  // O^T rows are written 4 columns per store
+  float inv = 1.f;
+  if constexpr (ATTN) {
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    inv = (l_run > 0.f) ? 1.0f / l_run : 0.f;
+  }
   St* po = O + (zh * Nq + q_index) * D + 4 * g;
 #pragma unroll
   for (int nt = 0; nt < NNT; ++nt) {
@@ -439,17 +499,29 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_attn(
   }
 }
 
-template <typename E, int BLK, int D, int NS>
-int launch_ns(const bs_layout* L, const void* Q, const void* K, const void* V, void* O, int Z, float c, bool causal,
-              hipStream_t s) {
+struct Args {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  float* S;
+  int Z;
+  float c;
+  bool causal;
+};
+
+template <typename E, int BLK, int D, int NS, int MODE>
+int launch_ns(const bs_layout* L, const Args& a, hipStream_t s) {
   using St = typename Elem<E>::storage;
-  const dim3 grid(L->H * L->nbr * Z), block(BLK * 4 * NS);
-  if (causal)
-    hipLaunchKernelGGL((k_attn<E, BLK, D, true, NS>), grid, block, 0, s, L->row_ptr, L->col_idx, L->row_order,
-                       (const St*)Q, (const St*)K, (const St*)V, (St*)O, Z, L->H, L->nbr, L->nbc, c);
+  const dim3 grid(L->H * L->nbr * a.Z), block(BLK * 4 * NS);
+  if (MODE == MODE_ATTN && a.causal)
+    hipLaunchKernelGGL((k_rowblock<E, BLK, D, true, NS, MODE>), grid, block, 0, s, L->row_ptr, L->col_idx,
+                       L->row_order, (const St*)a.Q, (const St*)a.K, (const St*)a.V, (St*)a.O, a.S, a.Z, L->H,
+                       L->nbr, L->nbc, L->nnz, a.c);
   else
-    hipLaunchKernelGGL((k_attn<E, BLK, D, false, NS>), grid, block, 0, s, L->row_ptr, L->col_idx, L->row_order,
-                       (const St*)Q, (const St*)K, (const St*)V, (St*)O, Z, L->H, L->nbr, L->nbc, c);
+    hipLaunchKernelGGL((k_rowblock<E, BLK, D, false, NS, MODE>), grid, block, 0, s, L->row_ptr, L->col_idx,
+                       L->row_order, (const St*)a.Q, (const St*)a.K, (const St*)a.V, (St*)a.O, a.S, a.Z, L->H,
+                       L->nbr, L->nbc, L->nnz, a.c);
   BSA_HIP(hipGetLastError());
   return BS_OK;
 }
@@ -466,48 +538,58 @@ inline int pick_key_groups(const bs_layout* L, int Z, int max_ns) {
   return ns;
 }
 
-template <typename E, int BLK, int D>
-int run(const bs_layout* L, const void* Q, const void* K, const void* V, void* O, int Z, float c, bool causal,
-        hipStream_t s) {
+template <typename E, int BLK, int D, int MODE>
+int run(const bs_layout* L, const Args& a, hipStream_t s) {
   // largest key-group count (up to 4, and 1024 threads) whose LDS fits in 160 KiB
-  constexpr size_t stage = Lds<E, BLK, D>::STAGE;
+  constexpr size_t stage = Lds<E, BLK, D, MODE>::STAGE;
   constexpr int max_ns = (BLK <= 64 && 4 * stage <= 160 * 1024) ? 4 : ((BLK <= 64 && 2 * stage <= 160 * 1024) ? 2 : 1);
-  const int ns = pick_key_groups(L, Z, max_ns);
+  const int ns = pick_key_groups(L, a.Z, max_ns);
   if constexpr (max_ns >= 4) {
-    if (ns >= 4) return launch_ns<E, BLK, D, 4>(L, Q, K, V, O, Z, c, causal, s);
+    if (ns >= 4) return launch_ns<E, BLK, D, 4, MODE>(L, a, s);
   }
   if constexpr (max_ns >= 2) {
-    if (ns >= 2) return launch_ns<E, BLK, D, 2>(L, Q, K, V, O, Z, c, causal, s);
+    if (ns >= 2) return launch_ns<E, BLK, D, 2, MODE>(L, a, s);
   }
-  return launch_ns<E, BLK, D, 1>(L, Q, K, V, O, Z, c, causal, s);
+  return launch_ns<E, BLK, D, 1, MODE>(L, a, s);
 }
 
-template <typename E, int D>
-int run_b(const bs_layout* L, const void* Q, const void* K, const void* V, void* O, int Z, float c, bool causal,
-          hipStream_t s) {
+template <typename E, int D, int MODE>
+int run_b(const bs_layout* L, const Args& a, hipStream_t s) {
   switch (L->block) {
-    case 16: return run<E, 16, D>(L, Q, K, V, O, Z, c, causal, s);
-    case 32: return run<E, 32, D>(L, Q, K, V, O, Z, c, causal, s);
-    case 64: return run<E, 64, D>(L, Q, K, V, O, Z, c, causal, s);
-    case 128: return run<E, 128, D>(L, Q, K, V, O, Z, c, causal, s);
+    case 16: return run<E, 16, D, MODE>(L, a, s);
+    case 32: return run<E, 32, D, MODE>(L, a, s);
+    case 64: return run<E, 64, D, MODE>(L, a, s);
+    case 128: return run<E, 128, D, MODE>(L, a, s);
   }
   return fail(BS_ERR_UNSUPPORTED, "block must be 16, 32, 64 or 128");
 }
 
-template <typename E>
-int run_e(const bs_layout* L, const void* Q, const void* K, const void* V, void* O, int Z, int d, float c,
-          bool causal, hipStream_t s) {
-  if (d == 64) return run_b<E, 64>(L, Q, K, V, O, Z, c, causal, s);
-  return run_b<E, 128>(L, Q, K, V, O, Z, c, causal, s);
+template <int MODE>
+int run_mode(const bs_layout* L, const Args& a, int d, bs_dtype dt, hipStream_t s) {
+  if (dt == BS_BF16) return d == 64 ? run_b<bf16_t, 64, MODE>(L, a, s) : run_b<bf16_t, 128, MODE>(L, a, s);
+  return d == 64 ? run_b<float, 64, MODE>(L, a, s) : run_b<float, 128, MODE>(L, a, s);
 }
 
 }  // namespace
 
 int launch_attention(const bs_layout* L, const void* Q, const void* K, const void* V, void* O, int Z, int d,
                      float scale, bool causal, bs_dtype dt, hipStream_t s) {
-  const float c = scale * kLog2e;
-  return dt == BS_BF16 ? run_e<bf16_t>(L, Q, K, V, O, Z, d, c, causal, s)
-                       : run_e<float>(L, Q, K, V, O, Z, d, c, causal, s);
+  const Args a{Q, K, V, O, nullptr, Z, scale * kLog2e, causal};
+  return run_mode<MODE_ATTN>(L, a, d, dt, s);
+}
+
+int launch_sdd_rowblock(const bs_layout* L, const void* A, const void* B, float* S, int Z, int K, bs_dtype dt,
+                        hipStream_t s) {
+  if (K != 64 && K != 128) return kNotApplicable;
+  const Args a{A, B, nullptr, nullptr, S, Z, 1.f, false};
+  return run_mode<MODE_SDD>(L, a, K, dt, s);
+}
+
+int launch_dsd_rowblock(const bs_layout* L, const float* P, const void* B, void* C, int Z, int Nd, bs_dtype dt,
+                        hipStream_t s) {
+  if (Nd != 64 && Nd != 128) return kNotApplicable;
+  const Args a{nullptr, nullptr, B, C, const_cast<float*>(P), Z, 1.f, false};
+  return run_mode<MODE_DSD>(L, a, Nd, dt, s);
 }
 
 }  // namespace bsa

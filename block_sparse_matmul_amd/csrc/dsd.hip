@@ -2,7 +2,10 @@
 // "question on blocksparse", second mode; in attention O = P V).
 //   C[z, h, r-block, :] = sum over stored (h, r, c) of P[z, k] . B[z, h, c-block, :]
 //
-// One workgroup (4 waves) per (batch, block row), longest rows first. The
+// Nd = 64 or 128 runs on the fused attention's row-block kernel (P read in
+// the score-register layout, B blocks staged through LDS). Other Nd take the
+// kernel below: one workgroup (4 waves) per (batch, block row), longest rows
+// first. The
 // output tiles of the row (block/T x Nd/T) are dealt to the waves; each
 // tile accumulates over every stored block of the row and over its columns.
 // P is read as 16-byte row vectors; the dense operand is read down its
@@ -125,6 +128,8 @@ int run_e(const bs_layout* L, const float* P, const void* B, void* C, int Z, int
 
 int launch_dsd(const bs_layout* L, const float* P, const void* B, void* C, int Z, int Nd, bs_dtype dt,
                hipStream_t s) {
+  const int rc = launch_dsd_rowblock(L, P, B, C, Z, Nd, dt, s);
+  if (rc != kNotApplicable) return rc;
   return dt == BS_BF16 ? run_e<bf16_t>(L, P, B, C, Z, Nd, s) : run_e<float>(L, P, B, C, Z, Nd, s);
 }
 

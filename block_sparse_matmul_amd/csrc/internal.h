@@ -61,6 +61,15 @@ int launch_attention(const bs_layout* L, const void* Q, const void* K,
                      const void* V, void* O, int Z, int d, float scale,
                      bool causal, bs_dtype dt, hipStream_t s);
 
+// SDD and DSD on the fused kernel's row-block machinery (LDS-staged
+// operands); they apply when the contraction (SDD) or output width (DSD) is
+// 64 or 128 and return kNotApplicable otherwise.
+constexpr int kNotApplicable = 1;
+int launch_sdd_rowblock(const bs_layout* L, const void* A, const void* B,
+                        float* S, int Z, int K, bs_dtype dt, hipStream_t s);
+int launch_dsd_rowblock(const bs_layout* L, const float* P, const void* B,
+                        void* C, int Z, int Nd, bs_dtype dt, hipStream_t s);
+
 bool log_enabled();
 
 }  // namespace bsa

@@ -3,8 +3,10 @@
 // For every stored block k = (h, r, c):
 //   S[z, k] = A[z, h, r-block, :] . B[z, h, c-block, :]^T      (fp32 out)
 //
-// One workgroup (4 waves) per (batch, block row), block rows taken longest
-// first. The row's output tiles (T x T, T = min(block, 32)) are dealt to the
+// K = 64 or 128 runs on the fused attention's row-block kernel (B blocks
+// staged through LDS, scores stored from the score registers). Other K take
+// the kernel below: one workgroup (4 waves) per (batch, block row), block
+// rows taken longest first. The row's output tiles (T x T, T = min(block, 32)) are dealt to the
 // waves; each tile is one MFMA accumulation over K with both operands read
 // as 16-byte row vectors (A rows are query rows, B rows are key rows), and
 // the tile is stored row by row (T consecutive floats per row).
@@ -84,6 +86,8 @@ int run_e(const bs_layout* L, const void* A, const void* B, float* S, int Z, int
 
 int launch_sdd(const bs_layout* L, const void* A, const void* B, float* S, int Z, int K, bs_dtype dt,
                hipStream_t s) {
+  const int rc = launch_sdd_rowblock(L, A, B, S, Z, K, dt, s);
+  if (rc != kNotApplicable) return rc;
   return dt == BS_BF16 ? run_e<bf16_t>(L, A, B, S, Z, K, s) : run_e<float>(L, A, B, S, Z, K, s);
 }
 
