@@ -92,17 +92,6 @@ struct Lds {
   static constexpr size_t STAGE = (size_t)(KBUF + VBUF) * sizeof(St);  // bytes per key group
 };
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-// 4 keys of one V column per lane, from a row-major bf16 tile in LDS: the
-// 16 lanes of a group pass the addresses of a 4-row x 16-column patch (lane
-// 4k + m: row k, columns 4m..4m+3) and lane i receives column i of the 4 rows
-__device__ __forceinline__ bf16x4 lds_read_tr16(const u16* p) {
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((__attribute__((address_space(3))) u16*)p));
-  return __builtin_bit_cast(bf16x4, v);
-}
-
 // Q, K, V, O: [Z][H][N][D] dense operands; S: [Z][nnz][BLK][BLK] fp32 block
 // values (SDD output, DSD input). MODE_ATTN uses Q, K, V -> O; MODE_SDD
 // uses Q (= A), K (= B) -> S; MODE_DSD uses S (= P), V (= B) -> O (= C).

@@ -26,6 +26,16 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint16_t u16;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// ds_read_b64_tr_b16 on a row-major bf16 tile in LDS: the 16 lanes of a
+// group pass the addresses of a 4-row x 16-column patch (lane 4k + m: row k,
+// columns 4m..4m+3) and lane i receives column i of the 4 rows
+__device__ __forceinline__ bf16x4 lds_read_tr16(const u16* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((__attribute__((address_space(3))) u16*)p));
+  return __builtin_bit_cast(bf16x4, v);
+}
 
 struct bf16_t {};  // tag for the bf16 element type (stored as 16-bit words)
 

@@ -88,7 +88,10 @@ def test_lut_rejects_non_binary_values():
 
 # --------------------------------------------------------------- SDD
 
-SDD_CASES = [(b, K, dt) for b in (16, 32, 64, 128) for K, dt in ((16, "f32"), (80, "f32"), (64, "bf16"), (48, "bf16"))]
+# K of 64 and 128 take the LDS-staged row-block kernel, other K the generic one
+SDD_CASES = [(b, K, dt) for b in (16, 32, 64, 128)
+             for K, dt in ((16, "f32"), (80, "f32"), (64, "f32"), (128, "f32"), (64, "bf16"), (128, "bf16"),
+                           (48, "bf16"))]
 
 
 @pytest.mark.parametrize("b,K,dt", SDD_CASES)
@@ -139,7 +142,9 @@ def test_softmax_in_place_and_long_rows():
 
 # --------------------------------------------------------------- DSD / DDS
 
-DSD_CASES = [(b, n, dt) for b in (16, 32, 64, 128) for n, dt in ((64, "f32"), (48, "f32"), (128, "bf16"), (16, "bf16"))]
+# Nd of 64 and 128 take the LDS-staged row-block kernel, other Nd the generic one
+DSD_CASES = [(b, n, dt) for b in (16, 32, 64, 128)
+             for n, dt in ((64, "f32"), (128, "f32"), (48, "f32"), (64, "bf16"), (128, "bf16"), (16, "bf16"))]
 
 
 @pytest.mark.parametrize("b,Nd,dt", DSD_CASES)
@@ -159,7 +164,9 @@ def test_dsd(b, Nd, dt):
     assert max_abs(f64(C), ref) <= TOL[dt]
 
 
-DDS_CASES = [(b, m, dt) for b in (16, 32, 64, 128) for m, dt in ((64, "f32"), (16, "f32"), (32, "bf16"), (48, "bf16"))]
+# M beyond 64 spans several 64-row chunks of the DDS grid (112, 80: a partial last chunk)
+DDS_CASES = [(b, m, dt) for b in (16, 32, 64, 128)
+             for m, dt in ((64, "f32"), (16, "f32"), (112, "f32"), (32, "bf16"), (48, "bf16"), (80, "bf16"))]
 
 
 @pytest.mark.parametrize("b,M,dt", DDS_CASES)
@@ -178,18 +185,39 @@ def test_dds(b, M, dt):
     assert max_abs(f64(C), ref) <= TOL[dt]
 
 
-def test_dds_random_values_relative():
-    """N(0,1) block values: fp32 rounding grows with the column length, so
-    the bound is relative to the largest output (1e-4 of max |C|)."""
-    b, M = 32, 64
+@pytest.mark.parametrize("b", [16, 32, 128])
+def test_dds_random_values_relative(b):
+    """Long columns (several 64- or 128-row slabs, which span several blocks
+    for small b) with N(0,1) block values: fp32 rounding grows with the
+    column length, so the bound is relative to the largest output (1e-4 of
+    max |C|)."""
+    M = 64
     lay = W.small_random_layout(2, 40, 6, 0.7, 17)
     nnz = int(lay.sum())
-    announce("dds random relative")
+    announce("dds random relative", b)
     A, S = _tensors([(1, 2, M, 40 * b), (1, nnz, b, b)], 18, "f32")
     L = bsa.Layout(torch.from_numpy(lay), b)
     C = bsa.dds(L, to_dev(A), to_dev(S))
     ref = oracle.dds(A, S, lay, b)
     assert max_abs(f64(C), ref) <= 1e-4 * np.abs(ref).max()
+
+
+@pytest.mark.parametrize("b", [16, 64])
+def test_dds_long_columns_bf16(b):
+    """bf16 over long columns whose length in 16-row tiles is odd (b = 16:
+    the last 32-deep product is half padding)."""
+    M = 48
+    lay = W.small_random_layout(2, 41, 5, 0.7, 19)
+    lay[:, :, 0] = 1  # 41 blocks: an odd tile count for b = 16
+    nnz = int(lay.sum())
+    announce("dds long columns bf16", b)
+    (A,) = _tensors([(2, 2, M, 41 * b)], 20, "bf16")
+    g = torch.Generator("cpu").manual_seed(21)
+    S = torch.rand((2, nnz, b, b), generator=g) / b
+    L = bsa.Layout(torch.from_numpy(lay), b)
+    C = bsa.dds(L, to_dev(A), to_dev(S))
+    ref = oracle.dds(A, S, lay, b)
+    assert max_abs(f64(C), ref) <= TOL["bf16"]
 
 
 # --------------------------------------------------------------- attention
@@ -296,3 +324,28 @@ def test_attention_batch_sweep_all_key_group_schedules(b, Z):
         ref = oracle.attention_rows(q, k, v, lay, b, 0.125, causal, rows)
         for n, (z, h, r) in enumerate(rows):
             assert max_abs(f64(O[z, h, r * b:(r + 1) * b]), ref[n]) <= TOL["f32"], (z, h, r, causal)
+
+
+@pytest.mark.parametrize("b", [16, 32, 64])
+@pytest.mark.parametrize("Z", [1, 128, 256])
+def test_ops_batch_sweep_all_key_group_schedules(b, Z):
+    """SDD, DSD (on the row-block kernel) and DDS split a row's or column's
+    blocks over 1, 2 or 4 key groups depending on its length against the
+    work per CU; a batch sweep on one layout exercises every choice. Checked
+    on sampled batch entries against the oracle."""
+    H, nb, d = 2, 4, 64
+    lay = W.small_random_layout(H, nb, nb, 0.5, 60 + b, force_diagonal=True)
+    nnz = int(lay.sum())
+    announce("ops batch sweep", b, Z)
+    a, bb, dense = _tensors([(Z, H, nb * b, d), (Z, H, nb * b, d), (Z, H, d, nb * b)], 61, "f32")
+    g = torch.Generator("cpu").manual_seed(62)
+    P = torch.rand((Z, nnz, b, b), generator=g) / b
+    L = bsa.Layout(torch.from_numpy(lay), b)
+    S = bsa.sdd(L, to_dev(a), to_dev(bb))
+    C = bsa.dsd(L, to_dev(P), to_dev(bb))
+    D = bsa.dds(L, to_dev(dense), to_dev(P))
+    for z in sorted({0, Z // 3, Z // 2, Z - 1}):
+        sl = slice(z, z + 1)
+        assert max_abs(f64(S[sl]), oracle.sdd(a[sl], bb[sl], lay, b)) <= TOL["f32"], ("sdd", z)
+        assert max_abs(f64(C[sl]), oracle.dsd(P[sl], bb[sl], lay, b)) <= TOL["f32"], ("dsd", z)
+        assert max_abs(f64(D[sl]), oracle.dds(dense[sl], P[sl], lay, b)) <= TOL["f32"], ("dds", z)
