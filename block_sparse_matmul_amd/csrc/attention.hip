@@ -45,7 +45,9 @@
 // The S^T register layout is also the layout of a row-major b x b block read
 // with one 16-byte load per lane (row li, columns 16 jt + 4 g ..), which is
 // how the SDD stores its scores and the DSD loads its P.
-// bf16: P is rounded to bf16 (RNE) for P.V, O once at the end.
+// bf16: P is rounded to bf16 (RNE) for P.V and the row sum l adds up those
+// rounded values (so the weights applied to V sum to one); O is rounded once
+// at the end.
 #include <math.h>
 
 #include <type_traits>
@@ -335,8 +337,7 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_rowblock(
         for (int jt = 0; jt < NJT; ++jt)
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) mx = fmaxf(mx, s[jt][rr]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = rows4_max(mx);
         const float m_blk = mx * cs;
         const bool upd = m_blk > m_run + kTau;
         if (__builtin_amdgcn_ballot_w64(upd) != 0) {  // wave-uniform
@@ -348,16 +349,19 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_rowblock(
           m_run = m_new;
         }
         const float m_sub = (m_run == -INFINITY) ? 0.f : m_run;
-        float ls = 0.f;
 #pragma unroll
         for (int jt = 0; jt < NJT; ++jt)
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            const float p = fast_exp2(fmaf(s[jt][rr], cs, -m_sub));
-            s[jt][rr] = p;
-            ls += p;
-          }
-        l_run += ls;
+          for (int rr = 0; rr < 4; ++rr) s[jt][rr] = fast_exp2(fmaf(s[jt][rr], cs, -m_sub));
+        if constexpr (!BF) {
+          // bf16 sums the rounded P below, two values per instruction
+          float ls = 0.f;
+#pragma unroll
+          for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) ls += s[jt][rr];
+          l_run += ls;
+        }
       }
 
       // ---- O^T[n][query] += V^T[n][keys] P^T[keys][query]
@@ -365,6 +369,16 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_rowblock(
         // lane (g, j = 4k + m) points at row 16h + 4g + k, columns 4m.. of
         // the n-tile; it gets back keys 16h + 4g + 0..3 of column nt*16 + li
         const u16* vb = &Vg[(kofs + 4 * g + (li >> 2)) * VSTR + 4 * (li & 3)];
+        // attention: the row sum l adds up P as rounded for the product (the
+        // weights that multiply V), two per v_dot2 against (1, 1)
+        float ls = 0.f;
+        const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+        auto sum_p = [&](const bf16x8& pb) {
+          if constexpr (ATTN) {
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[e], pb[e + 1]}, ones, ls, false);
+          }
+        };
         if constexpr (NJT >= 2) {
           // operands read right before use: the bf16 kernel is register bound
           // (two 8-wave workgroups per CU need <= 128 VGPRs)
@@ -373,6 +387,7 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_rowblock(
             const bf16x8 pb = {to_bf16(s[2 * jp][0]),     to_bf16(s[2 * jp][1]),     to_bf16(s[2 * jp][2]),
                                to_bf16(s[2 * jp][3]),     to_bf16(s[2 * jp + 1][0]), to_bf16(s[2 * jp + 1][1]),
                                to_bf16(s[2 * jp + 1][2]), to_bf16(s[2 * jp + 1][3])};
+            sum_p(pb);
 #pragma unroll
             for (int nt = 0; nt < NNT; ++nt) {
               const bf16x4 a0 = lds_read_tr16(vb + (32 * jp) * VSTR + nt * 16);
@@ -384,6 +399,7 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_rowblock(
         } else {  // a single 16-key tile: the other half of the k range is zero
           const __bf16 zb = (__bf16)0.f;
           const bf16x8 pb = {to_bf16(s[0][0]), to_bf16(s[0][1]), to_bf16(s[0][2]), to_bf16(s[0][3]), zb, zb, zb, zb};
+          sum_p(pb);
 #pragma unroll
           for (int nt = 0; nt < NNT; ++nt) {
             const bf16x4 a0 = lds_read_tr16(vb + nt * 16);
@@ -391,6 +407,7 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_rowblock(
             o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[nt], 0, 0, 0);
           }
         }
+        if constexpr (ATTN) l_run += ls;
       } else {
         // one V element per lane and instruction; tile jt+1 is read while
         // tile jt is multiplied
@@ -472,8 +489,7 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_rowblock(
   // O^T rows are written 4 columns per store
   float inv = 1.f;
   if constexpr (ATTN) {
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
+    l_run = rows4_sum(l_run);
     inv = (l_run > 0.f) ? 1.0f / l_run : 0.f;
   }
   St* po = O + (zh * Nq + q_index) * D + 4 * g;

@@ -37,6 +37,25 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const u16* p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
+// Max / sum over the four 16-lane rows of a wave (lanes l, l^16, l^32,
+// l^48), leaving the result in every lane. permlane16_swap returns, for
+// each pair of rows (2k, 2k+1), row 2k twice in its first result and row
+// 2k+1 twice in its second; permlane32_swap does the same for the two
+// halves. Two swaps and two operations, no LDS traffic; every lane ends
+// with the bitwise-identical value.
+__device__ __forceinline__ float rows4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 struct bf16_t {};  // tag for the bf16 element type (stored as 16-bit words)
 
 template <int T>
