@@ -579,6 +579,10 @@ int run_mode(const bs_layout* L, const Args& a, int d, bs_dtype dt, hipStream_t 
 
 int launch_attention(const bs_layout* L, const void* Q, const void* K, const void* V, void* O, int Z, int d,
                      float scale, bool causal, bs_dtype dt, hipStream_t s) {
+  if (dt == BS_BF16) {
+    const int rc = launch_attention_bf16_wide(L, Q, K, V, O, Z, d, scale, causal, s);
+    if (rc != kNotApplicable) return rc;
+  }
   const Args a{Q, K, V, O, nullptr, Z, scale * kLog2e, causal};
   return run_mode<MODE_ATTN>(L, a, d, dt, s);
 }

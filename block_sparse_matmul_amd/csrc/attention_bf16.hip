@@ -1,0 +1,461 @@
+// Fused block-sparse attention, bf16, blocks of 32 to 128: the same
+// computation as the row-block kernel (SDD -> block-sparse softmax -> DSD of
+// Triton issue 117, "question on blocksparse", with the streaming softmax of
+// the Triton tutorial, Puzzles 8 and 9), laid out for the bf16 matrix cores.
+//
+// What differs from the row-block kernel:
+//  * each wave owns 32 query rows (two 16-row tiles), so every K or V
+//    operand read from LDS feeds two MFMAs: half the LDS read traffic per
+//    flop, which is what bounds the 16-row layout in bf16;
+//  * blocks are staged with LDS DMA (global_load_lds_dwordx4: every lane
+//    moves 16 bytes from its own global address into consecutive LDS
+//    slots), so staging needs no registers and no LDS store instructions.
+//    Rows are stored unpadded with their 16-byte chunks XOR-swizzled by row
+//    (d = 128: slot = chunk ^ ((2 row) & 14); d = 64: slot = chunk ^
+//    (((row >> 1) ^ row) & 7)), which keeps the K reads (16 bytes per lane)
+//    and the transposing V reads (ds_read_b64_tr_b16) free of bank
+//    conflicts, as measured on gfx950;
+//  * per block: K and V have one stage each; V of the block is fetched at
+//    the top of the step (hidden by the first score product), K of the next
+//    block as soon as every wave is past its last score product.
+//
+// Per 64-key sub-step and wave (16x16x32 bf16 MFMA tiles, as in the
+// row-block kernel): S^T = K Q^T for both query tiles from one K read;
+// softmax in the log2 domain with lazy rescale; O^T += V^T P^T for both
+// tiles from one pair of transposing V reads. The row sum adds up P as
+// rounded to bf16 for the product (v_dot2 against (1, 1)).
+#include <math.h>
+
+#include "internal.h"
+#include "tile.h"
+
+namespace bsa {
+namespace {
+
+constexpr float kLog2eB = 1.4426950408889634f;
+constexpr float kTauB = 8.0f;  // lazy-rescale headroom, log2 units
+
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+template <int D>
+struct Swz;
+template <>
+struct Swz<128> {  // 256-byte rows, 16 chunks
+  static __device__ __forceinline__ int f(int r) { return (2 * r) & 14; }
+};
+template <>
+struct Swz<64> {  // 128-byte rows, 8 chunks
+  static __device__ __forceinline__ int f(int r) { return ((r >> 1) ^ r) & 7; }
+};
+
+template <int BLK, int D>
+struct WideCfg {
+  static constexpr int NW = BLK / 32;            // waves per key group
+  static constexpr int RB = D * 2;               // bytes per row
+  static constexpr int SB = BLK * RB;            // bytes per staged matrix
+  static constexpr int NNT = D / 16;             // 16-column tiles of O
+  static constexpr int SLOT = 64 * (2 + 4 * NNT);  // floats per wave and tile for the merge
+  // LDS of a workgroup with ns key groups: K stages and V stages; the merge
+  // (one query tile at a time) reuses the K stages
+  static constexpr size_t bytes(int ns) { return (size_t)ns * 2 * SB; }
+  static constexpr bool merge_fits(int ns) { return ns == 1 || (size_t)(ns - 1) * NW * SLOT * 4 <= (size_t)ns * SB; }
+};
+
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt and lgkmcnt left at "no wait")
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_vmcnt0() { wait_vmcnt<0>(); }
+
+template <int BLK, int D, bool CAUSAL, int NS>
+__global__ __launch_bounds__(BLK * 2 * NS) void k_attn_bf16(
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, const int32_t* __restrict__ row_order_h,
+    const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V, u16* __restrict__ O, int Z,
+    int H, int nbr, int nbc, float c) {
+  using Cfg = WideCfg<BLK, D>;
+  constexpr int NW = Cfg::NW, NT = 64 * NW;
+  constexpr int NQ = D / 32;         // Q fragments per lane and tile
+  constexpr int CPR = D / 8;         // 16-byte chunks per row
+  constexpr int RB = Cfg::RB;
+  constexpr int RPI = 1024 / RB;     // rows per DMA instruction (64 lanes x 16 bytes)
+  constexpr int SB = Cfg::SB;
+  constexpr int NI = SB / 1024 / NW;  // DMA instructions per wave and matrix
+  constexpr int KS = BLK < 64 ? BLK : 64;  // keys per sub-step
+  constexpr int NSUB = BLK / KS;
+  constexpr int NJT = KS / 16;
+  constexpr int NNT = Cfg::NNT;
+  constexpr int SLOT = Cfg::SLOT;
+  static_assert(NI >= 1 && SB % (1024 * NW) == 0, "whole DMA instructions per wave");
+  static_assert(NJT % 2 == 0, "32-key products");
+
+  // K and V stages in separate arrays, so that the compiler can tell the
+  // K reads from the V transfers in flight (and the other way round)
+  __shared__ __attribute__((aligned(16))) unsigned char Ks[NS * SB];
+  __shared__ __attribute__((aligned(16))) unsigned char Vs[NS * SB];
+
+  const int tid_all = threadIdx.x;
+  const int sg = __builtin_amdgcn_readfirstlane(tid_all / NT);  // key group
+  const int tid = tid_all % NT;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int li = lane & 15, g = lane >> 4;
+  unsigned char* const Kg = Ks + sg * SB;
+  unsigned char* const Vg = Vs + sg * SB;
+  // unit -> (z, h) major, then the head's rows longest first
+  const int unit = xcd_unit(blockIdx.x, gridDim.x);
+  const int zhu = unit / nbr;
+  const int z = zhu / H, h = zhu % H;
+  const int hr = row_order_h[h * nbr + unit % nbr];
+  const int r = hr % nbr;
+  const int k0 = row_ptr[hr], k1 = row_ptr[hr + 1];
+  const int64_t zh = (int64_t)z * H + h;
+  const int64_t Nq = (int64_t)nbr * BLK, Nk = (int64_t)nbc * BLK;
+  const int q_lo = r * BLK + wave * 32;  // first query row of this wave
+  const u16* Kz = K + zh * Nk * D;
+  const u16* Vz = V + zh * Nk * D;
+
+  // ---- Q of both tiles as B fragments (8 values of one row per lane);
+  // only the sign of scale*log2(e) is folded in (exact in bf16)
+  bf16x8 qf[2][NQ];
+  const float sgn = c > 0.f ? 1.f : (c < 0.f ? -1.f : 0.f);
+  const float cs = (c == 0.f) ? 1.f : fabsf(c);
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const u16* pq = Q + (zh * Nq + q_lo + 16 * t + li) * D + g * 8;
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      qf[t][u] = *reinterpret_cast<const bf16x8*>(pq + u * 32);
+      if (sgn != 1.f) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[t][u][e] = to_bf16((float)qf[t][u][e] * sgn);
+      }
+    }
+  }
+
+  // ---- DMA: instruction i of this wave moves rows (wave + NW i) * RPI ..
+  // of a block; lane l fills slot l % CPR of row l / CPR with the chunk
+  // that the swizzle puts there. The swizzle of a row depends only on the
+  // parity of the instruction, so two per-lane offsets cover every one.
+  int dofs[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int ri = lane / CPR, slot = lane % CPR;
+    dofs[p] = ri * D + ((slot ^ Swz<D>::f(p * RPI + ri)) * 8);
+  }
+  const int d_even = (wave & 1) ? dofs[1] : dofs[0];
+  const int d_odd = (wave & 1) ? dofs[0] : dofs[1];
+  // one part of a matrix: the KS rows of one sub-step (the whole block
+  // with one sub-step); NIP instructions per wave
+  constexpr int NIP = NI / NSUB;
+  auto dma = [&](const u16* gpart, unsigned char* spart) {
+#pragma unroll
+    for (int i = 0; i < NIP; ++i) {
+      const int I = wave + NW * i;  // uniform
+      const u16* src = gpart + I * RPI * D + (((NW * i) & 1) ? d_odd : d_even);
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_u8*)(spart + I * 1024), 16, 0, 0);
+    }
+  };
+  auto kpart = [&](int e, int x) { return Kz + (int64_t)col_idx[e] * BLK * D + x * KS * D; };
+  auto vpart = [&](int e, int x) { return Vz + (int64_t)col_idx[e] * BLK * D + x * KS * D; };
+
+  // ---- LDS read offsets (bytes). K: lane (g, li) reads row 16 jt + li,
+  // chunk 4u + g; V: lane (g, 4k + m) reads row 4g + k, the 8 bytes at
+  // column 16 nt + 4m. Row offsets that are multiples of 16 do not change
+  // the swizzle and go into the instruction offsets.
+  int koff[NQ], voff[NNT];
+#pragma unroll
+  for (int u = 0; u < NQ; ++u) koff[u] = li * RB + (((4 * u + g) ^ Swz<D>::f(li)) * 16);
+  {
+    const int k = li >> 2, m = li & 3, vr = 4 * g + k;
+#pragma unroll
+    for (int nt = 0; nt < NNT; ++nt) voff[nt] = vr * RB + (((2 * nt + (m >> 1)) ^ Swz<D>::f(vr)) * 16) + 8 * (m & 1);
+  }
+
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  f32x4 o[2][NNT];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int nt = 0; nt < NNT; ++nt) o[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+
+  // Transfers and barriers. With one sub-step: [A] K of the block has
+  // landed -> barrier -> fetch V; score product; softmax; [B] V has landed
+  // -> barrier (every wave is past the score product) -> fetch the next K;
+  // P.V. With two sub-steps each matrix is moved in halves (the 64 keys of
+  // a sub-step), so a half is refetched as soon as its sub-step is done
+  // with it and has most of a block of work to arrive:
+  //   [S x] K half x has landed -> barrier -> fetch the V half that the
+  //         previous sub-step freed; score product on K half x;
+  //   [P x] V half x has landed -> barrier -> fetch K half x of the next
+  //         block; softmax; P.V on V half x.
+  // Every barrier is block-wide (all key groups); transfers complete in
+  // issue order, so each wait names how many later ones may stay in flight.
+  const int nsteps = (k1 - k0 + NS - 1) / NS;
+  unsigned char* const Kp[2] = {Kg, Kg + KS * RB};
+  unsigned char* const Vp[2] = {Vg, Vg + KS * RB};
+  if (k0 + sg < k1) {
+    dma(kpart(k0 + sg, 0), Kp[0]);
+    if constexpr (NSUB == 2) {
+      dma(vpart(k0 + sg, 0), Vp[0]);
+      dma(kpart(k0 + sg, 1), Kp[1]);
+    }
+  }
+  for (int step = 0; step < nsteps; ++step) {
+    const int kk = k0 + step * NS + sg;
+    const bool valid = kk < k1;
+    const bool has_next = kk + NS < k1;
+    const int cb = valid ? col_idx[kk] : 0;
+    if constexpr (NSUB == 1) {
+      wait_vmcnt0();
+      __syncthreads();  // [A]
+      if (valid) dma(vpart(kk, 0), Vp[0]);
+    }
+    const bool mask_block = CAUSAL && (cb * BLK + BLK - 1 > q_lo);
+    const bool compute = valid && !(CAUSAL && cb * BLK > q_lo + 31);
+
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub) {
+      const int kofs = sub * KS;
+      if constexpr (NSUB == 2) {
+        // [S sub]: later transfers in flight: V(this, 0) and K(this, 1)
+        // before sub-step 0; V(this, 1) and K(next, 0) before sub-step 1
+        if (sub == 0) {
+          if (valid) wait_vmcnt<2 * NIP>(); else wait_vmcnt0();
+        } else {
+          if (has_next) wait_vmcnt<2 * NIP>(); else if (valid) wait_vmcnt<NIP>(); else wait_vmcnt0();
+        }
+        __syncthreads();
+        if (sub == 0) {
+          if (valid) dma(vpart(kk, 1), Vp[1]);
+        } else {
+          if (has_next) dma(vpart(kk + NS, 0), Vp[0]);
+        }
+      }
+      const unsigned char* const Kc = Kp[sub];
+      f32x4 s[2][NJT];
+      // ---- S^T = K Q^T for both tiles
+      if (compute) {
+        // the K operands of tile jt+1 are read while tile jt is multiplied
+        bf16x8 ka[2][NQ];
+#pragma unroll
+        for (int u = 0; u < NQ; ++u) ka[0][u] = *reinterpret_cast<const bf16x8*>(Kc + koff[u]);
+#pragma unroll
+        for (int jt = 0; jt < NJT; ++jt) {
+          if (jt + 1 < NJT) {
+#pragma unroll
+            for (int u = 0; u < NQ; ++u)
+              ka[(jt + 1) & 1][u] = *reinterpret_cast<const bf16x8*>(Kc + 16 * (jt + 1) * RB + koff[u]);
+          }
+          __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the products
+          s[0][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          s[1][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int u = 0; u < NQ; ++u) {
+            s[0][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[jt & 1][u], qf[0][u], s[0][jt], 0, 0, 0);
+            s[1][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[jt & 1][u], qf[1][u], s[1][jt], 0, 0, 0);
+          }
+        }
+      }
+      if constexpr (NSUB == 2) {
+        // [P sub]: later transfers in flight: K(this, 1) and V(this, 1)
+        // before sub-step 0's P.V; K(next, 0) and V(next, 0) before
+        // sub-step 1's
+        if (sub == 0) {
+          if (valid) wait_vmcnt<2 * NIP>(); else wait_vmcnt0();
+        } else {
+          if (has_next) wait_vmcnt<2 * NIP>(); else wait_vmcnt0();
+        }
+        __syncthreads();
+        if (has_next) dma(kpart(kk + NS, sub), Kp[sub]);
+      }
+
+      // ---- softmax of both tiles
+      if (compute) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int q_index = q_lo + 16 * t + li;
+          if (mask_block) {
+#pragma unroll
+            for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr)
+                if (cb * BLK + kofs + 16 * jt + 4 * g + rr > q_index) s[t][jt][rr] = -INFINITY;
+          }
+          float mx = -INFINITY;
+#pragma unroll
+          for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) mx = fmaxf(mx, s[t][jt][rr]);
+          mx = rows4_max(mx);
+          const float m_blk = mx * cs;
+          const bool upd = m_blk > m_run[t] + kTauB;
+          if (__builtin_amdgcn_ballot_w64(upd) != 0) {  // wave-uniform
+            const float m_new = upd ? m_blk : m_run[t];
+            const float alpha = __builtin_amdgcn_exp2f(m_run[t] - m_new);  // 0 when m_run = -inf
+            l_run[t] *= alpha;
+#pragma unroll
+            for (int nt = 0; nt < NNT; ++nt) o[t][nt] *= alpha;
+            m_run[t] = m_new;
+          }
+          const float m_sub = (m_run[t] == -INFINITY) ? 0.f : m_run[t];
+#pragma unroll
+          for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) s[t][jt][rr] = __builtin_amdgcn_exp2f(fmaf(s[t][jt][rr], cs, -m_sub));
+        }
+      }
+
+      if constexpr (NSUB == 1) {
+        wait_vmcnt0();    // this wave's part of V (the only transfer in flight)
+        __syncthreads();  // [B]
+        if (has_next) dma(kpart(kk + NS, 0), Kp[0]);
+      }
+      if (!compute) continue;
+
+      // ---- O^T += V^T P^T for both tiles from one pair of V reads
+#pragma unroll
+      for (int jp = 0; jp < NJT / 2; ++jp) {
+        bf16x8 pb[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          pb[t] = bf16x8{to_bf16(s[t][2 * jp][0]),     to_bf16(s[t][2 * jp][1]),     to_bf16(s[t][2 * jp][2]),
+                         to_bf16(s[t][2 * jp][3]),     to_bf16(s[t][2 * jp + 1][0]), to_bf16(s[t][2 * jp + 1][1]),
+                         to_bf16(s[t][2 * jp + 1][2]), to_bf16(s[t][2 * jp + 1][3])};
+#pragma unroll
+          for (int e = 0; e < 8; e += 2)
+            l_run[t] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[t][e], pb[t][e + 1]}, ones, l_run[t], false);
+        }
+        // every V operand of the 32 keys is requested before the first
+        // product, so the reads stream behind the MFMAs
+        const unsigned char* vb = Vp[sub] + 32 * jp * RB;
+        bf16x4 va0[NNT], va1[NNT];
+#pragma unroll
+        for (int nt = 0; nt < NNT; ++nt) {
+          va0[nt] = lds_read_tr16(reinterpret_cast<const u16*>(vb + voff[nt]));
+          va1[nt] = lds_read_tr16(reinterpret_cast<const u16*>(vb + 16 * RB + voff[nt]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int nt = 0; nt < NNT; ++nt) {
+          const bf16x8 a = {va0[nt][0], va0[nt][1], va0[nt][2], va0[nt][3],
+                            va1[nt][0], va1[nt][1], va1[nt][2], va1[nt][3]};
+          o[0][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[0], o[0][nt], 0, 0, 0);
+          o[1][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[1], o[1][nt], 0, 0, 0);
+        }
+      }
+    }  // sub-step
+  }
+
+  // ---- merge the key groups into group 0 through the K stages, one query
+  // tile at a time: each side's (l, O) is rescaled by exp2(m_side - m_max)
+  if constexpr (NS > 1) {
+    float* red = reinterpret_cast<float*>(Ks);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      __syncthreads();
+      if (sg > 0) {
+        float* slot = red + ((sg - 1) * NW + wave) * SLOT;
+        slot[lane] = m_run[t];
+        slot[64 + lane] = l_run[t];
+#pragma unroll
+        for (int nt = 0; nt < NNT; ++nt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) slot[128 + (nt * 4 + e) * 64 + lane] = o[t][nt][e];
+      }
+      __syncthreads();
+      if (sg == 0) {
+#pragma unroll
+        for (int s2 = 1; s2 < NS; ++s2) {
+          const float* slot = red + ((s2 - 1) * NW + wave) * SLOT;
+          const float m2 = slot[lane], l2 = slot[64 + lane];
+          const float m_new = fmaxf(m_run[t], m2);
+          const float a1 = (m_new == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[t] - m_new);
+          const float a2 = (m_new == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m2 - m_new);
+          l_run[t] = l_run[t] * a1 + l2 * a2;
+#pragma unroll
+          for (int nt = 0; nt < NNT; ++nt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[t][nt][e] = o[t][nt][e] * a1 + slot[128 + (nt * 4 + e) * 64 + lane] * a2;
+          m_run[t] = m_new;
+        }
+      }
+    }
+    if (sg > 0) return;
+  }
+
+  // ---- finish: divide by l (summed over the 4 lane rows), write O rows
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const float l = rows4_sum(l_run[t]);
+    const float inv = (l > 0.f) ? 1.0f / l : 0.f;
+    u16* po = O + (zh * Nq + q_lo + 16 * t + li) * D + 4 * g;
+#pragma unroll
+    for (int nt = 0; nt < NNT; ++nt)
+      *reinterpret_cast<bf16x4*>(po + nt * 16) = bf16x4{to_bf16(o[t][nt][0] * inv), to_bf16(o[t][nt][1] * inv),
+                                                        to_bf16(o[t][nt][2] * inv), to_bf16(o[t][nt][3] * inv)};
+  }
+}
+
+template <int BLK, int D, int NS>
+int launch_ns(const bs_layout* L, const void* Q, const void* K, const void* V, void* O, int Z, float c, bool causal,
+              hipStream_t s) {
+  const dim3 grid(L->H * L->nbr * Z), block(BLK * 2 * NS);
+  if (causal)
+    hipLaunchKernelGGL((k_attn_bf16<BLK, D, true, NS>), grid, block, 0, s, L->row_ptr, L->col_idx, L->row_order_h,
+                       (const u16*)Q, (const u16*)K, (const u16*)V, (u16*)O, Z, L->H, L->nbr, L->nbc, c);
+  else
+    hipLaunchKernelGGL((k_attn_bf16<BLK, D, false, NS>), grid, block, 0, s, L->row_ptr, L->col_idx, L->row_order_h,
+                       (const u16*)Q, (const u16*)K, (const u16*)V, (u16*)O, Z, L->H, L->nbr, L->nbc, c);
+  BSA_HIP(hipGetLastError());
+  return BS_OK;
+}
+
+// Key groups per workgroup: split a row's blocks over NS groups once the
+// longest row alone (about two workgroups share a CU) outlasts a CU's share
+// of the job.
+template <int BLK, int D>
+int run(const bs_layout* L, const void* Q, const void* K, const void* V, void* O, int Z, float c, bool causal,
+        hipStream_t s) {
+  using Cfg = WideCfg<BLK, D>;
+  constexpr size_t cap = 160 * 1024;
+  constexpr int max_ns = (Cfg::bytes(4) <= cap && Cfg::merge_fits(4) && BLK * 8 <= 1024)
+                             ? 4
+                             : ((Cfg::bytes(2) <= cap && Cfg::merge_fits(2)) ? 2 : 1);
+  const double per_cu = (double)Z * (double)L->nnz / L->num_cus;
+  int ns = 1;
+  while (ns < max_ns && 2.0 * L->max_row_len / ns > per_cu) ns *= 2;
+  if constexpr (max_ns >= 4) {
+    if (ns >= 4) return launch_ns<BLK, D, 4>(L, Q, K, V, O, Z, c, causal, s);
+  }
+  if constexpr (max_ns >= 2) {
+    if (ns >= 2) return launch_ns<BLK, D, 2>(L, Q, K, V, O, Z, c, causal, s);
+  }
+  return launch_ns<BLK, D, 1>(L, Q, K, V, O, Z, c, causal, s);
+}
+
+template <int D>
+int run_b(const bs_layout* L, const void* Q, const void* K, const void* V, void* O, int Z, float c, bool causal,
+          hipStream_t s) {
+  switch (L->block) {
+    case 32: return run<32, D>(L, Q, K, V, O, Z, c, causal, s);
+    case 64: return run<64, D>(L, Q, K, V, O, Z, c, causal, s);
+    case 128: return run<128, D>(L, Q, K, V, O, Z, c, causal, s);
+  }
+  return kNotApplicable;
+}
+
+}  // namespace
+
+int launch_attention_bf16_wide(const bs_layout* L, const void* Q, const void* K, const void* V, void* O, int Z, int d,
+                               float scale, bool causal, hipStream_t s) {
+  const float c = scale * kLog2eB;
+  if (d == 64) return run_b<64>(L, Q, K, V, O, Z, c, causal, s);
+  if (d == 128) return run_b<128>(L, Q, K, V, O, Z, c, causal, s);
+  return kNotApplicable;
+}
+
+}  // namespace bsa

@@ -26,7 +26,19 @@ struct bs_layout {
   int32_t* blk_id = nullptr;     // [nnz]
   int32_t* row_order = nullptr;  // [H*nbr] block rows, longest first
   int32_t* col_order = nullptr;  // [H*nbc] block columns, longest first
+  // the same orders grouped by head: head h's rows at h*nbr.., longest first
+  int32_t* row_order_h = nullptr;  // [H*nbr]
+  int32_t* col_order_h = nullptr;  // [H*nbc]
 };
+
+// Workgroup -> work unit for kernels that walk a head's rows (or columns)
+// together: workgroup b runs on XCD b % 8 (round-robin dispatch), and each
+// XCD gets a contiguous range of the G units, so the rows in flight on one
+// XCD come from few (batch, head) pairs and share that XCD's L2.
+__device__ __forceinline__ int xcd_unit(int b, int G) {
+  const int q = G >> 3, rem = G & 7, x = b & 7, j = b >> 3;
+  return x * q + (x < rem ? x : rem) + j;
+}
 
 namespace bsa {
 
@@ -69,6 +81,11 @@ int launch_sdd_rowblock(const bs_layout* L, const void* A, const void* B,
                         float* S, int Z, int K, bs_dtype dt, hipStream_t s);
 int launch_dsd_rowblock(const bs_layout* L, const float* P, const void* B,
                         void* C, int Z, int Nd, bs_dtype dt, hipStream_t s);
+
+// bf16 fused attention on the 32-rows-per-wave kernel (blocks of 32, 64,
+// 128); returns kNotApplicable for other blocks or head sizes.
+int launch_attention_bf16_wide(const bs_layout* L, const void* Q, const void* K, const void* V, void* O, int Z,
+                               int d, float scale, bool causal, hipStream_t s);
 
 bool log_enabled();
 

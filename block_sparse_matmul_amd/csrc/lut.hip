@@ -145,6 +145,36 @@ __global__ __launch_bounds__(64) void k_order(const int32_t* __restrict__ count,
   }
 }
 
+// Stable partition of an order by head (item / per_head), run by a single
+// wave like the sort above: head h's items land at h*per_head.., in the
+// order they have in the input (longest first). cursor[h] counts the items
+// of head h placed so far (zero on entry).
+__global__ __launch_bounds__(64) void k_group_by_head(const int32_t* __restrict__ in, int n, int per_head,
+                                                      int32_t* __restrict__ cursor, int32_t* __restrict__ out) {
+  __shared__ int32_t keys[kWave];
+  const int lane = threadIdx.x;
+  for (int base = 0; base < n; base += kWave) {
+    const int i = base + lane;
+    const int item = (i < n) ? in[i] : 0;
+    const int key = (i < n) ? item / per_head : -1;
+    keys[lane] = key;
+    __syncthreads();
+    int before = 0, after = 0;
+    for (int j = 0; j < kWave; ++j) {
+      const int kj = keys[j];
+      before += (j < lane && kj == key);
+      after += (j > lane && kj == key);
+    }
+    const int start = (i < n) ? cursor[key] : 0;
+    __syncthreads();
+    if (i < n) {
+      out[key * per_head + start + before] = item;
+      if (after == 0) cursor[key] = start + before + 1;  // last of its head in this chunk
+    }
+    __syncthreads();
+  }
+}
+
 // One wave per block row: write col_idx in ascending column order and the
 // id of every stored block into a dense map (read back by the CSC fill).
 __global__ __launch_bounds__(256) void k_fill_rows(const uint8_t* __restrict__ lay, int rows, int nbc,
@@ -231,10 +261,11 @@ int build_tables(bs_layout* L, const uint8_t* lay, hipStream_t s) {
   const int rows = H * nbr, cols = H * nbc;
   const int64_t cells = (int64_t)rows * nbc;
 
-  // fixed-size tables: row_ptr, col_ptr, row_order, col_order
-  const size_t fixed = (size_t)(rows + 1) + (cols + 1) + rows + cols;
-  // temporaries: counts, summary, two histograms, id map
-  const size_t tmp_n = (size_t)rows + cols + SUM_N + (nbc + 2) + (nbr + 2) + (size_t)cells;
+  // fixed-size tables: row_ptr, col_ptr, row_order, col_order,
+  // row_order_h, col_order_h
+  const size_t fixed = (size_t)(rows + 1) + (cols + 1) + 2 * (size_t)rows + 2 * (size_t)cols;
+  // temporaries: counts, summary, two histograms, two head cursors, id map
+  const size_t tmp_n = (size_t)rows + cols + SUM_N + (nbc + 2) + (nbr + 2) + 2 * (size_t)H + (size_t)cells;
   int32_t* fixed_mem = nullptr;
   int32_t* tmp = nullptr;
   if (hipMalloc(&fixed_mem, fixed * sizeof(int32_t)) != hipSuccess) {
@@ -250,12 +281,16 @@ int build_tables(bs_layout* L, const uint8_t* lay, hipStream_t s) {
   int32_t* col_ptr = row_ptr + rows + 1;
   int32_t* row_order = col_ptr + cols + 1;
   int32_t* col_order = row_order + rows;
+  int32_t* row_order_h = col_order + cols;
+  int32_t* col_order_h = row_order_h + rows;
   int32_t* row_cnt = tmp;
   int32_t* col_cnt = row_cnt + rows;
   int32_t* summary = col_cnt + cols;
   int32_t* hist_r = summary + SUM_N;
   int32_t* hist_c = hist_r + (nbc + 2);
-  int32_t* idmap = hist_c + (nbr + 2);
+  int32_t* cursor_r = hist_c + (nbr + 2);
+  int32_t* cursor_c = cursor_r + H;
+  int32_t* idmap = cursor_c + H;
 
   auto cleanup = [&](int code) {
     (void)hipStreamSynchronize(s);
@@ -269,7 +304,7 @@ int build_tables(bs_layout* L, const uint8_t* lay, hipStream_t s) {
     if (e_ != hipSuccess) return cleanup(hip_fail(e_, #call));   \
   } while (0)
 
-  BSA_TRY(hipMemsetAsync(summary, 0, (SUM_N + (nbc + 2) + (nbr + 2)) * sizeof(int32_t), s));
+  BSA_TRY(hipMemsetAsync(summary, 0, (SUM_N + (nbc + 2) + (nbr + 2) + 2 * (size_t)H) * sizeof(int32_t), s));
   hipLaunchKernelGGL(k_count_rows, dim3(blocks_for(rows, 4)), dim3(256), 0, s, lay, rows, nbc, row_cnt, summary);
   hipLaunchKernelGGL(k_count_cols, dim3(blocks_for(cols, 256)), dim3(256), 0, s, lay, H, nbr, nbc, col_cnt, summary);
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, row_cnt, rows, row_ptr, summary, (int)SUM_NNZ_ROWS);
@@ -278,6 +313,8 @@ int build_tables(bs_layout* L, const uint8_t* lay, hipStream_t s) {
   hipLaunchKernelGGL(k_len_hist, dim3(blocks_for(cols, 256)), dim3(256), 0, s, col_cnt, cols, hist_c);
   hipLaunchKernelGGL(k_order, dim3(1), dim3(64), 0, s, row_cnt, rows, hist_r, nbc, row_order);
   hipLaunchKernelGGL(k_order, dim3(1), dim3(64), 0, s, col_cnt, cols, hist_c, nbr, col_order);
+  hipLaunchKernelGGL(k_group_by_head, dim3(1), dim3(64), 0, s, row_order, rows, nbr, cursor_r, row_order_h);
+  hipLaunchKernelGGL(k_group_by_head, dim3(1), dim3(64), 0, s, col_order, cols, nbc, cursor_c, col_order_h);
   BSA_TRY(hipGetLastError());
 
   int32_t sum_host[SUM_N];
@@ -321,6 +358,8 @@ int build_tables(bs_layout* L, const uint8_t* lay, hipStream_t s) {
   L->col_ptr = col_ptr;
   L->row_order = row_order;
   L->col_order = col_order;
+  L->row_order_h = row_order_h;
+  L->col_order_h = col_order_h;
   // the nnz arrays live in their own allocation, remembered through col_idx
   return BS_OK;
 }

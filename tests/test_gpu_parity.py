@@ -349,3 +349,27 @@ def test_ops_batch_sweep_all_key_group_schedules(b, Z):
         assert max_abs(f64(S[sl]), oracle.sdd(a[sl], bb[sl], lay, b)) <= TOL["f32"], ("sdd", z)
         assert max_abs(f64(C[sl]), oracle.dsd(P[sl], bb[sl], lay, b)) <= TOL["f32"], ("dsd", z)
         assert max_abs(f64(D[sl]), oracle.dds(dense[sl], P[sl], lay, b)) <= TOL["f32"], ("dds", z)
+
+
+BF16_SWEEP = [(32, 1), (32, 80), (32, 256), (64, 1), (64, 80), (64, 256), (128, 1), (128, 40), (128, 256)]
+
+
+@pytest.mark.parametrize("b,Z", BF16_SWEEP)
+@pytest.mark.parametrize("d", [64, 128])
+def test_attention_bf16_batch_sweep_all_key_group_schedules(b, Z, d):
+    """bf16 attention with blocks of 32 to 128 runs on the kernel with 32
+    query rows per wave; its key-group count (1, 2 or 4, as the LDS allows)
+    follows the batch size the same way. Sampled block rows against the
+    oracle, causal and not."""
+    H, nb = 2, 4
+    lay = W.small_random_layout(H, nb, nb, 0.5, 50 + b, force_diagonal=True)
+    announce("attention bf16 batch sweep", b, Z, d)
+    q, k, v = _tensors([(Z, H, nb * b, d)] * 3, 52, "bf16")
+    L = bsa.Layout(torch.from_numpy(lay), b)
+    scale = 1.0 / np.sqrt(d)
+    for causal in (False, True):
+        O = bsa.attention(L, to_dev(q), to_dev(k), to_dev(v), scale, causal)
+        rows = [(0, 0, 0), (Z - 1, 1, nb - 1), (Z // 2, 0, 2), (Z // 3, 1, 1)]
+        ref = oracle.attention_rows(q, k, v, lay, b, scale, causal, rows)
+        for n, (z, h, r) in enumerate(rows):
+            assert max_abs(f64(O[z, h, r * b:(r + 1) * b]), ref[n]) <= TOL["bf16"], (z, h, r, causal)
