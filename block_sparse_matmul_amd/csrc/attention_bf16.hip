@@ -72,9 +72,9 @@ __device__ __forceinline__ void wait_vmcnt0() { wait_vmcnt<0>(); }
 
 template <int BLK, int D, bool CAUSAL, int NS>
 __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_bf16(
-    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, const int32_t* __restrict__ row_order_h,
-    const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V, u16* __restrict__ O, int Z,
-    int H, int nbr, int nbc, float c) {
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, const int32_t* __restrict__ row_order,
+    const int32_t* __restrict__ row_order_h, const u16* __restrict__ Q, const u16* __restrict__ K,
+    const u16* __restrict__ V, u16* __restrict__ O, int Z, int H, int nbr, int nbc, float c, int grouped) {
   using Cfg = WideCfg<BLK, D>;
   constexpr int NW = Cfg::NW, NT = 64 * NW;
   constexpr int NQ = D / 32;         // Q fragments per lane and tile
@@ -104,12 +104,21 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_bf16(
   const int li = lane & 15, g = lane >> 4;
   unsigned char* const Kg = Ks + sg * SB;
   unsigned char* const Vg = Vs + sg * SB;
-  // unit -> (z, h) major, then the head's rows longest first
-  const int unit = xcd_unit(blockIdx.x, gridDim.x);
-  const int zhu = unit / nbr;
-  const int z = zhu / H, h = zhu % H;
-  const int hr = row_order_h[h * nbr + unit % nbr];
-  const int r = hr % nbr;
+  // Which block row: with rows of similar length, XCD-aware and grouped by
+  // (batch, head), the head's rows longest first (K and V of a head stay in
+  // the XCD's L2 while its rows are in flight); otherwise longest first
+  // across the whole job, batch index fastest (the long rows start first).
+  int z, hr;
+  if (grouped) {
+    const int unit = xcd_unit(blockIdx.x, gridDim.x);
+    const int zhu = unit / nbr;
+    z = zhu / H;
+    hr = row_order_h[(zhu % H) * nbr + unit % nbr];
+  } else {
+    z = blockIdx.x % Z;
+    hr = row_order[blockIdx.x / Z];
+  }
+  const int h = hr / nbr, r = hr % nbr;
   const int k0 = row_ptr[hr], k1 = row_ptr[hr + 1];
   const int64_t zh = (int64_t)z * H + h;
   const int64_t Nq = (int64_t)nbr * BLK, Nk = (int64_t)nbc * BLK;
@@ -404,12 +413,19 @@ template <int BLK, int D, int NS>
 int launch_ns(const bs_layout* L, const void* Q, const void* K, const void* V, void* O, int Z, float c, bool causal,
               hipStream_t s) {
   const dim3 grid(L->H * L->nbr * Z), block(BLK * 2 * NS);
+  // head-grouped order when the longest row (split over NS key groups) is
+  // at most a quarter of the work of one workgroup slot (two per CU): then
+  // even a long row that starts late adds little to the end of the kernel
+  const double per_slot = (double)Z * (double)L->nnz / (2.0 * L->num_cus);
+  const int grouped = (4.0 * L->max_row_len / NS <= per_slot) ? 1 : 0;
   if (causal)
-    hipLaunchKernelGGL((k_attn_bf16<BLK, D, true, NS>), grid, block, 0, s, L->row_ptr, L->col_idx, L->row_order_h,
-                       (const u16*)Q, (const u16*)K, (const u16*)V, (u16*)O, Z, L->H, L->nbr, L->nbc, c);
+    hipLaunchKernelGGL((k_attn_bf16<BLK, D, true, NS>), grid, block, 0, s, L->row_ptr, L->col_idx, L->row_order,
+                       L->row_order_h, (const u16*)Q, (const u16*)K, (const u16*)V, (u16*)O, Z, L->H, L->nbr, L->nbc,
+                       c, grouped);
   else
-    hipLaunchKernelGGL((k_attn_bf16<BLK, D, false, NS>), grid, block, 0, s, L->row_ptr, L->col_idx, L->row_order_h,
-                       (const u16*)Q, (const u16*)K, (const u16*)V, (u16*)O, Z, L->H, L->nbr, L->nbc, c);
+    hipLaunchKernelGGL((k_attn_bf16<BLK, D, false, NS>), grid, block, 0, s, L->row_ptr, L->col_idx, L->row_order,
+                       L->row_order_h, (const u16*)Q, (const u16*)K, (const u16*)V, (u16*)O, Z, L->H, L->nbr, L->nbc,
+                       c, grouped);
   BSA_HIP(hipGetLastError());
   return BS_OK;
 }

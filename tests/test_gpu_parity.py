@@ -373,3 +373,23 @@ def test_attention_bf16_batch_sweep_all_key_group_schedules(b, Z, d):
         ref = oracle.attention_rows(q, k, v, lay, b, scale, causal, rows)
         for n, (z, h, r) in enumerate(rows):
             assert max_abs(f64(O[z, h, r * b:(r + 1) * b]), ref[n]) <= TOL["bf16"], (z, h, r, causal)
+
+
+@pytest.mark.parametrize("b", [32, 64, 128])
+def test_attention_bf16_head_grouped_order(b):
+    """When no row is long against a workgroup's share of the job, the bf16
+    kernel walks the rows grouped by (batch, head), one contiguous range per
+    XCD; a dense layout with a large batch takes that order. Sampled block
+    rows across batch entries and heads against the oracle."""
+    H, nb, d, Z = 2, 4, 128, 256
+    lay = np.ones((H, nb, nb), np.uint8)
+    announce("attention bf16 head-grouped order", b)
+    q, k, v = _tensors([(Z, H, nb * b, d)] * 3, 53, "bf16")
+    L = bsa.Layout(torch.from_numpy(lay), b)
+    scale = 1.0 / np.sqrt(d)
+    for causal in (False, True):
+        O = bsa.attention(L, to_dev(q), to_dev(k), to_dev(v), scale, causal)
+        rows = [(0, 0, 0), (Z - 1, 1, nb - 1), (Z // 2, 0, 2), (Z // 3, 1, 1), (7, 1, 3), (130, 0, 1)]
+        ref = oracle.attention_rows(q, k, v, lay, b, scale, causal, rows)
+        for n, (z, h, r) in enumerate(rows):
+            assert max_abs(f64(O[z, h, r * b:(r + 1) * b]), ref[n]) <= TOL["bf16"], (z, h, r, causal)
