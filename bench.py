@@ -61,7 +61,8 @@ def _source_hash(files):
     return h.hexdigest()[:16]
 
 
-ATTN_SOURCES = ["block_sparse_matmul_amd/csrc/attention.hip", "block_sparse_matmul_amd/csrc/tile.h"]
+ATTN_SOURCES = ["block_sparse_matmul_amd/csrc/attention.hip", "block_sparse_matmul_amd/csrc/attention_bf16.hip",
+                "block_sparse_matmul_amd/csrc/tile.h", "block_sparse_matmul_amd/csrc/internal.h"]
 
 
 def _traffic(workload, launches_flops):
