@@ -13,9 +13,12 @@
 // b contiguous floats per block) are read as 16-byte vectors, 256 floats per
 // wave pass, and kept in registers (up to R vectors per lane) between the
 // max/sum pass and the write pass, so an in-register row costs one read and
-// one write of HBM; longer rows are read a second time. Cross-lane max and
-// sum use butterfly shuffles. P may alias S: each vector is read before the
-// same lanes write it.
+// one write of HBM; longer rows are read a second time. S is read and P
+// written with nontemporal (streaming) accesses: each element is touched
+// once, so it should not displace cached data. Cross-lane max and sum use
+// butterfly shuffles. P may alias S: each vector is read before the same
+// lanes write it. exp2 is the hardware v_exp_f32 (results below the
+// smallest normal flush to zero).
 #include <math.h>
 
 #include "internal.h"
@@ -60,7 +63,7 @@ __global__ __launch_bounds__(256) void k_softmax(const int32_t* __restrict__ row
   auto load = [&](int e) -> f32x4 {  // scaled, masked values of entries e..e+3
     f32x4 x = {NEG, NEG, NEG, NEG};
     if (e < n) {
-      x = *reinterpret_cast<const f32x4*>(S + addr(e));
+      x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + addr(e)));
       x *= c;
       if (CAUSAL) {
         const int kl = e / b, j = e % b;
@@ -101,7 +104,7 @@ __global__ __launch_bounds__(256) void k_softmax(const int32_t* __restrict__ row
     if (p < passes) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        cache[p][q] = exp2f(cache[p][q] - m);
+        cache[p][q] = __builtin_amdgcn_exp2f(cache[p][q] - m);
         s += cache[p][q];
       }
     }
@@ -109,21 +112,21 @@ __global__ __launch_bounds__(256) void k_softmax(const int32_t* __restrict__ row
   for (int p = R; p < passes; ++p) {
     const f32x4 x = load(p * 256 + lane * 4);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) s += exp2f(x[q] - m);
+    for (int q = 0; q < 4; ++q) s += __builtin_amdgcn_exp2f(x[q] - m);
   }
   const float inv = 1.0f / wave_sum(s);
 #pragma unroll
   for (int p = 0; p < R; ++p) {
     const int e = p * 256 + lane * 4;
-    if (p < passes && e < n) *reinterpret_cast<f32x4*>(P + addr(e)) = cache[p] * inv;
+    if (p < passes && e < n) __builtin_nontemporal_store(cache[p] * inv, reinterpret_cast<f32x4*>(P + addr(e)));
   }
   for (int p = R; p < passes; ++p) {
     const int e = p * 256 + lane * 4;
     f32x4 x = load(e);
     if (e < n) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) x[q] = exp2f(x[q] - m) * inv;
-      *reinterpret_cast<f32x4*>(P + addr(e)) = x;
+      for (int q = 0; q < 4; ++q) x[q] = __builtin_amdgcn_exp2f(x[q] - m) * inv;
+      __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(P + addr(e)));
     }
   }
 }
