@@ -131,7 +131,9 @@ __global__ __launch_bounds__(256 * NS) void k_dds(const int32_t* __restrict__ co
       if (qw < total_rows) {
         const int q = q0 + srow[i];
         const int64_t k = blk_id[e0 + qw / BLK];
-        sreg[i] = *reinterpret_cast<const f32x4*>(Sz + k * (BLK * BLK) + (q % BLK) * BLK + scol[i]);
+        // S is read once: a streaming load keeps it from displacing A
+        sreg[i] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(Sz + k * (BLK * BLK) + (q % BLK) * BLK + scol[i]));
       }
     }
     if (active) {
