@@ -44,6 +44,7 @@ __all__ = [
     "element_mask", "sdd", "softmax", "dsd", "dds",
     "attention_dense", "attention_blocks", "attention_rows",
     "attention_blockrow", "nnz_flops_attention", "nnz_flops_dds",
+    "softmax_backward", "dsd_t", "attention_backward_dense", "attention_backward_blocks",
 ]
 
 ALLOWED_BLOCKS = (16, 32, 64, 128)
@@ -332,6 +333,90 @@ def attention_rows(Q, K, V, layout, block: int, scale: float, causal: bool,
 # ---------------------------------------------------------------------------
 # work accounting (FLOPs over stored blocks only)
 # ---------------------------------------------------------------------------
+
+# ---------------------------------------------------------------------------
+# backward: the exact gradient of the forward, two routes
+# ---------------------------------------------------------------------------
+#
+# The pages give the autograd pattern (Triton tutorial: a forward kernel, a
+# backward kernel that receives the gradient of the output and returns the
+# gradients of the inputs, both wrapped in one autograd function) and the
+# three modes the attention gradient is made of. The formulas below are the
+# plain calculus of O = P V with P the masked row softmax of
+# X = scale Q K^T + M: for a loss L with dO = dL/dO,
+#   dV = P^T dO,  dP = dO V^T,  dX = P * (dP - rowsum(P * dP)),
+#   dQ = scale dX K,  dK = scale dX^T Q.
+# Masked entries have P = 0 and so get no gradient.
+
+
+def softmax_backward(P, dP, layout, block: int, scale: float) -> np.ndarray:
+    """Gradient of the block-sparse softmax with respect to its input S,
+    given its output P and the gradient dP of the output: for each query
+    row, D = sum over the row's stored entries of P * dP, and
+    dS = scale * P * (dP - D). Entries the mask hid (P = 0) get zero."""
+    P, dP = _f64(P), _f64(dP)
+    lut = lut_from_layout(layout)
+    lay = check_layout(layout)
+    H, nbr, _ = lay.shape
+    dS = np.zeros_like(P)
+    for hr in range(H * nbr):
+        ks = list(range(lut["row_ptr"][hr], lut["row_ptr"][hr + 1]))
+        if not ks:
+            continue
+        for z in range(P.shape[0]):
+            D = sum((P[z, k] * dP[z, k]).sum(axis=1, keepdims=True) for k in ks)   # [b, 1]
+            for k in ks:
+                dS[z, k] = scale * P[z, k] * (dP[z, k] - D)
+    return dS
+
+
+def dsd_t(S, B, layout, block: int) -> np.ndarray:
+    """Transposed sparse x dense: C[z, h, c-block, :] = sum over stored
+    (h, r, c) of S[z, k]^T @ B[z, h, r-block, :] (the DSD of the transposed
+    block matrix; in attention's backward dK = dS^T Q and dV = P^T dO).
+    Block columns with no stored block give zero rows."""
+    S, B = _f64(S), _f64(B)
+    lay = check_layout(layout)
+    H, _, nbc = lay.shape
+    b = block
+    Z, Nd = B.shape[0], B.shape[3]
+    C = np.zeros((Z, H, nbc * b, Nd), dtype=np.float64)
+    for k, (h, r, c) in enumerate(_blocks(lay)):
+        for z in range(Z):
+            C[z, h, c * b:(c + 1) * b, :] += S[z, k].T @ B[z, h, r * b:(r + 1) * b, :]
+    return C
+
+
+def attention_backward_dense(Q, K, V, dO, layout, block: int, scale: float, causal: bool = False):
+    """Route (i) of the gradient: dense matrices with the element mask.
+    Returns (dQ, dK, dV) for the forward of attention_dense."""
+    Q, K, V, dO = _f64(Q), _f64(K), _f64(V), _f64(dO)
+    mask = element_mask(layout, block, causal)
+    Z, H = Q.shape[:2]
+    dQ, dK, dV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
+    for z in range(Z):
+        for h in range(H):
+            x = np.where(mask[h], scale * (Q[z, h] @ K[z, h].T), -np.inf)
+            m = x.max(axis=1, keepdims=True)
+            e = np.where(np.isfinite(m), np.exp(x - np.where(np.isfinite(m), m, 0.0)), 0.0)
+            s = e.sum(axis=1, keepdims=True)
+            P = np.divide(e, s, out=np.zeros_like(e), where=s > 0)
+            dV[z, h] = P.T @ dO[z, h]
+            dP = dO[z, h] @ V[z, h].T
+            dX = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+            dQ[z, h] = scale * (dX @ K[z, h])
+            dK[z, h] = scale * (dX.T @ Q[z, h])
+    return dQ, dK, dV
+
+
+def attention_backward_blocks(Q, K, V, dO, layout, block: int, scale: float, causal: bool = False):
+    """Route (ii) of the gradient, on the block-sparse operators: P by SDD
+    and softmax (recomputed), dP = SDD(dO, V), dS = softmax_backward(P, dP),
+    dQ = DSD(dS, K), dK = DSD^T(dS, Q), dV = DSD^T(P, dO)."""
+    P = softmax(sdd(Q, K, layout, block), layout, block, scale, causal)
+    dS = softmax_backward(P, sdd(dO, V, layout, block), layout, block, scale)
+    return dsd(dS, K, layout, block), dsd_t(dS, Q, layout, block), dsd_t(P, dO, layout, block)
+
 
 def nnz_flops_attention(nnz: int, Z: int, block: int, d: int) -> int:
     """2 b^2 d flops per stored block for SDD plus 2 b^2 d for DSD."""

@@ -2,7 +2,8 @@
 
 Each case changes one expression of the oracle's source (in a child process,
 on the CPU) to a plausible slip -- a transposed operand, a dropped scale, a
-flipped or off-by-one mask, a wrong block index, a NaN on empty rows -- and
+flipped or off-by-one mask, a wrong block index, a NaN on empty rows, a
+dropped term of the softmax gradient -- and
 runs the oracle pin suite against it. A pin suite that still passes would not
 be able to tell that mistake from the method.
 """
@@ -52,6 +53,21 @@ MUTANTS = {
     "acsr_stride_ignored": (
         "c = slope * r + offset + stride * k",
         "c = slope * r + offset + k"),
+    "softmax_backward_row_term_dropped": (
+        "dS[z, k] = scale * P[z, k] * (dP[z, k] - D)",
+        "dS[z, k] = scale * P[z, k] * dP[z, k]"),
+    "softmax_backward_scale_dropped": (
+        "dS[z, k] = scale * P[z, k] * (dP[z, k] - D)",
+        "dS[z, k] = P[z, k] * (dP[z, k] - D)"),
+    "dsd_t_block_not_transposed": (
+        "C[z, h, c * b:(c + 1) * b, :] += S[z, k].T @ B[z, h, r * b:(r + 1) * b, :]",
+        "C[z, h, c * b:(c + 1) * b, :] += S[z, k] @ B[z, h, r * b:(r + 1) * b, :]"),
+    "dense_backward_dk_untransposed": (
+        "dK[z, h] = scale * (dX.T @ Q[z, h])",
+        "dK[z, h] = scale * (dX @ Q[z, h])"),
+    "dense_backward_dv_untransposed": (
+        "dV[z, h] = P.T @ dO[z, h]",
+        "dV[z, h] = P @ dO[z, h]"),
     "rows_wrong_head_mask": (
         "mask = np.repeat(lay[h, r].astype(bool), b)[None, :].repeat(b, axis=0)",
         "mask = np.repeat(lay[0, r].astype(bool), b)[None, :].repeat(b, axis=0)"),
@@ -63,7 +79,8 @@ def _run_pins(mutant):
     env["BSA_ORACLE_MUTANT"] = json.dumps(list(mutant))
     cmd = [sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
            os.path.join(ROOT, "tests", "test_oracle_lut.py"),
-           os.path.join(ROOT, "tests", "test_oracle_ops.py")]
+           os.path.join(ROOT, "tests", "test_oracle_ops.py"),
+           os.path.join(ROOT, "tests", "test_oracle_backward.py")]
     return subprocess.run(cmd, cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
 
 
