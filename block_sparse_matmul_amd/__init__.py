@@ -10,6 +10,8 @@ supplies device memory and the current stream.
     O = dsd(L, P, v)                  # O = P V
     C = dds(L, a, S)                  # C = A S
     O = attention(L, q, k, v, scale, causal)   # fused SDD -> softmax -> DSD
+    dq, dk, dv = attention_backward(L, q, k, v, do, scale, causal)
+    O = attention_autograd(L, q, k, v, scale, causal)   # differentiable
 
 Operation semantics follow the three block-sparse modes and the softmax of
 Triton issue 117 ("question on blocksparse"); see include/bsattn.h.
@@ -25,7 +27,8 @@ import numpy as np
 from . import _lib
 from ._lib import AcsrTerm, BsError, BS_BF16, BS_CAUSAL, BS_F32, check, lib
 
-__all__ = ["Layout", "sdd", "softmax", "dsd", "dds", "attention", "BsError", "lib"]
+__all__ = ["Layout", "sdd", "softmax", "dsd", "dds", "attention", "softmax_backward", "dsd_t",
+           "attention_backward", "attention_autograd", "BsError", "lib"]
 
 
 def _torch():
@@ -144,6 +147,18 @@ def _empty(shape, dtype, device):
     return _torch().empty(shape, dtype=dtype, device=device)
 
 
+def _out(out, shape, dtype, device, name="out"):
+    """A new output tensor, or the caller's after checking that the kernels
+    can write all of it (shape, dtype, device, contiguity)."""
+    shape = tuple(shape)
+    if out is None:
+        return _empty(shape, dtype, device)
+    if (tuple(out.shape) != shape or out.dtype != dtype or not out.is_cuda or out.device != device
+            or not out.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {shape} on {device}")
+    return out
+
+
 def sdd(L: Layout, a, b, out=None):
     """S[z, k] = a[z, h, r-block, :] @ b[z, h, c-block, :]^T for each stored block."""
     torch = _torch()
@@ -152,10 +167,7 @@ def sdd(L: Layout, a, b, out=None):
     Z, H, Na, K = a.shape
     if a.dtype != b.dtype or b.shape != (Z, H, L.nbc * L.block, K) or (H, Na) != (L.H, L.nbr * L.block):
         raise ValueError("a must be [Z, H, nbr*b, K] and b [Z, H, nbc*b, K] of one dtype")
-    if out is None:
-        out = _empty((Z, L.nnz, L.block, L.block), torch.float32, a.device)
-    elif out.shape != (Z, L.nnz, L.block, L.block) or out.dtype != torch.float32 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float32 [Z, nnz, b, b] tensor")
+    out = _out(out, (Z, L.nnz, L.block, L.block), torch.float32, a.device)
     check(lib().bs_sdd(L.handle, _ptr(a), _ptr(b), _ptr(out), Z, K, _dtype_code(a), _stream(a.device)))
     return out
 
@@ -166,10 +178,7 @@ def softmax(L: Layout, s, scale: float, causal: bool = False, out=None, inplace:
     _check_dense("s", s)
     if s.dtype != torch.float32 or s.shape[1:] != (L.nnz, L.block, L.block):
         raise ValueError("s must be float32 [Z, nnz, b, b]")
-    if inplace:
-        out = s
-    elif out is None:
-        out = torch.empty_like(s)
+    out = s if inplace else _out(out, s.shape, torch.float32, s.device)
     check(lib().bs_softmax(L.handle, _ptr(s), _ptr(out), s.shape[0], float(scale),
                            BS_CAUSAL if causal else 0, _stream(s.device)))
     return out
@@ -185,8 +194,7 @@ def dsd(L: Layout, p, b, out=None):
         raise ValueError("p must be float32 [Z, nnz, b, b]")
     if (H, Nb) != (L.H, L.nbc * L.block):
         raise ValueError("b must be [Z, H, nbc*b, Nd]")
-    if out is None:
-        out = _empty((Z, H, L.nbr * L.block, Nd), b.dtype, b.device)
+    out = _out(out, (Z, H, L.nbr * L.block, Nd), b.dtype, b.device)
     check(lib().bs_dsd(L.handle, _ptr(p), _ptr(b), _ptr(out), Z, Nd, _dtype_code(b), _stream(b.device)))
     return out
 
@@ -201,8 +209,7 @@ def dds(L: Layout, a, s, out=None):
         raise ValueError("s must be float32 [Z, nnz, b, b]")
     if (H, Na) != (L.H, L.nbr * L.block):
         raise ValueError("a must be [Z, H, M, nbr*b]")
-    if out is None:
-        out = _empty((Z, H, M, L.nbc * L.block), a.dtype, a.device)
+    out = _out(out, (Z, H, M, L.nbc * L.block), a.dtype, a.device)
     check(lib().bs_dds(L.handle, _ptr(a), _ptr(s), _ptr(out), Z, M, _dtype_code(a), _stream(a.device)))
     return out
 
@@ -218,8 +225,104 @@ def attention(L: Layout, q, k, v, scale: Optional[float] = None, causal: bool = 
         raise ValueError("q must be [Z, H, nbr*b, d]; k, v [Z, H, nbc*b, d]")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = _empty(q.shape, q.dtype, q.device)
+    out = _out(out, q.shape, q.dtype, q.device)
     check(lib().bs_attention(L.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(out), Z, d, float(scale),
                              BS_CAUSAL if causal else 0, _dtype_code(q), _stream(q.device)))
     return out
+
+
+# ------------------------------------------------------------------ backward
+
+def softmax_backward(L: Layout, p, dp, scale: float, out=None, inplace: bool = False):
+    """Gradient of softmax with respect to its input: for each query row,
+    dS = scale * p * (dp - sum over the row of p * dp)."""
+    torch = _torch()
+    _check_dense("p", p)
+    _check_dense("dp", dp)
+    if p.dtype != torch.float32 or p.shape[1:] != (L.nnz, L.block, L.block) or dp.shape != p.shape \
+            or dp.dtype != torch.float32:
+        raise ValueError("p and dp must be float32 [Z, nnz, b, b]")
+    out = dp if inplace else _out(out, p.shape, torch.float32, p.device)
+    check(lib().bs_softmax_backward(L.handle, _ptr(p), _ptr(dp), _ptr(out), p.shape[0], float(scale),
+                                    _stream(p.device)))
+    return out
+
+
+def dsd_t(L: Layout, s, b, out=None):
+    """C[z, h, c-block, :] = sum over stored (h, r, c) of s[z, k]^T @ b[z, h, r-block, :]."""
+    torch = _torch()
+    _check_dense("s", s)
+    _check_dense("b", b)
+    Z, H, Nb, Nd = b.shape
+    if s.dtype != torch.float32 or s.shape != (Z, L.nnz, L.block, L.block):
+        raise ValueError("s must be float32 [Z, nnz, b, b]")
+    if (H, Nb) != (L.H, L.nbr * L.block):
+        raise ValueError("b must be [Z, H, nbr*b, Nd]")
+    out = _out(out, (Z, H, L.nbc * L.block, Nd), b.dtype, b.device)
+    check(lib().bs_dsd_t(L.handle, _ptr(s), _ptr(b), _ptr(out), Z, Nd, _dtype_code(b), _stream(b.device)))
+    return out
+
+
+def attention_backward(L: Layout, q, k, v, do, scale: Optional[float] = None, causal: bool = False,
+                       workspace: Optional[Tuple] = None):
+    """(dq, dk, dv) of attention() for the output gradient do, in one library
+    call: P recomputed by SDD and softmax, dP = SDD(do, v), dS = softmax
+    gradient, dq = DSD(dS, k), dk = DSD^T(dS, q), dv = DSD^T(P, do).
+    workspace: optional pair of float32 [Z, nnz, b, b] tensors."""
+    torch = _torch()
+    for n, t in (("q", q), ("k", k), ("v", v), ("do", do)):
+        _check_dense(n, t)
+    Z, H, Nq, d = q.shape
+    if not (q.dtype == k.dtype == v.dtype == do.dtype):
+        raise ValueError("q, k, v, do must share a dtype")
+    if (H, Nq) != (L.H, L.nbr * L.block) or k.shape != (Z, H, L.nbc * L.block, d) or v.shape != k.shape \
+            or do.shape != q.shape:
+        raise ValueError("q and do must be [Z, H, nbr*b, d]; k, v [Z, H, nbc*b, d]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    ws_shape = (Z, L.nnz, L.block, L.block)
+    ws_s, ws_p = workspace if workspace is not None else (None, None)
+    ws_s = _out(ws_s, ws_shape, torch.float32, q.device, "workspace")
+    ws_p = _out(ws_p, ws_shape, torch.float32, q.device, "workspace")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    check(lib().bs_attention_backward(L.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
+                                      _ptr(ws_s), _ptr(ws_p), Z, d, float(scale), BS_CAUSAL if causal else 0,
+                                      _dtype_code(q), _stream(q.device)))
+    return dq, dk, dv
+
+
+_AUTOGRAD_FN = None
+
+
+def _autograd_fn():
+    """The torch.autograd.Function pairing attention() with
+    attention_backward() (built on first use, so importing this package
+    does not import torch)."""
+    global _AUTOGRAD_FN
+    if _AUTOGRAD_FN is None:
+        torch = _torch()
+
+        class BlockSparseAttention(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q, k, v, L, scale, causal):
+                ctx.save_for_backward(q, k, v)
+                ctx.L, ctx.scale, ctx.causal = L, scale, causal
+                return attention(L, q, k, v, scale, causal)
+
+            @staticmethod
+            def backward(ctx, do):
+                q, k, v = ctx.saved_tensors
+                dq, dk, dv = attention_backward(ctx.L, q, k, v, do.contiguous(), ctx.scale, ctx.causal)
+                return dq, dk, dv, None, None, None
+
+        _AUTOGRAD_FN = BlockSparseAttention
+    return _AUTOGRAD_FN
+
+
+def attention_autograd(L: Layout, q, k, v, scale: Optional[float] = None, causal: bool = False):
+    """attention() as a differentiable torch op (forward: the fused kernel;
+    backward: attention_backward)."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    return _autograd_fn().apply(q, k, v, L, float(scale), bool(causal))
+

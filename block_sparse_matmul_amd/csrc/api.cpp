@@ -62,7 +62,8 @@ int check_dims(int H, int nbr, int nbc, int block) {
 // one workgroup per (batch, block row / column) on a 1-D grid
 int check_grid(const bs_layout* L, int Z) {
   const int64_t units = (int64_t)Z * L->H * (L->nbr > L->nbc ? L->nbr : L->nbc);
-  if (units > (int64_t)1 << 22) return fail(BS_ERR_SHAPE, "Z*H*blocks per side exceeds 2^22 workgroups");
+  // below 2^22 workgroups: with up to 1024 threads each, the grid stays under 2^32 work-items
+  if (units >= (int64_t)1 << 22) return fail(BS_ERR_SHAPE, "Z*H*blocks per side must be below 2^22 workgroups");
   return BS_OK;
 }
 
@@ -266,6 +267,66 @@ int bs_dsd(bs_layout_t L, const float* P, const void* B, void* C, int Z, int Nd,
   if (int rc = check_grid(L, Z)) return rc;
   log_call("dsd", L, Z, Nd);
   return bsa::launch_dsd(L, P, B, C, Z, Nd, dt, (hipStream_t)stream);
+}
+
+int bs_softmax_backward(bs_layout_t L, const float* P, const float* dP, float* dS, int Z, float scale, void* stream) {
+  if (int rc = check_handle(L)) return rc;
+  if (Z < 0) return fail(BS_ERR_INVALID_ARG, "Z must be >= 0");
+  const bool work = Z > 0 && L->nnz > 0;
+  if (int rc = check_ptrs(work, {P, dP, dS})) return rc;
+  if (!work) return BS_OK;
+  if ((int64_t)L->H * L->nbr * L->block > std::numeric_limits<int32_t>::max() - 4)
+    return fail(BS_ERR_SHAPE, "too many query rows");
+  log_call("softmax_backward", L, Z, 0);
+  return bsa::launch_softmax_backward(L, P, dP, dS, Z, scale, (hipStream_t)stream);
+}
+
+int bs_dsd_t(bs_layout_t L, const float* S, const void* B, void* C, int Z, int Nd, bs_dtype dt, void* stream) {
+  if (int rc = check_handle(L)) return rc;
+  if (int rc = check_dtype(dt)) return rc;
+  if (Z < 0 || Nd <= 0) return fail(BS_ERR_INVALID_ARG, "Z must be >= 0 and Nd > 0");
+  if (Nd != 64 && Nd != 128) return fail(BS_ERR_UNSUPPORTED, "Nd must be 64 or 128");
+  const bool work = Z > 0;
+  if (int rc = check_ptrs(work, {B, C})) return rc;
+  if (work && L->nnz > 0) {
+    if (int rc = check_ptrs(true, {S})) return rc;
+  }
+  if (!work) return BS_OK;
+  if (int rc = check_grid(L, Z)) return rc;
+  log_call("dsd_t", L, Z, Nd);
+  return bsa::launch_dsd_t(L, S, B, C, Z, Nd, dt, (hipStream_t)stream);
+}
+
+int bs_attention_backward(bs_layout_t L, const void* Q, const void* K, const void* V, const void* dO, void* dQ,
+                          void* dK, void* dV, float* ws_s, float* ws_p, int Z, int d, float scale, int flags,
+                          bs_dtype dt, void* stream) {
+  if (int rc = check_handle(L)) return rc;
+  if (int rc = check_dtype(dt)) return rc;
+  if (flags & ~BS_CAUSAL) return fail(BS_ERR_INVALID_ARG, "unknown flag");
+  if (Z < 0) return fail(BS_ERR_INVALID_ARG, "Z must be >= 0");
+  if (d != 64 && d != 128) return fail(BS_ERR_UNSUPPORTED, "head size d must be 64 or 128");
+  const bool causal = flags & BS_CAUSAL;
+  if (causal && L->nbr != L->nbc) return fail(BS_ERR_INVALID_ARG, "causal attention needs a square layout");
+  const bool work = Z > 0;
+  if (int rc = check_ptrs(work, {Q, K, V, dO, dQ, dK, dV})) return rc;
+  if (work && L->nnz > 0) {
+    if (int rc = check_ptrs(true, {ws_s, ws_p})) return rc;
+  }
+  if (!work) return BS_OK;
+  if (int rc = check_grid(L, Z)) return rc;
+  if ((int64_t)Z * L->nnz * L->block * L->block > ((int64_t)1 << 46))
+    return fail(BS_ERR_SHAPE, "block-sparse tensor too large");
+  if ((int64_t)L->H * L->nbr * L->block > std::numeric_limits<int32_t>::max() - 4)
+    return fail(BS_ERR_SHAPE, "too many query rows");
+  log_call("attention_backward", L, Z, d);
+  hipStream_t s = (hipStream_t)stream;
+  if (int rc = bsa::launch_sdd(L, Q, K, ws_s, Z, d, dt, s)) return rc;                  // S = Q K^T
+  if (int rc = bsa::launch_softmax(L, ws_s, ws_p, Z, scale, causal, s)) return rc;     // P
+  if (int rc = bsa::launch_sdd(L, dO, V, ws_s, Z, d, dt, s)) return rc;                 // dP = dO V^T
+  if (int rc = bsa::launch_softmax_backward(L, ws_p, ws_s, ws_s, Z, scale, s)) return rc;  // dS
+  if (int rc = bsa::launch_dsd(L, ws_s, K, dQ, Z, d, dt, s)) return rc;                 // dQ = dS K
+  if (int rc = bsa::launch_dsd_t(L, ws_s, Q, dK, Z, d, dt, s)) return rc;               // dK = dS^T Q
+  return bsa::launch_dsd_t(L, ws_p, dO, dV, Z, d, dt, s);                               // dV = P^T dO
 }
 
 int bs_dds(bs_layout_t L, const void* A, const float* S, void* C, int Z, int M, bs_dtype dt, void* stream) {

@@ -61,7 +61,10 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kTau = 8.0f;  // lazy-rescale headroom, log2 units
 
-enum Mode { MODE_ATTN = 0, MODE_SDD = 1, MODE_DSD = 2 };
+// MODE_DSDT is the DSD of the transposed block matrix (C = S^T-blocks x B):
+// the same kernel walking block columns (CSC) and reading each stored block
+// transposed.
+enum Mode { MODE_ATTN = 0, MODE_SDD = 1, MODE_DSD = 2, MODE_DSDT = 3 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -89,25 +92,30 @@ struct Lds {
   using St = typename Elem<E>::storage;
   static constexpr int KSTR = D + 32 / (int)sizeof(St);
   static constexpr int VSTR = std::is_same<E, bf16_t>::value ? D + 16 : D + 4;
-  static constexpr int KBUF = MODE == MODE_DSD ? 0 : BLK * KSTR;  // elements per key group
+  static constexpr int KBUF = (MODE == MODE_DSD || MODE == MODE_DSDT) ? 0 : BLK * KSTR;  // per key group
   static constexpr int VBUF = MODE == MODE_SDD ? 0 : BLK * VSTR;
   static constexpr size_t STAGE = (size_t)(KBUF + VBUF) * sizeof(St);  // bytes per key group
 };
 
 // Q, K, V, O: [Z][H][N][D] dense operands; S: [Z][nnz][BLK][BLK] fp32 block
 // values (SDD output, DSD input). MODE_ATTN uses Q, K, V -> O; MODE_SDD
-// uses Q (= A), K (= B) -> S; MODE_DSD uses S (= P), V (= B) -> O (= C).
+// uses Q (= A), K (= B) -> S; MODE_DSD uses S (= P), V (= B) -> O (= C);
+// MODE_DSDT takes the column tables (col_ptr, row_idx, col_order and blk_id
+// in place of row_ptr, col_idx, row_order and the identity) with nbr and nbc
+// swapped, and reads each block of S transposed.
 template <typename E, int BLK, int D, bool CAUSAL, int NS, int MODE>
 __global__ __launch_bounds__(BLK * 4 * NS) void k_rowblock(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, const int32_t* __restrict__ row_order,
     const typename Elem<E>::storage* __restrict__ Q, const typename Elem<E>::storage* __restrict__ K,
     const typename Elem<E>::storage* __restrict__ V, typename Elem<E>::storage* __restrict__ O,
-    float* __restrict__ S, int Z, int H, int nbr, int nbc, int64_t nnz, float c) {
+    float* __restrict__ S, const int32_t* __restrict__ blk_id, int Z, int H, int nbr, int nbc, int64_t nnz,
+    float c) {
   using St = typename Elem<E>::storage;
   using Vec = typename Cfg<E>::Vec;
   constexpr bool BF = std::is_same<E, bf16_t>::value;
   constexpr bool ATTN = MODE == MODE_ATTN;
-  constexpr bool HASK = MODE != MODE_DSD;  // score product (Q, K staged)
+  constexpr bool DSDT = MODE == MODE_DSDT;
+  constexpr bool HASK = MODE != MODE_DSD && !DSDT;  // score product (Q, K staged)
   constexpr bool HASV = MODE != MODE_SDD;  // P.V product (V staged)
   constexpr int VEC = Cfg<E>::VEC, KC = Cfg<E>::KC;
   constexpr int NW = BLK / 16, NT = 64 * NW;  // waves / threads of one key group
@@ -254,7 +262,11 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_rowblock(
     // blocks whose every key is after every query of this wave add nothing
     const bool compute = valid && !(ATTN && CAUSAL && cb * BLK > q_lo + 15);
     const bool mask_block = ATTN && CAUSAL && (cb * BLK + BLK - 1 > q_lo);
-    float* const s_blk = S + ((int64_t)z * nnz + kk) * (BLK * BLK) + s_lane;
+    const int64_t blk = DSDT ? (valid ? (int64_t)blk_id[kk] : 0) : (int64_t)kk;  // stored block id
+    float* const s_blk = S + ((int64_t)z * nnz + blk) * (BLK * BLK) + s_lane;
+    // DSDT: element (i, j) of the transposed block is S[j][i]; this lane
+    // needs keys kofs + 16 jt + 4 g + rr of query wave*16 + li
+    const float* const st_blk = S + ((int64_t)z * nnz + blk) * (BLK * BLK) + (int64_t)(4 * g) * BLK + wave * 16 + li;
 
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub) {
@@ -312,6 +324,14 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_rowblock(
           }
         }
         continue;
+      }
+      if constexpr (DSDT) {
+        if (compute) {
+#pragma unroll
+          for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) s[jt][rr] = st_blk[(int64_t)(kofs + 16 * jt + rr) * BLK];
+        }
       }
       if constexpr (MODE == MODE_DSD) {
         // P block rows straight into the score-register layout
@@ -525,15 +545,21 @@ struct Args {
 template <typename E, int BLK, int D, int NS, int MODE>
 int launch_ns(const bs_layout* L, const Args& a, hipStream_t s) {
   using St = typename Elem<E>::storage;
-  const dim3 grid(L->H * L->nbr * a.Z), block(BLK * 4 * NS);
+  constexpr bool T = MODE == MODE_DSDT;  // column-wise
+  const int units = T ? L->nbc : L->nbr;
+  const dim3 grid(L->H * units * a.Z), block(BLK * 4 * NS);
+  const int32_t* ptr = T ? L->col_ptr : L->row_ptr;
+  const int32_t* idx = T ? L->row_idx : L->col_idx;
+  const int32_t* order = T ? L->col_order : L->row_order;
+  const int32_t* bid = T ? L->blk_id : nullptr;
+  const int nb_out = T ? L->nbc : L->nbr, nb_in = T ? L->nbr : L->nbc;
   if (MODE == MODE_ATTN && a.causal)
-    hipLaunchKernelGGL((k_rowblock<E, BLK, D, true, NS, MODE>), grid, block, 0, s, L->row_ptr, L->col_idx,
-                       L->row_order, (const St*)a.Q, (const St*)a.K, (const St*)a.V, (St*)a.O, a.S, a.Z, L->H,
-                       L->nbr, L->nbc, L->nnz, a.c);
+    hipLaunchKernelGGL((k_rowblock<E, BLK, D, true, NS, MODE>), grid, block, 0, s, ptr, idx, order, (const St*)a.Q,
+                       (const St*)a.K, (const St*)a.V, (St*)a.O, a.S, bid, a.Z, L->H, nb_out, nb_in, L->nnz, a.c);
   else
-    hipLaunchKernelGGL((k_rowblock<E, BLK, D, false, NS, MODE>), grid, block, 0, s, L->row_ptr, L->col_idx,
-                       L->row_order, (const St*)a.Q, (const St*)a.K, (const St*)a.V, (St*)a.O, a.S, a.Z, L->H,
-                       L->nbr, L->nbc, L->nnz, a.c);
+    hipLaunchKernelGGL((k_rowblock<E, BLK, D, false, NS, MODE>), grid, block, 0, s, ptr, idx, order,
+                       (const St*)a.Q, (const St*)a.K, (const St*)a.V, (St*)a.O, a.S, bid, a.Z, L->H, nb_out, nb_in,
+                       L->nnz, a.c);
   BSA_HIP(hipGetLastError());
   return BS_OK;
 }
@@ -543,10 +569,10 @@ int launch_ns(const bs_layout* L, const Args& a, hipStream_t s) {
 // whole share of the job is Z*nnz/CUs block-times: once the longest row
 // exceeds that, it sets the end of the kernel. NS groups cut the row's own
 // time by NS (the groups run its blocks side by side and merge at the end).
-inline int pick_key_groups(const bs_layout* L, int Z, int max_ns) {
+inline int pick_key_groups(const bs_layout* L, int Z, int max_ns, int max_len) {
   const double per_cu = (double)Z * (double)L->nnz / L->num_cus;
   int ns = 1;
-  while (ns < max_ns && 4.0 * L->max_row_len / ns > per_cu) ns *= 2;
+  while (ns < max_ns && 4.0 * max_len / ns > per_cu) ns *= 2;
   return ns;
 }
 
@@ -555,7 +581,7 @@ int run(const bs_layout* L, const Args& a, hipStream_t s) {
   // largest key-group count (up to 4, and 1024 threads) whose LDS fits in 160 KiB
   constexpr size_t stage = Lds<E, BLK, D, MODE>::STAGE;
   constexpr int max_ns = (BLK <= 64 && 4 * stage <= 160 * 1024) ? 4 : ((BLK <= 64 && 2 * stage <= 160 * 1024) ? 2 : 1);
-  const int ns = pick_key_groups(L, a.Z, max_ns);
+  const int ns = pick_key_groups(L, a.Z, max_ns, MODE == MODE_DSDT ? L->max_col_len : L->max_row_len);
   if constexpr (max_ns >= 4) {
     if (ns >= 4) return launch_ns<E, BLK, D, 4, MODE>(L, a, s);
   }
@@ -606,6 +632,13 @@ int launch_dsd_rowblock(const bs_layout* L, const float* P, const void* B, void*
   if (Nd != 64 && Nd != 128) return kNotApplicable;
   const Args a{nullptr, nullptr, B, C, const_cast<float*>(P), Z, 1.f, false};
   return run_mode<MODE_DSD>(L, a, Nd, dt, s);
+}
+
+int launch_dsd_t(const bs_layout* L, const float* S, const void* B, void* C, int Z, int Nd, bs_dtype dt,
+                 hipStream_t s) {
+  if (Nd != 64 && Nd != 128) return fail(BS_ERR_UNSUPPORTED, "bs_dsd_t supports Nd = 64 or 128");
+  const Args a{nullptr, nullptr, B, C, const_cast<float*>(S), Z, 1.f, false};
+  return run_mode<MODE_DSDT>(L, a, Nd, dt, s);
 }
 
 }  // namespace bsa

@@ -72,6 +72,10 @@ int launch_dds(const bs_layout* L, const void* A, const float* S, void* C,
 int launch_attention(const bs_layout* L, const void* Q, const void* K,
                      const void* V, void* O, int Z, int d, float scale,
                      bool causal, bs_dtype dt, hipStream_t s);
+int launch_softmax_backward(const bs_layout* L, const float* P, const float* dP, float* dS, int Z, float scale,
+                            hipStream_t s);
+int launch_dsd_t(const bs_layout* L, const float* S, const void* B, void* C, int Z, int Nd, bs_dtype dt,
+                 hipStream_t s);
 
 // SDD and DSD on the fused kernel's row-block machinery (LDS-staged
 // operands); they apply when the contraction (SDD) or output width (DSD) is

@@ -143,7 +143,87 @@ void launch_r(const bs_layout* L, const float* S, float* P, int Z, float c, bool
                        L->block, L->nnz, c);
 }
 
+// Gradient of the softmax above with respect to its input S, given P and
+// dP = dL/dP: per query row D = sum of P * dP over the row's stored entries,
+// then dS = scale * P * (dP - D) (entries the mask hid have P = 0 and get
+// 0). Same row-per-wave layout; both P and dP are kept in registers (up to R
+// vectors each) between the reduction and the write, longer rows are read
+// again. dS may alias dP (or P): every vector is read before the same lanes
+// write it.
+template <int R>
+__global__ __launch_bounds__(256) void k_softmax_bwd(const int32_t* __restrict__ row_ptr, const float* P,
+                                                     const float* dP, float* dS, int rows, int b, int64_t nnz,
+                                                     float scale) {
+  const int lane = threadIdx.x & 63;
+  const int qrow = blockIdx.x * 4 + (threadIdx.x >> 6);  // (h, r, i) flattened
+  if (qrow >= rows * b) return;
+  const int z = blockIdx.y;
+  const int hr = qrow / b, i = qrow % b;
+  const int k0 = row_ptr[hr], k1 = row_ptr[hr + 1];
+  const int n = (k1 - k0) * b;
+  const int64_t zbase = (int64_t)z * nnz;
+  auto addr = [&](int e) -> int64_t {
+    const int kl = e / b, j = e % b;
+    return ((zbase + k0 + kl) * b + i) * (int64_t)b + j;
+  };
+  auto load = [&](const float* X, int e) -> f32x4 {
+    return e < n ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(X + addr(e))) : f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  const int passes = (n + 255) / 256;
+  f32x4 cp[R], cd[R];
+  float acc = 0.f;
+#pragma unroll
+  for (int p = 0; p < R; ++p) {
+    if (p < passes) {
+      const int e = p * 256 + lane * 4;
+      cp[p] = load(P, e);
+      cd[p] = load(dP, e);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc = fmaf(cp[p][q], cd[p][q], acc);
+    }
+  }
+  for (int p = R; p < passes; ++p) {
+    const int e = p * 256 + lane * 4;
+    const f32x4 x = load(P, e), y = load(dP, e);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc = fmaf(x[q], y[q], acc);
+  }
+  const float D = wave_sum(acc);
+#pragma unroll
+  for (int p = 0; p < R; ++p) {
+    const int e = p * 256 + lane * 4;
+    if (p < passes && e < n)
+      __builtin_nontemporal_store(scale * cp[p] * (cd[p] - D), reinterpret_cast<f32x4*>(dS + addr(e)));
+  }
+  for (int p = R; p < passes; ++p) {
+    const int e = p * 256 + lane * 4;
+    const f32x4 x = load(P, e), y = load(dP, e);
+    if (e < n) __builtin_nontemporal_store(scale * x * (y - D), reinterpret_cast<f32x4*>(dS + addr(e)));
+  }
+}
+
+template <int R>
+void launch_bwd_r(const bs_layout* L, const float* P, const float* dP, float* dS, int Z, float scale, hipStream_t s) {
+  const int rows = L->H * L->nbr;
+  const dim3 grid((unsigned)(((int64_t)rows * L->block + 3) / 4), Z);
+  hipLaunchKernelGGL((k_softmax_bwd<R>), grid, dim3(256), 0, s, L->row_ptr, P, dP, dS, rows, L->block, L->nnz,
+                     scale);
+}
+
 }  // namespace
+
+int launch_softmax_backward(const bs_layout* L, const float* P, const float* dP, float* dS, int Z, float scale,
+                            hipStream_t s) {
+  const int64_t longest = (int64_t)L->max_row_len * L->block;
+  if (longest <= 4 * 256)
+    launch_bwd_r<4>(L, P, dP, dS, Z, scale, s);
+  else if (longest <= 8 * 256)
+    launch_bwd_r<8>(L, P, dP, dS, Z, scale, s);
+  else
+    launch_bwd_r<16>(L, P, dP, dS, Z, scale, s);
+  BSA_HIP(hipGetLastError());
+  return BS_OK;
+}
 
 int launch_softmax(const bs_layout* L, const float* S, float* P, int Z, float scale, bool causal, hipStream_t s) {
   const int64_t longest = (int64_t)L->max_row_len * L->block;  // floats in the longest row

@@ -155,6 +155,43 @@ int bs_attention(bs_layout_t L, const void* Q, const void* K, const void* V,
                  void* O, int Z, int d, float scale, int flags, bs_dtype dt,
                  void* stream);
 
+/* ---- backward (the exact gradient of the forward above) ----
+   The attention gradient is made of the same three modes (the issue's
+   SDD / DSD / DDS) plus the softmax gradient; the autograd pattern (forward
+   kernel, backward kernel, one autograd function) is the Triton tutorial's.
+   With P the softmax output and dO = dL/dO:
+     dV = P^T dO, dP = dO V^T, dS = scale * P * (dP - rowsum(P * dP)),
+     dQ = dS K, dK = dS^T Q. */
+
+/* Gradient of bs_softmax with respect to S, given its output P and
+   dP = dL/dP: for query row i of block row r of head h,
+   D = sum over the row's stored entries of P * dP, and
+   dS = scale * P * (dP - D); entries the mask hid (P = 0) get zero.
+   P, dP, dS: float32 [Z][nnz][b][b]; dS may equal dP or P (in place). */
+int bs_softmax_backward(bs_layout_t L, const float* P, const float* dP,
+                        float* dS, int Z, float scale, void* stream);
+
+/* DSD of the transposed block matrix:
+   C[z,h,c-block,:] = sum over stored (h,r,c) of S[z,k]^T . B[z,h,r-block,:]
+   (in attention's backward dK = dS^T Q and dV = P^T dO).
+   S: float32 [Z][nnz][b][b]; B: [Z][H][nbr*b][Nd], C: [Z][H][nbc*b][Nd] of
+   dtype dt (bf16: S is rounded to bf16 for the product, C is rounded from
+   the float32 accumulator). Block columns with no stored block are written
+   as zero. Nd in {64, 128}. */
+int bs_dsd_t(bs_layout_t L, const float* S, const void* B, void* C, int Z,
+             int Nd, bs_dtype dt, void* stream);
+
+/* Backward of bs_attention: dQ, dK, dV from Q, K, V and dO, recomputing P
+   (SDD, softmax), then dP = SDD(dO, V), dS = softmax gradient,
+   dQ = DSD(dS, K), dK = DSD^T(dS, Q), dV = DSD^T(P, dO). Shapes and dtype
+   as bs_attention (dQ like Q, dK and dV like K); d in {64, 128}.
+   ws_s and ws_p are caller-owned float32 workspaces of Z*nnz*b*b elements
+   each (the library allocates nothing here); on return ws_p holds P. */
+int bs_attention_backward(bs_layout_t L, const void* Q, const void* K,
+                          const void* V, const void* dO, void* dQ, void* dK,
+                          void* dV, float* ws_s, float* ws_p, int Z, int d,
+                          float scale, int flags, bs_dtype dt, void* stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* bs_last_error(void);
 
