@@ -83,6 +83,13 @@ def _traffic(workload, launches_flops):
         return None
 
 
+def attention_flops(nnz, Z, block, d):
+    """FLOPs on stored blocks: 2 b^2 d for the score product plus 2 b^2 d for
+    P.V, per stored block and batch entry (masked halves of diagonal blocks
+    count)."""
+    return 4 * block * block * d * nnz * Z
+
+
 def cpu_baseline(w, lay, q, k, v, budget_s=12.0, seed=0):
     """The oracle's per-block route on a seeded random sample of block rows,
     for about budget_s seconds of CPU time; TFLOP/s over the sampled rows'
@@ -123,7 +130,6 @@ def run_workload(w, steps, warmup, with_ops=True, with_cpu=True):
 
     import block_sparse_matmul_amd as bsa
     import workloads as W
-    import oracle
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -139,7 +145,7 @@ def run_workload(w, steps, warmup, with_ops=True, with_cpu=True):
         L = bsa.Layout(torch.from_numpy(lay), w.block)
     lut_ms = (time.perf_counter() - t0) * 1e3
     out = torch.empty_like(q)
-    flops = oracle.nnz_flops_attention(L.nnz, w.Z, w.block, w.d)
+    flops = attention_flops(L.nnz, w.Z, w.block, w.d)
 
     def step():
         bsa.attention(L, q, k, v, w.scale, w.causal, out=out)
@@ -180,6 +186,19 @@ def run_workload(w, steps, warmup, with_ops=True, with_cpu=True):
                 "softmax_hbm_frac": round(2 * sbytes / (t_sm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             }
             del S, O2
+            # backward: P recomputed (SDD, softmax), dP = SDD(dO, V), softmax
+            # gradient, dQ = DSD(dS, K), dK and dV by DSD^T: five products
+            g = torch.Generator("cpu").manual_seed(1)
+            do = torch.randn(q.shape, generator=g).to(q.dtype).to(dev)
+            ws = (torch.empty((w.Z, L.nnz, w.block, w.block), dtype=torch.float32, device=dev),
+                  torch.empty((w.Z, L.nnz, w.block, w.block), dtype=torch.float32, device=dev))
+            bsa.attention_backward(L, q, k, v, do, w.scale, w.causal, workspace=ws)
+            t_bwd = _events_time(lambda: bsa.attention_backward(L, q, k, v, do, w.scale, w.causal, workspace=ws),
+                                 n, stream)
+            fb = 10 * w.block * w.block * w.d * L.nnz * w.Z
+            ops["backward"] = {"ms": round(t_bwd, 4), "tflops": round(fb / (t_bwd * 1e-3) / 1e12, 3),
+                               "flops": "10 b^2 d per stored block (5 products, P recomputed)"}
+            del do, ws
         if w.dds_m:
             A, Sd = W.make_dds_operands(w, L.nnz)
             A, Sd = A.to(dev), Sd.to(dev)
@@ -187,7 +206,7 @@ def run_workload(w, steps, warmup, with_ops=True, with_cpu=True):
             n = max(3, steps // 2)
             bsa.dds(L, A, Sd, out=C)
             t_dds = _events_time(lambda: bsa.dds(L, A, Sd, out=C), n, stream)
-            fd = oracle.nnz_flops_dds(L.nnz, w.Z, w.block, w.dds_m)
+            fd = 2 * w.block * w.block * w.dds_m * L.nnz * w.Z
             ops["dds"] = {"ms": round(t_dds, 4), "tflops": round(fd / (t_dds * 1e-3) / 1e12, 3),
                           "frac": round(fd / (t_dds * 1e-3) / 1e12 / PEAK_TFLOPS[w.dtype], 4), "M": w.dds_m}
             del A, Sd, C
