@@ -9,6 +9,9 @@
 #include <limits>
 #include <string>
 
+#include <algorithm>
+#include <vector>
+
 #include "internal.h"
 
 namespace bsa {
@@ -141,6 +144,44 @@ int bs_layout_build(const uint8_t* layout, int H, int nbr, int nbc, int block, v
   return finish_build(L, layout, (hipStream_t)stream, out);
 }
 
+// ACSR terms analysed on the host (SPLAT's just-in-time reading of the
+// format): when every term has slope 1 and covers every row, the columns of
+// row r are r + d for d in one set of relative offsets (the union of the
+// terms' offset + stride*k), clipped to the grid. That set, sorted, lets the
+// fused kernel compute a row's columns instead of loading them. Offsets that
+// no row can use (outside -(nbr-1) .. nbc-1) are dropped. Returns BS_OK also
+// when the terms do not qualify (the handle then keeps only the CSR tables).
+static int analyse_band(bs_layout* L, const bs_acsr_term* terms, int n_terms) {
+  if (n_terms == 0) return BS_OK;
+  const int64_t lo = -(int64_t)(L->nbr - 1), hi = (int64_t)L->nbc - 1;
+  std::vector<int32_t> d;
+  for (int t = 0; t < n_terms; ++t) {
+    const bs_acsr_term& T = terms[t];
+    if (T.slope != 1 || T.row_begin > 0 || T.row_end < L->nbr) return BS_OK;
+    if ((int64_t)T.count > 2 * (hi - lo + 1)) return BS_OK;  // beyond any row: leave it to the tables
+    for (int64_t k = 0; k < T.count; ++k) {
+      const int64_t v = (int64_t)T.offset + (int64_t)T.stride * k;
+      if (v >= lo && v <= hi) d.push_back((int32_t)v);
+    }
+  }
+  std::sort(d.begin(), d.end());
+  d.erase(std::unique(d.begin(), d.end()), d.end());
+  if (d.empty()) return BS_OK;
+  int32_t* dev = nullptr;
+  if (hipMalloc(&dev, d.size() * sizeof(int32_t)) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(BS_ERR_OOM, "hipMalloc of the ACSR offsets failed");
+  }
+  hipError_t e = hipMemcpy(dev, d.data(), d.size() * sizeof(int32_t), hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(dev);
+    return bsa::hip_fail(e, "hipMemcpy(ACSR offsets)");
+  }
+  L->band_off = dev;
+  L->band_n = (int)d.size();
+  return BS_OK;
+}
+
 int bs_layout_build_acsr(const bs_acsr_term* terms, int n_terms, int H, int nbr, int nbc, int block, void* stream,
                          bs_layout_t* out) {
   if (!out) return fail(BS_ERR_INVALID_ARG, "out is NULL");
@@ -179,6 +220,10 @@ int bs_layout_build_acsr(const bs_acsr_term* terms, int n_terms, int H, int nbr,
     L->block = block;
     (void)hipGetDevice(&L->device);
     rc = finish_build(L, lay, s, out);  // synchronises s before returning
+    if (rc == BS_OK && (rc = analyse_band(*out, terms, n_terms)) != BS_OK) {
+      bs_layout_free(*out);
+      *out = nullptr;
+    }
   } else {
     (void)hipStreamSynchronize(s);
   }
@@ -220,6 +265,7 @@ void bs_layout_free(bs_layout_t L) {
   if (!L) return;
   if (L->col_idx) (void)hipFree(L->col_idx);  // start of the nnz allocation
   if (L->mem) (void)hipFree(L->mem);
+  if (L->band_off) (void)hipFree(L->band_off);
   delete L;
 }
 

@@ -108,8 +108,8 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_rowblock(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, const int32_t* __restrict__ row_order,
     const typename Elem<E>::storage* __restrict__ Q, const typename Elem<E>::storage* __restrict__ K,
     const typename Elem<E>::storage* __restrict__ V, typename Elem<E>::storage* __restrict__ O,
-    float* __restrict__ S, const int32_t* __restrict__ blk_id, int Z, int H, int nbr, int nbc, int64_t nnz,
-    float c) {
+    float* __restrict__ S, const int32_t* __restrict__ blk_id, const int32_t* __restrict__ band, int band_n, int Z,
+    int H, int nbr, int nbc, int64_t nnz, float c) {
   using St = typename Elem<E>::storage;
   using Vec = typename Cfg<E>::Vec;
   constexpr bool BF = std::is_same<E, bf16_t>::value;
@@ -156,7 +156,29 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_rowblock(
   const int hr = row_order[blockIdx.x / Z];
   const int z = blockIdx.x % Z;
   const int h = hr / nbr, r = hr % nbr;
-  const int k0 = row_ptr[hr], k1 = row_ptr[hr + 1];
+  // The row's blocks: positions k0..k1-1 of the column table, or, for a
+  // slope-1 ACSR layout (band != null, attention only), columns r + band[i]
+  // for the offsets that keep the column on the grid (found by two binary
+  // searches in the sorted offsets; same ascending order as the table)
+  int k0, k1, boff = 0;
+  if (band != nullptr) {
+    auto first_at_least = [&](int v) {
+      int lo = 0, hi = band_n;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (band[mid] < v) lo = mid + 1;
+        else hi = mid;
+      }
+      return lo;
+    };
+    boff = first_at_least(-(hr % nbr));
+    k0 = 0;
+    k1 = first_at_least(nbc - (hr % nbr)) - boff;
+  } else {
+    k0 = row_ptr[hr];
+    k1 = row_ptr[hr + 1];
+  }
+  auto col_of = [&](int kk) { return band != nullptr ? hr % nbr + band[boff + kk] : col_idx[kk]; };
   const int64_t zh = (int64_t)z * H + h;
   const int64_t Nq = (int64_t)nbr * BLK, Nk = (int64_t)nbc * BLK;
   const int q_lo = r * BLK + wave * 16;  // first query row of this wave
@@ -236,12 +258,12 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_rowblock(
   const int nsteps = (k1 - k0 + NS - 1) / NS;
   if (k0 + sg < k1) {
     if constexpr (SPLIT) {
-      stage_load_to(stg, Kz, col_idx[k0 + sg]);
+      stage_load_to(stg, Kz, col_of(k0 + sg));
       stage_store_from(stg, Kg, koff);
-      stage_load_to(stg, Vz, col_idx[k0 + sg]);
+      stage_load_to(stg, Vz, col_of(k0 + sg));
       stage_store_from(stg, Vg, voff);
     } else {
-      load_next(col_idx[k0 + sg]);
+      load_next(col_of(k0 + sg));
     }
   }
   if constexpr (SPLIT) __syncthreads();
@@ -249,7 +271,7 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_rowblock(
     const int kk = k0 + step * NS + sg;
     const bool valid = kk < k1;
     const bool has_next = kk + NS < k1;
-    const int cb_next = has_next ? col_idx[kk + NS] : 0;
+    const int cb_next = has_next ? col_of(kk + NS) : 0;
     if constexpr (!SPLIT) {
       __syncthreads();  // every wave is done with the previous blocks in LDS
       if (valid) store_next();
@@ -258,7 +280,7 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_rowblock(
     } else {
       if (has_next) stage_load_to(stg, Kz, cb_next);
     }
-    const int cb = valid ? col_idx[kk] : 0;
+    const int cb = valid ? col_of(kk) : 0;
     // blocks whose every key is after every query of this wave add nothing
     const bool compute = valid && !(ATTN && CAUSAL && cb * BLK > q_lo + 15);
     const bool mask_block = ATTN && CAUSAL && (cb * BLK + BLK - 1 > q_lo);
@@ -540,6 +562,7 @@ struct Args {
   int Z;
   float c;
   bool causal;
+  bool use_band = false;  // attention on a slope-1 ACSR layout: computed columns
 };
 
 template <typename E, int BLK, int D, int NS, int MODE>
@@ -553,13 +576,18 @@ int launch_ns(const bs_layout* L, const Args& a, hipStream_t s) {
   const int32_t* order = T ? L->col_order : L->row_order;
   const int32_t* bid = T ? L->blk_id : nullptr;
   const int nb_out = T ? L->nbc : L->nbr, nb_in = T ? L->nbr : L->nbc;
+  // the fused kernel computes slope-1 ACSR columns (the other modes index S by
+  // the table position, so they keep the table)
+  const int32_t* band = (MODE == MODE_ATTN && a.use_band) ? L->band_off : nullptr;
+  const int band_n = band ? L->band_n : 0;
   if (MODE == MODE_ATTN && a.causal)
     hipLaunchKernelGGL((k_rowblock<E, BLK, D, true, NS, MODE>), grid, block, 0, s, ptr, idx, order, (const St*)a.Q,
-                       (const St*)a.K, (const St*)a.V, (St*)a.O, a.S, bid, a.Z, L->H, nb_out, nb_in, L->nnz, a.c);
+                       (const St*)a.K, (const St*)a.V, (St*)a.O, a.S, bid, band, band_n, a.Z, L->H, nb_out, nb_in,
+                       L->nnz, a.c);
   else
     hipLaunchKernelGGL((k_rowblock<E, BLK, D, false, NS, MODE>), grid, block, 0, s, ptr, idx, order,
-                       (const St*)a.Q, (const St*)a.K, (const St*)a.V, (St*)a.O, a.S, bid, a.Z, L->H, nb_out, nb_in,
-                       L->nnz, a.c);
+                       (const St*)a.Q, (const St*)a.K, (const St*)a.V, (St*)a.O, a.S, bid, band, band_n, a.Z, L->H,
+                       nb_out, nb_in, L->nnz, a.c);
   BSA_HIP(hipGetLastError());
   return BS_OK;
 }
@@ -616,7 +644,8 @@ int launch_attention(const bs_layout* L, const void* Q, const void* K, const voi
     const int rc = launch_attention_bf16_wide(L, Q, K, V, O, Z, d, scale, causal, s);
     if (rc != kNotApplicable) return rc;
   }
-  const Args a{Q, K, V, O, nullptr, Z, scale * kLog2e, causal};
+  Args a{Q, K, V, O, nullptr, Z, scale * kLog2e, causal};
+  a.use_band = L->band_off != nullptr;
   return run_mode<MODE_ATTN>(L, a, d, dt, s);
 }
 

@@ -29,6 +29,11 @@ struct bs_layout {
   // the same orders grouped by head: head h's rows at h*nbr.., longest first
   int32_t* row_order_h = nullptr;  // [H*nbr]
   int32_t* col_order_h = nullptr;  // [H*nbc]
+  // ACSR layouts whose terms all have slope 1 and cover every row: row r
+  // holds the columns r + d for d in this sorted offset set, clipped to the
+  // grid (own allocation; null otherwise)
+  int32_t* band_off = nullptr;
+  int band_n = 0;
 };
 
 // Workgroup -> work unit for kernels that walk a head's rows (or columns)
