@@ -61,7 +61,7 @@ def _source_hash(files):
     return h.hexdigest()[:16]
 
 
-ATTN_SOURCES = ["block_sparse_matmul_amd/csrc/attention.hip", "block_sparse_matmul_amd/csrc/attention_bf16.hip",
+ATTN_SOURCES = ["block_sparse_matmul_amd/csrc/attention.hip", "block_sparse_matmul_amd/csrc/attention_wide.hip",
                 "block_sparse_matmul_amd/csrc/tile.h", "block_sparse_matmul_amd/csrc/internal.h"]
 
 

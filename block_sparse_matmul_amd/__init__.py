@@ -25,7 +25,7 @@ from typing import Dict, Optional, Sequence, Tuple
 import numpy as np
 
 from . import _lib
-from ._lib import AcsrTerm, BsError, BS_BF16, BS_CAUSAL, BS_F32, check, lib
+from ._lib import AcsrTerm, BsError, BS_BF16, BS_CAUSAL, BS_F16, BS_F32, check, lib
 
 __all__ = ["Layout", "sdd", "softmax", "dsd", "dds", "attention", "softmax_backward", "dsd_t",
            "attention_backward", "attention_autograd", "BsError", "lib"]
@@ -47,7 +47,9 @@ def _dtype_code(t) -> int:
         return BS_F32
     if t.dtype == torch.bfloat16:
         return BS_BF16
-    raise TypeError(f"dense operands must be float32 or bfloat16, got {t.dtype}")
+    if t.dtype == torch.float16:
+        return BS_F16
+    raise TypeError(f"dense operands must be float32, bfloat16 or float16, got {t.dtype}")
 
 
 def _check_dense(name, t, ndim=4):

@@ -21,6 +21,7 @@ BS_ERR_OOM = -6
 BS_ERR_NO_DEVICE = -7
 BS_F32 = 0
 BS_BF16 = 1
+BS_F16 = 2
 BS_CAUSAL = 1
 
 # every symbol the header declares, with (restype, argtypes)

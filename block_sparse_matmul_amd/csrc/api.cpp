@@ -71,7 +71,8 @@ int check_grid(const bs_layout* L, int Z) {
 }
 
 int check_dtype(bs_dtype dt) {
-  if (dt != BS_F32 && dt != BS_BF16) return fail(BS_ERR_INVALID_ARG, "dtype must be BS_F32 or BS_BF16");
+  if (dt != BS_F32 && dt != BS_BF16 && dt != BS_F16)
+    return fail(BS_ERR_INVALID_ARG, "dtype must be BS_F32, BS_BF16 or BS_F16");
   return BS_OK;
 }
 

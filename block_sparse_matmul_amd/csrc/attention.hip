@@ -20,15 +20,15 @@
 // chosen by measuring the operand read patterns on gfx950; every operand
 // read below is free of bank conflicts.
 //
-// Per 64-key sub-step and wave, with 16x16 MFMA tiles (fp32 16x16x4, bf16
-// 16x16x32):
+// Per 64-key sub-step and wave, with 16x16 MFMA tiles (fp32 16x16x4; bf16
+// and fp16, the 16-bit types, 16x16x32):
 //   S^T = K_c Q^T     A = K rows from LDS, B = the wave's Q rows (registers,
 //                     loaded once). In the accumulator every lane then owns
 //                     ONE query row (its column) and 4 keys per 16-key tile,
 //                     so row max / sum are in-lane plus one butterfly over
 //                     the 4 lane groups.
 //   softmax           log2 domain (scale*log2(e) folded into Q for fp32, into
-//                     one fma for bf16); causal mask only on blocks that
+//                     one fma for 16-bit types); causal mask only on blocks that
 //                     reach the diagonal; raw v_exp_f32. The reference max
 //                     moves only when a block's max exceeds it by more than
 //                     TAU (so p <= 2^TAU): numerator and denominator share it,
@@ -38,15 +38,15 @@
 //                     transpose); O^T also keeps one query row per lane, so
 //                     the rescale is a per-lane scalar. fp32 takes one V
 //                     element per lane and instruction (one 4-byte LDS read);
-//                     bf16 takes 8 keys of one column per lane from two
+//                     16-bit types take 8 keys of one column per lane from two
 //                     ds_read_b64_tr_b16 (each 16-lane group reads a 4-key x
 //                     16-column patch and every lane receives the 4 keys of
 //                     its own column), so V never needs a transposed copy.
 // The S^T register layout is also the layout of a row-major b x b block read
 // with one 16-byte load per lane (row li, columns 16 jt + 4 g ..), which is
 // how the SDD stores its scores and the DSD loads its P.
-// bf16: P is rounded to bf16 (RNE) for P.V and the row sum l adds up those
-// rounded values (so the weights applied to V sum to one); O is rounded once
+// 16-bit types: P is rounded to the operand type (RNE) for P.V and the row
+// sum l adds up those rounded values (so the weights applied to V sum to one); O is rounded once
 // at the end.
 #include <math.h>
 
@@ -76,22 +76,26 @@ struct Cfg<float> {
   static constexpr int KC = 16;   // contraction values per 16-byte lane vector group (4 groups x 4)
   typedef f32x4 Vec;
 };
-template <>
-struct Cfg<bf16_t> {
+template <typename E>
+struct Cfg16 {
   static constexpr int VEC = 8;
   static constexpr int KC = 32;
-  typedef bf16x8 Vec;
+  typedef typename H16<E>::V8 Vec;
 };
+template <>
+struct Cfg<bf16_t> : Cfg16<bf16_t> {};
+template <>
+struct Cfg<f16_t> : Cfg16<f16_t> {};
 
 // padded LDS row strides (elements), measured free of bank conflicts for the
 // operand reads of the kernel: K rows 32 mod 256 bytes; V rows 16 mod 64
-// bytes (fp32, one 4-byte read per lane) or 32 mod 256 bytes (bf16,
+// bytes (fp32, one 4-byte read per lane) or 32 mod 256 bytes (16-bit types,
 // transposing 8-byte reads)
 template <typename E, int BLK, int D, int MODE>
 struct Lds {
   using St = typename Elem<E>::storage;
   static constexpr int KSTR = D + 32 / (int)sizeof(St);
-  static constexpr int VSTR = std::is_same<E, bf16_t>::value ? D + 16 : D + 4;
+  static constexpr int VSTR = std::is_same<E, float>::value ? D + 4 : D + 16;
   static constexpr int KBUF = (MODE == MODE_DSD || MODE == MODE_DSDT) ? 0 : BLK * KSTR;  // per key group
   static constexpr int VBUF = MODE == MODE_SDD ? 0 : BLK * VSTR;
   static constexpr size_t STAGE = (size_t)(KBUF + VBUF) * sizeof(St);  // bytes per key group
@@ -112,7 +116,7 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_rowblock(
     int H, int nbr, int nbc, int64_t nnz, float c) {
   using St = typename Elem<E>::storage;
   using Vec = typename Cfg<E>::Vec;
-  constexpr bool BF = std::is_same<E, bf16_t>::value;
+  constexpr bool BF = !std::is_same<E, float>::value;  // a 16-bit element type (bf16, fp16)
   constexpr bool ATTN = MODE == MODE_ATTN;
   constexpr bool DSDT = MODE == MODE_DSDT;
   constexpr bool HASK = MODE != MODE_DSD && !DSDT;  // score product (Q, K staged)
@@ -189,7 +193,7 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_rowblock(
   const int64_t s_lane = (int64_t)(wave * 16 + li) * BLK + 4 * g;
 
   // ---- Q as B fragments; attention folds scale*log2(e) in (fp32) or only
-  // its sign (bf16, exact); the SDD uses Q as is
+  // its sign (16-bit types, exact); the SDD uses Q as is
   Vec qf[HASK ? NQ : 1];
   float cs = 1.f;
   if constexpr (HASK) {
@@ -202,7 +206,7 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_rowblock(
 #pragma unroll
         for (int u = 0; u < NQ; ++u)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) qf[u][e] = to_bf16((float)qf[u][e] * sgn);
+          for (int e = 0; e < 8; ++e) qf[u][e] = H16<E>::cvt((float)qf[u][e] * sgn);
       }
       cs = (c == 0.f) ? 1.f : fabsf(c);
     } else if constexpr (ATTN) {
@@ -308,7 +312,7 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_rowblock(
 #pragma unroll
             for (int u = 0; u < NQ; ++u) {
               const Vec a = *reinterpret_cast<const Vec*>(kbase + 16 * jt * KSTR + u * KC);
-              s[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[u], s[jt], 0, 0, 0);
+              s[jt] = H16<E>::mfma16(a, qf[u], s[jt]);
             }
           }
         } else {
@@ -403,7 +407,7 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_rowblock(
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) s[jt][rr] = fast_exp2(fmaf(s[jt][rr], cs, -m_sub));
         if constexpr (!BF) {
-          // bf16 sums the rounded P below, two values per instruction
+          // 16-bit types sum the rounded P below, two values per instruction
           float ls = 0.f;
 #pragma unroll
           for (int jt = 0; jt < NJT; ++jt)
@@ -420,40 +424,43 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_rowblock(
         const u16* vb = &Vg[(kofs + 4 * g + (li >> 2)) * VSTR + 4 * (li & 3)];
         // attention: the row sum l adds up P as rounded for the product (the
         // weights that multiply V), two per v_dot2 against (1, 1)
+        using HT = H16<E>;
+        using V8 = typename HT::V8;
+        using V4 = typename HT::V4;
         float ls = 0.f;
-        const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
-        auto sum_p = [&](const bf16x8& pb) {
+        const typename HT::V2 ones = {HT::cvt(1.f), HT::cvt(1.f)};
+        auto sum_p = [&](const V8& pb) {
           if constexpr (ATTN) {
 #pragma unroll
-            for (int e = 0; e < 8; e += 2) ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[e], pb[e + 1]}, ones, ls, false);
+            for (int e = 0; e < 8; e += 2) ls = HT::dot2(typename HT::V2{pb[e], pb[e + 1]}, ones, ls);
           }
         };
         if constexpr (NJT >= 2) {
-          // operands read right before use: the bf16 kernel is register bound
-          // (two 8-wave workgroups per CU need <= 128 VGPRs)
+          // operands read right before use: the 16-bit kernel is register
+          // bound (two 8-wave workgroups per CU need <= 128 VGPRs)
 #pragma unroll
           for (int jp = 0; jp < NJT / 2; ++jp) {
-            const bf16x8 pb = {to_bf16(s[2 * jp][0]),     to_bf16(s[2 * jp][1]),     to_bf16(s[2 * jp][2]),
-                               to_bf16(s[2 * jp][3]),     to_bf16(s[2 * jp + 1][0]), to_bf16(s[2 * jp + 1][1]),
-                               to_bf16(s[2 * jp + 1][2]), to_bf16(s[2 * jp + 1][3])};
+            const V8 pb = {HT::cvt(s[2 * jp][0]),     HT::cvt(s[2 * jp][1]),     HT::cvt(s[2 * jp][2]),
+                           HT::cvt(s[2 * jp][3]),     HT::cvt(s[2 * jp + 1][0]), HT::cvt(s[2 * jp + 1][1]),
+                           HT::cvt(s[2 * jp + 1][2]), HT::cvt(s[2 * jp + 1][3])};
             sum_p(pb);
 #pragma unroll
             for (int nt = 0; nt < NNT; ++nt) {
-              const bf16x4 a0 = lds_read_tr16(vb + (32 * jp) * VSTR + nt * 16);
-              const bf16x4 a1 = lds_read_tr16(vb + (32 * jp + 16) * VSTR + nt * 16);
-              const bf16x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-              o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[nt], 0, 0, 0);
+              const V4 a0 = lds_read_tr16_as<V4>(vb + (32 * jp) * VSTR + nt * 16);
+              const V4 a1 = lds_read_tr16_as<V4>(vb + (32 * jp + 16) * VSTR + nt * 16);
+              const V8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+              o[nt] = HT::mfma16(a, pb, o[nt]);
             }
           }
         } else {  // a single 16-key tile: the other half of the k range is zero
-          const __bf16 zb = (__bf16)0.f;
-          const bf16x8 pb = {to_bf16(s[0][0]), to_bf16(s[0][1]), to_bf16(s[0][2]), to_bf16(s[0][3]), zb, zb, zb, zb};
+          const typename HT::T zb = HT::cvt(0.f);
+          const V8 pb = {HT::cvt(s[0][0]), HT::cvt(s[0][1]), HT::cvt(s[0][2]), HT::cvt(s[0][3]), zb, zb, zb, zb};
           sum_p(pb);
 #pragma unroll
           for (int nt = 0; nt < NNT; ++nt) {
-            const bf16x4 a0 = lds_read_tr16(vb + nt * 16);
-            const bf16x8 a = {a0[0], a0[1], a0[2], a0[3], zb, zb, zb, zb};
-            o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[nt], 0, 0, 0);
+            const V4 a0 = lds_read_tr16_as<V4>(vb + nt * 16);
+            const V8 a = {a0[0], a0[1], a0[2], a0[3], zb, zb, zb, zb};
+            o[nt] = HT::mfma16(a, pb, o[nt]);
           }
         }
         if constexpr (ATTN) l_run += ls;
@@ -545,8 +552,9 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_rowblock(
 #pragma unroll
   for (int nt = 0; nt < NNT; ++nt) {
     if constexpr (BF) {
-      *reinterpret_cast<bf16x4*>(po + nt * 16) =
-          bf16x4{to_bf16(o[nt][0] * inv), to_bf16(o[nt][1] * inv), to_bf16(o[nt][2] * inv), to_bf16(o[nt][3] * inv)};
+      using HT = H16<E>;
+      *reinterpret_cast<typename HT::V4*>(po + nt * 16) = typename HT::V4{
+          HT::cvt(o[nt][0] * inv), HT::cvt(o[nt][1] * inv), HT::cvt(o[nt][2] * inv), HT::cvt(o[nt][3] * inv)};
     } else {
       *reinterpret_cast<f32x4*>(po + nt * 16) = o[nt] * inv;
     }
@@ -633,6 +641,7 @@ int run_b(const bs_layout* L, const Args& a, hipStream_t s) {
 template <int MODE>
 int run_mode(const bs_layout* L, const Args& a, int d, bs_dtype dt, hipStream_t s) {
   if (dt == BS_BF16) return d == 64 ? run_b<bf16_t, 64, MODE>(L, a, s) : run_b<bf16_t, 128, MODE>(L, a, s);
+  if (dt == BS_F16) return d == 64 ? run_b<f16_t, 64, MODE>(L, a, s) : run_b<f16_t, 128, MODE>(L, a, s);
   return d == 64 ? run_b<float, 64, MODE>(L, a, s) : run_b<float, 128, MODE>(L, a, s);
 }
 
@@ -640,8 +649,8 @@ int run_mode(const bs_layout* L, const Args& a, int d, bs_dtype dt, hipStream_t 
 
 int launch_attention(const bs_layout* L, const void* Q, const void* K, const void* V, void* O, int Z, int d,
                      float scale, bool causal, bs_dtype dt, hipStream_t s) {
-  if (dt == BS_BF16) {
-    const int rc = launch_attention_bf16_wide(L, Q, K, V, O, Z, d, scale, causal, s);
+  if (dt != BS_F32) {
+    const int rc = launch_attention_wide(L, Q, K, V, O, Z, d, scale, causal, dt, s);
     if (rc != kNotApplicable) return rc;
   }
   Args a{Q, K, V, O, nullptr, Z, scale * kLog2e, causal};

@@ -1,12 +1,13 @@
-// Fused block-sparse attention, bf16, blocks of 32 to 128: the same
-// computation as the row-block kernel (SDD -> block-sparse softmax -> DSD of
-// Triton issue 117, "question on blocksparse", with the streaming softmax of
-// the Triton tutorial, Puzzles 8 and 9), laid out for the bf16 matrix cores.
+// Fused block-sparse attention, 16-bit operands (bf16 or fp16), blocks of
+// 32 to 128: the same computation as the row-block kernel (SDD ->
+// block-sparse softmax -> DSD of Triton issue 117, "question on
+// blocksparse", with the streaming softmax of the Triton tutorial, Puzzles 8
+// and 9), laid out for the 16-bit matrix cores.
 //
 // What differs from the row-block kernel:
 //  * each wave owns 32 query rows (two 16-row tiles), so every K or V
 //    operand read from LDS feeds two MFMAs: half the LDS read traffic per
-//    flop, which is what bounds the 16-row layout in bf16;
+//    flop, which is what bounds the 16-row layout with 16-bit operands;
 //  * blocks are staged with LDS DMA (global_load_lds_dwordx4: every lane
 //    moves 16 bytes from its own global address into consecutive LDS
 //    slots), so staging needs no registers and no LDS store instructions.
@@ -19,11 +20,11 @@
 //    the top of the step (hidden by the first score product), K of the next
 //    block as soon as every wave is past its last score product.
 //
-// Per 64-key sub-step and wave (16x16x32 bf16 MFMA tiles, as in the
+// Per 64-key sub-step and wave (16x16x32 bf16 / fp16 MFMA tiles, as in the
 // row-block kernel): S^T = K Q^T for both query tiles from one K read;
 // softmax in the log2 domain with lazy rescale; O^T += V^T P^T for both
 // tiles from one pair of transposing V reads. The row sum adds up P as
-// rounded to bf16 for the product (v_dot2 against (1, 1)).
+// rounded to the operand type for the product (v_dot2 against (1, 1)).
 #include <math.h>
 
 #include "internal.h"
@@ -70,12 +71,16 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wait_vmcnt0() { wait_vmcnt<0>(); }
 
-template <int BLK, int D, bool CAUSAL, int NS>
-__global__ __launch_bounds__(BLK * 2 * NS) void k_attn_bf16(
+template <typename E, int BLK, int D, bool CAUSAL, int NS>
+__global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, const int32_t* __restrict__ row_order,
     const int32_t* __restrict__ row_order_h, const u16* __restrict__ Q, const u16* __restrict__ K,
     const u16* __restrict__ V, u16* __restrict__ O, int Z, int H, int nbr, int nbc, float c, int grouped) {
   using Cfg = WideCfg<BLK, D>;
+  using HT = H16<E>;
+  using V8 = typename HT::V8;
+  using V4 = typename HT::V4;
+  using V2 = typename HT::V2;
   constexpr int NW = Cfg::NW, NT = 64 * NW;
   constexpr int NQ = D / 32;         // Q fragments per lane and tile
   constexpr int CPR = D / 8;         // 16-byte chunks per row
@@ -127,8 +132,8 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_bf16(
   const u16* Vz = V + zh * Nk * D;
 
   // ---- Q of both tiles as B fragments (8 values of one row per lane);
-  // only the sign of scale*log2(e) is folded in (exact in bf16)
-  bf16x8 qf[2][NQ];
+  // only the sign of scale*log2(e) is folded in (exact in 16 bits)
+  V8 qf[2][NQ];
   const float sgn = c > 0.f ? 1.f : (c < 0.f ? -1.f : 0.f);
   const float cs = (c == 0.f) ? 1.f : fabsf(c);
 #pragma unroll
@@ -136,10 +141,10 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_bf16(
     const u16* pq = Q + (zh * Nq + q_lo + 16 * t + li) * D + g * 8;
 #pragma unroll
     for (int u = 0; u < NQ; ++u) {
-      qf[t][u] = *reinterpret_cast<const bf16x8*>(pq + u * 32);
+      qf[t][u] = *reinterpret_cast<const V8*>(pq + u * 32);
       if (sgn != 1.f) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qf[t][u][e] = to_bf16((float)qf[t][u][e] * sgn);
+        for (int e = 0; e < 8; ++e) qf[t][u][e] = HT::cvt((float)qf[t][u][e] * sgn);
       }
     }
   }
@@ -189,7 +194,7 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_bf16(
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int nt = 0; nt < NNT; ++nt) o[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+  const V2 ones = {HT::cvt(1.f), HT::cvt(1.f)};
 
   // Transfers and barriers. With one sub-step: [A] K of the block has
   // landed -> barrier -> fetch V; score product; softmax; [B] V has landed
@@ -249,23 +254,23 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_bf16(
       // ---- S^T = K Q^T for both tiles
       if (compute) {
         // the K operands of tile jt+1 are read while tile jt is multiplied
-        bf16x8 ka[2][NQ];
+        V8 ka[2][NQ];
 #pragma unroll
-        for (int u = 0; u < NQ; ++u) ka[0][u] = *reinterpret_cast<const bf16x8*>(Kc + koff[u]);
+        for (int u = 0; u < NQ; ++u) ka[0][u] = *reinterpret_cast<const V8*>(Kc + koff[u]);
 #pragma unroll
         for (int jt = 0; jt < NJT; ++jt) {
           if (jt + 1 < NJT) {
 #pragma unroll
             for (int u = 0; u < NQ; ++u)
-              ka[(jt + 1) & 1][u] = *reinterpret_cast<const bf16x8*>(Kc + 16 * (jt + 1) * RB + koff[u]);
+              ka[(jt + 1) & 1][u] = *reinterpret_cast<const V8*>(Kc + 16 * (jt + 1) * RB + koff[u]);
           }
           __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the products
           s[0][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
           s[1][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int u = 0; u < NQ; ++u) {
-            s[0][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[jt & 1][u], qf[0][u], s[0][jt], 0, 0, 0);
-            s[1][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[jt & 1][u], qf[1][u], s[1][jt], 0, 0, 0);
+            s[0][jt] = HT::mfma16(ka[jt & 1][u], qf[0][u], s[0][jt]);
+            s[1][jt] = HT::mfma16(ka[jt & 1][u], qf[1][u], s[1][jt]);
           }
         }
       }
@@ -328,32 +333,32 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_bf16(
       // ---- O^T += V^T P^T for both tiles from one pair of V reads
 #pragma unroll
       for (int jp = 0; jp < NJT / 2; ++jp) {
-        bf16x8 pb[2];
+        V8 pb[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          pb[t] = bf16x8{to_bf16(s[t][2 * jp][0]),     to_bf16(s[t][2 * jp][1]),     to_bf16(s[t][2 * jp][2]),
-                         to_bf16(s[t][2 * jp][3]),     to_bf16(s[t][2 * jp + 1][0]), to_bf16(s[t][2 * jp + 1][1]),
-                         to_bf16(s[t][2 * jp + 1][2]), to_bf16(s[t][2 * jp + 1][3])};
+          pb[t] = V8{HT::cvt(s[t][2 * jp][0]),     HT::cvt(s[t][2 * jp][1]),     HT::cvt(s[t][2 * jp][2]),
+                     HT::cvt(s[t][2 * jp][3]),     HT::cvt(s[t][2 * jp + 1][0]), HT::cvt(s[t][2 * jp + 1][1]),
+                     HT::cvt(s[t][2 * jp + 1][2]), HT::cvt(s[t][2 * jp + 1][3])};
 #pragma unroll
           for (int e = 0; e < 8; e += 2)
-            l_run[t] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[t][e], pb[t][e + 1]}, ones, l_run[t], false);
+            l_run[t] = HT::dot2(V2{pb[t][e], pb[t][e + 1]}, ones, l_run[t]);
         }
         // every V operand of the 32 keys is requested before the first
         // product, so the reads stream behind the MFMAs
         const unsigned char* vb = Vp[sub] + 32 * jp * RB;
-        bf16x4 va0[NNT], va1[NNT];
+        V4 va0[NNT], va1[NNT];
 #pragma unroll
         for (int nt = 0; nt < NNT; ++nt) {
-          va0[nt] = lds_read_tr16(reinterpret_cast<const u16*>(vb + voff[nt]));
-          va1[nt] = lds_read_tr16(reinterpret_cast<const u16*>(vb + 16 * RB + voff[nt]));
+          va0[nt] = lds_read_tr16_as<V4>(reinterpret_cast<const u16*>(vb + voff[nt]));
+          va1[nt] = lds_read_tr16_as<V4>(reinterpret_cast<const u16*>(vb + 16 * RB + voff[nt]));
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int nt = 0; nt < NNT; ++nt) {
-          const bf16x8 a = {va0[nt][0], va0[nt][1], va0[nt][2], va0[nt][3],
+          const V8 a = {va0[nt][0], va0[nt][1], va0[nt][2], va0[nt][3],
                             va1[nt][0], va1[nt][1], va1[nt][2], va1[nt][3]};
-          o[0][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[0], o[0][nt], 0, 0, 0);
-          o[1][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[1], o[1][nt], 0, 0, 0);
+          o[0][nt] = HT::mfma16(a, pb[0], o[0][nt]);
+          o[1][nt] = HT::mfma16(a, pb[1], o[1][nt]);
         }
       }
     }  // sub-step
@@ -404,12 +409,12 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_bf16(
     u16* po = O + (zh * Nq + q_lo + 16 * t + li) * D + 4 * g;
 #pragma unroll
     for (int nt = 0; nt < NNT; ++nt)
-      *reinterpret_cast<bf16x4*>(po + nt * 16) = bf16x4{to_bf16(o[t][nt][0] * inv), to_bf16(o[t][nt][1] * inv),
-                                                        to_bf16(o[t][nt][2] * inv), to_bf16(o[t][nt][3] * inv)};
+      *reinterpret_cast<V4*>(po + nt * 16) =
+          V4{HT::cvt(o[t][nt][0] * inv), HT::cvt(o[t][nt][1] * inv), HT::cvt(o[t][nt][2] * inv), HT::cvt(o[t][nt][3] * inv)};
   }
 }
 
-template <int BLK, int D, int NS>
+template <typename E, int BLK, int D, int NS>
 int launch_ns(const bs_layout* L, const void* Q, const void* K, const void* V, void* O, int Z, float c, bool causal,
               hipStream_t s) {
   const dim3 grid(L->H * L->nbr * Z), block(BLK * 2 * NS);
@@ -419,11 +424,11 @@ int launch_ns(const bs_layout* L, const void* Q, const void* K, const void* V, v
   const double per_slot = (double)Z * (double)L->nnz / (2.0 * L->num_cus);
   const int grouped = (4.0 * L->max_row_len / NS <= per_slot) ? 1 : 0;
   if (causal)
-    hipLaunchKernelGGL((k_attn_bf16<BLK, D, true, NS>), grid, block, 0, s, L->row_ptr, L->col_idx, L->row_order,
+    hipLaunchKernelGGL((k_attn_wide<E, BLK, D, true, NS>), grid, block, 0, s, L->row_ptr, L->col_idx, L->row_order,
                        L->row_order_h, (const u16*)Q, (const u16*)K, (const u16*)V, (u16*)O, Z, L->H, L->nbr, L->nbc,
                        c, grouped);
   else
-    hipLaunchKernelGGL((k_attn_bf16<BLK, D, false, NS>), grid, block, 0, s, L->row_ptr, L->col_idx, L->row_order,
+    hipLaunchKernelGGL((k_attn_wide<E, BLK, D, false, NS>), grid, block, 0, s, L->row_ptr, L->col_idx, L->row_order,
                        L->row_order_h, (const u16*)Q, (const u16*)K, (const u16*)V, (u16*)O, Z, L->H, L->nbr, L->nbc,
                        c, grouped);
   BSA_HIP(hipGetLastError());
@@ -433,7 +438,7 @@ int launch_ns(const bs_layout* L, const void* Q, const void* K, const void* V, v
 // Key groups per workgroup: split a row's blocks over NS groups once the
 // longest row alone (about two workgroups share a CU) outlasts a CU's share
 // of the job.
-template <int BLK, int D>
+template <typename E, int BLK, int D>
 int run(const bs_layout* L, const void* Q, const void* K, const void* V, void* O, int Z, float c, bool causal,
         hipStream_t s) {
   using Cfg = WideCfg<BLK, D>;
@@ -445,32 +450,37 @@ int run(const bs_layout* L, const void* Q, const void* K, const void* V, void* O
   int ns = 1;
   while (ns < max_ns && 2.0 * L->max_row_len / ns > per_cu) ns *= 2;
   if constexpr (max_ns >= 4) {
-    if (ns >= 4) return launch_ns<BLK, D, 4>(L, Q, K, V, O, Z, c, causal, s);
+    if (ns >= 4) return launch_ns<E, BLK, D, 4>(L, Q, K, V, O, Z, c, causal, s);
   }
   if constexpr (max_ns >= 2) {
-    if (ns >= 2) return launch_ns<BLK, D, 2>(L, Q, K, V, O, Z, c, causal, s);
+    if (ns >= 2) return launch_ns<E, BLK, D, 2>(L, Q, K, V, O, Z, c, causal, s);
   }
-  return launch_ns<BLK, D, 1>(L, Q, K, V, O, Z, c, causal, s);
+  return launch_ns<E, BLK, D, 1>(L, Q, K, V, O, Z, c, causal, s);
 }
 
-template <int D>
+template <typename E, int D>
 int run_b(const bs_layout* L, const void* Q, const void* K, const void* V, void* O, int Z, float c, bool causal,
           hipStream_t s) {
   switch (L->block) {
-    case 32: return run<32, D>(L, Q, K, V, O, Z, c, causal, s);
-    case 64: return run<64, D>(L, Q, K, V, O, Z, c, causal, s);
-    case 128: return run<128, D>(L, Q, K, V, O, Z, c, causal, s);
+    case 32: return run<E, 32, D>(L, Q, K, V, O, Z, c, causal, s);
+    case 64: return run<E, 64, D>(L, Q, K, V, O, Z, c, causal, s);
+    case 128: return run<E, 128, D>(L, Q, K, V, O, Z, c, causal, s);
   }
   return kNotApplicable;
 }
 
 }  // namespace
 
-int launch_attention_bf16_wide(const bs_layout* L, const void* Q, const void* K, const void* V, void* O, int Z, int d,
-                               float scale, bool causal, hipStream_t s) {
+int launch_attention_wide(const bs_layout* L, const void* Q, const void* K, const void* V, void* O, int Z, int d,
+                          float scale, bool causal, bs_dtype dt, hipStream_t s) {
   const float c = scale * kLog2eB;
-  if (d == 64) return run_b<64>(L, Q, K, V, O, Z, c, causal, s);
-  if (d == 128) return run_b<128>(L, Q, K, V, O, Z, c, causal, s);
+  if (dt == BS_BF16) {
+    if (d == 64) return run_b<bf16_t, 64>(L, Q, K, V, O, Z, c, causal, s);
+    if (d == 128) return run_b<bf16_t, 128>(L, Q, K, V, O, Z, c, causal, s);
+  } else if (dt == BS_F16) {
+    if (d == 64) return run_b<f16_t, 64>(L, Q, K, V, O, Z, c, causal, s);
+    if (d == 128) return run_b<f16_t, 128>(L, Q, K, V, O, Z, c, causal, s);
+  }
   return kNotApplicable;
 }
 

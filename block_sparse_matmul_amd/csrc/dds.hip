@@ -12,19 +12,20 @@
 // walked in slabs of 64 rows (128 for 16 x 16 blocks, so one slab can span
 // several blocks and a step always carries enough work to hide its two
 // barriers): a slab is staged into LDS row-major (16-byte loads and stores,
-// bf16 rounded on the way) and the next slab and its A fragments are already
+// 16-bit types rounded on the way) and the next slab and its A fragments are already
 // in flight while the current one is multiplied.
 //
 // The contraction runs over the rows of S, which is the strided direction
 // of a row-major block; so S is the MFMA A operand, read from LDS one
 // column element per lane (fp32: one 4-byte read, rows padded to 16 mod 64
-// bytes; bf16: two ds_read_b64_tr_b16, each 16-lane group reading a
+// bytes; 16-bit types: two ds_read_b64_tr_b16, each 16-lane group reading a
 // 4-row x 16-column patch so that every lane receives 4 rows of its own
 // column), and A is the B operand, straight from global memory as 16-byte
-// (fp32) or 8-byte (bf16) row vectors. With 16x16 tiles
+// (fp32) or 8-byte (bf16, fp16) row vectors. With 16x16 tiles
 //   C^T[j][m] += S^T[j][r] A^T[r][m]
 // every lane ends up with 4 consecutive output columns of one row m, which
-// it stores as one vector. bf16: S rounded to bf16 (RNE) for the product, C
+// it stores as one vector. 16-bit types: S rounded to the operand type (RNE)
+// for the product, C
 // from the fp32 accumulator. Columns with no stored block are written as
 // zeros.
 #include <type_traits>
@@ -45,11 +46,15 @@ template <>
 struct Row4<bf16_t> {
   typedef bf16x4 type;
 };
+template <>
+struct Row4<f16_t> {
+  typedef f16x4 type;
+};
 
 template <typename E, int BLK>
 struct DdsLds {
   using St = typename Elem<E>::storage;
-  static constexpr bool BF = std::is_same<E, bf16_t>::value;
+  static constexpr bool BF = !std::is_same<E, float>::value;  // a 16-bit element type
   // contraction rows per step: the column's stored blocks are walked as one
   // long contraction (block after block), 64 rows at a time (128 for 16 x
   // 16 blocks)
@@ -151,8 +156,9 @@ __global__ __launch_bounds__(256 * NS) void k_dds(const int32_t* __restrict__ co
     for (int i = 0; i < KCH; ++i) {
       if (q0 + __builtin_amdgcn_readfirstlane(srow[i]) >= total_rows) continue;
       if constexpr (BF) {
-        *reinterpret_cast<bf16x4*>(&Sg[loff[i]]) =
-            bf16x4{to_bf16(sreg[i][0]), to_bf16(sreg[i][1]), to_bf16(sreg[i][2]), to_bf16(sreg[i][3])};
+        using HT = H16<E>;
+        *reinterpret_cast<typename HT::V4*>(&Sg[loff[i]]) = typename HT::V4{
+            HT::cvt(sreg[i][0]), HT::cvt(sreg[i][1]), HT::cvt(sreg[i][2]), HT::cvt(sreg[i][3])};
       } else {
         *reinterpret_cast<f32x4*>(&Sg[loff[i]]) = sreg[i];
       }
@@ -183,20 +189,23 @@ __global__ __launch_bounds__(256 * NS) void k_dds(const int32_t* __restrict__ co
     if constexpr (BF) {
       // lane (g, 4k + q) points at row 4g + k, columns 4q.. of an n-tile and
       // receives rows 4g + 0..3 of column li
+      using HT = H16<E>;
+      using V8 = typename HT::V8;
+      using V4 = typename HT::V4;
       const u16* sb = &Sg[(4 * g + (li >> 2)) * SSTR + 4 * (li & 3)];
-      const __bf16 zb = (__bf16)0.f;
-      const bf16x4 z4 = {zb, zb, zb, zb};
+      const typename HT::T zb = HT::cvt(0.f);
+      const V4 z4 = {zb, zb, zb, zb};
       // tiles 2jp and 2jp+1 in one 32-deep product; a lone last tile is
       // padded with zeros
       auto pair_step = [&](int jp, bool full) {
-        const bf16x4 b1 = full ? acur[2 * jp + 1] : z4;
-        const bf16x8 b = {acur[2 * jp][0], acur[2 * jp][1], acur[2 * jp][2], acur[2 * jp][3], b1[0], b1[1], b1[2], b1[3]};
+        const V4 b1 = full ? acur[2 * jp + 1] : z4;
+        const V8 b = {acur[2 * jp][0], acur[2 * jp][1], acur[2 * jp][2], acur[2 * jp][3], b1[0], b1[1], b1[2], b1[3]};
 #pragma unroll
         for (int nt = 0; nt < NNT; ++nt) {
-          const bf16x4 a0 = lds_read_tr16(sb + (32 * jp) * SSTR + nt * 16);
-          const bf16x4 a1 = full ? lds_read_tr16(sb + (32 * jp + 16) * SSTR + nt * 16) : z4;
-          const bf16x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-          o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, o[nt], 0, 0, 0);
+          const V4 a0 = lds_read_tr16_as<V4>(sb + (32 * jp) * SSTR + nt * 16);
+          const V4 a1 = full ? lds_read_tr16_as<V4>(sb + (32 * jp + 16) * SSTR + nt * 16) : z4;
+          const V8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+          o[nt] = HT::mfma16(a, b, o[nt]);
         }
       };
 #pragma unroll
@@ -262,8 +271,9 @@ __global__ __launch_bounds__(256 * NS) void k_dds(const int32_t* __restrict__ co
 #pragma unroll
   for (int nt = 0; nt < NNT; ++nt) {
     if constexpr (BF) {
-      *reinterpret_cast<bf16x4*>(pc + nt * 16) =
-          bf16x4{to_bf16(o[nt][0]), to_bf16(o[nt][1]), to_bf16(o[nt][2]), to_bf16(o[nt][3])};
+      using HT = H16<E>;
+      *reinterpret_cast<typename HT::V4*>(pc + nt * 16) =
+          typename HT::V4{HT::cvt(o[nt][0]), HT::cvt(o[nt][1]), HT::cvt(o[nt][2]), HT::cvt(o[nt][3])};
     } else {
       *reinterpret_cast<f32x4*>(pc + nt * 16) = o[nt];
     }
@@ -315,7 +325,9 @@ int run_e(const bs_layout* L, const void* A, const float* S, void* C, int Z, int
 int launch_dds(const bs_layout* L, const void* A, const float* S, void* C, int Z, int M, bs_dtype dt,
                hipStream_t s) {
   if ((M + 63) / 64 > 65535) return fail(BS_ERR_SHAPE, "M must be at most 65535*64 for the DDS");
-  return dt == BS_BF16 ? run_e<bf16_t>(L, A, S, C, Z, M, s) : run_e<float>(L, A, S, C, Z, M, s);
+  if (dt == BS_BF16) return run_e<bf16_t>(L, A, S, C, Z, M, s);
+  if (dt == BS_F16) return run_e<f16_t>(L, A, S, C, Z, M, s);
+  return run_e<float>(L, A, S, C, Z, M, s);
 }
 
 }  // namespace bsa

@@ -10,8 +10,8 @@
 // tile accumulates over every stored block of the row and over its columns.
 // P is read as 16-byte row vectors; the dense operand is read down its
 // columns (T consecutive elements of one row per k value, coalesced across
-// lanes). bf16: P is rounded to bf16 for the product, C from the fp32
-// accumulator. Rows with no stored block are written as zeros.
+// lanes). 16-bit types: P is rounded to the operand type for the product,
+// C from the fp32 accumulator. Rows with no stored block are written as zeros.
 #include "internal.h"
 #include "tile.h"
 
@@ -34,24 +34,29 @@ struct PFrag<float> {
     return f;
   }
 };
-template <>
-struct PFrag<bf16_t> {
-  // eight fp32 values rounded to bf16
-  static __device__ __forceinline__ Frag<bf16_t> load(const float* p) {
+template <typename E>
+struct PFrag16 {
+  using HT = H16<E>;
+  // eight fp32 values rounded to the 16-bit type
+  static __device__ __forceinline__ Frag<E> load(const float* p) {
     const f32x4 a = *reinterpret_cast<const f32x4*>(p);
     const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
-    Frag<bf16_t> f;
-    f.v = bf16x8{to_bf16(a[0]), to_bf16(a[1]), to_bf16(a[2]), to_bf16(a[3]),
-                 to_bf16(b[0]), to_bf16(b[1]), to_bf16(b[2]), to_bf16(b[3])};
+    Frag<E> f;
+    f.v = typename HT::V8{HT::cvt(a[0]), HT::cvt(a[1]), HT::cvt(a[2]), HT::cvt(a[3]),
+                          HT::cvt(b[0]), HT::cvt(b[1]), HT::cvt(b[2]), HT::cvt(b[3])};
     return f;
   }
-  static __device__ __forceinline__ Frag<bf16_t> column(const u16* p, int64_t stride) {
-    Frag<bf16_t> f;
+  static __device__ __forceinline__ Frag<E> column(const u16* p, int64_t stride) {
+    Frag<E> f;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) f.v[q] = __builtin_bit_cast(__bf16, p[q * stride]);
+    for (int q = 0; q < 8; ++q) f.v[q] = __builtin_bit_cast(typename HT::T, p[q * stride]);
     return f;
   }
 };
+template <>
+struct PFrag<bf16_t> : PFrag16<bf16_t> {};
+template <>
+struct PFrag<f16_t> : PFrag16<f16_t> {};
 
 template <typename E, int BLK, int T>
 __global__ __launch_bounds__(256) void k_dsd(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
@@ -94,7 +99,7 @@ __global__ __launch_bounds__(256) void k_dsd(const int32_t* __restrict__ row_ptr
     }
     St* pc = C + (zh * nbr * BLK + (int64_t)r * BLK + ti * T) * Nd + tn * T + li;
 #pragma unroll
-    for (int q = 0; q < NR; ++q) store_elem(pc + (int64_t)acc_row<T>(q, g) * Nd, acc[q]);
+    for (int q = 0; q < NR; ++q) store_elem<E>(pc + (int64_t)acc_row<T>(q, g) * Nd, acc[q]);
   }
 }
 
@@ -130,7 +135,9 @@ int launch_dsd(const bs_layout* L, const float* P, const void* B, void* C, int Z
                hipStream_t s) {
   const int rc = launch_dsd_rowblock(L, P, B, C, Z, Nd, dt, s);
   if (rc != kNotApplicable) return rc;
-  return dt == BS_BF16 ? run_e<bf16_t>(L, P, B, C, Z, Nd, s) : run_e<float>(L, P, B, C, Z, Nd, s);
+  if (dt == BS_BF16) return run_e<bf16_t>(L, P, B, C, Z, Nd, s);
+  if (dt == BS_F16) return run_e<f16_t>(L, P, B, C, Z, Nd, s);
+  return run_e<float>(L, P, B, C, Z, Nd, s);
 }
 
 }  // namespace bsa

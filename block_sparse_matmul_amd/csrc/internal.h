@@ -91,10 +91,11 @@ int launch_sdd_rowblock(const bs_layout* L, const void* A, const void* B,
 int launch_dsd_rowblock(const bs_layout* L, const float* P, const void* B,
                         void* C, int Z, int Nd, bs_dtype dt, hipStream_t s);
 
-// bf16 fused attention on the 32-rows-per-wave kernel (blocks of 32, 64,
-// 128); returns kNotApplicable for other blocks or head sizes.
-int launch_attention_bf16_wide(const bs_layout* L, const void* Q, const void* K, const void* V, void* O, int Z,
-                               int d, float scale, bool causal, hipStream_t s);
+// 16-bit (bf16, fp16) fused attention on the 32-rows-per-wave kernel
+// (blocks of 32, 64, 128); returns kNotApplicable for other blocks, head
+// sizes or types.
+int launch_attention_wide(const bs_layout* L, const void* Q, const void* K, const void* V, void* O, int Z, int d,
+                          float scale, bool causal, bs_dtype dt, hipStream_t s);
 
 bool log_enabled();
 

@@ -88,7 +88,9 @@ int launch_sdd(const bs_layout* L, const void* A, const void* B, float* S, int Z
                hipStream_t s) {
   const int rc = launch_sdd_rowblock(L, A, B, S, Z, K, dt, s);
   if (rc != kNotApplicable) return rc;
-  return dt == BS_BF16 ? run_e<bf16_t>(L, A, B, S, Z, K, s) : run_e<float>(L, A, B, S, Z, K, s);
+  if (dt == BS_BF16) return run_e<bf16_t>(L, A, B, S, Z, K, s);
+  if (dt == BS_F16) return run_e<f16_t>(L, A, B, S, Z, K, s);
+  return run_e<float>(L, A, B, S, Z, K, s);
 }
 
 }  // namespace bsa

@@ -48,8 +48,11 @@ extern "C" {
 typedef struct bs_layout* bs_layout_t;
 
 /* element type of the dense operands (block-sparse tensors are always
-   float32) */
-typedef enum { BS_F32 = 0, BS_BF16 = 1 } bs_dtype;
+   float32): IEEE binary32, bfloat16 or IEEE binary16. With the 16-bit types
+   the products run on the 16-bit matrix cores with float32 accumulation;
+   float32 values that feed a product (P, S) are rounded to the operand type
+   (round to nearest even) and results are rounded once at the end. */
+typedef enum { BS_F32 = 0, BS_BF16 = 1, BS_F16 = 2 } bs_dtype;
 
 /* flags for bs_softmax / bs_attention */
 enum { BS_CAUSAL = 1 };
@@ -129,8 +132,9 @@ int bs_softmax(bs_layout_t L, const float* S, float* P, int Z, float scale,
 /* DSD: C[z,h,r-block,:] = sum over stored (h,r,c) of P[z,k] . B[z,h,c-block,:]
    (the issue's second mode; in attention O = P V).
    P: float32 [Z][nnz][b][b]; B: [Z][H][nbc*b][Nd], C: [Z][H][nbr*b][Nd] of
-   dtype dt (bf16: P is rounded to bf16 for the product, C is rounded from
-   the float32 accumulator). Rows with no stored block are written as zero.
+   dtype dt (16-bit types: P is rounded to dt for the product, C is rounded
+   from the float32 accumulator). Rows with no stored block are written as
+   zero.
    Nd > 0 and a multiple of 16. */
 int bs_dsd(bs_layout_t L, const float* P, const void* B, void* C, int Z,
            int Nd, bs_dtype dt, void* stream);
@@ -148,9 +152,9 @@ int bs_dds(bs_layout_t L, const void* A, const float* S, void* C, int Z,
    kernel (the issue's attention composition) with a streaming row softmax
    (running max and sum, Triton tutorial Puzzles 8 and 9); P never leaves
    the chip. Q: [Z][H][nbr*b][d], K, V: [Z][H][nbc*b][d], O: [Z][H][nbr*b][d],
-   all of dtype dt; d in {64, 128}. bf16: scores and softmax in float32, P
-   rounded to bf16 for the P.V product, O rounded from float32. Rows with
-   no visible key are zero. */
+   all of dtype dt; d in {64, 128}. 16-bit types: scores and softmax in
+   float32, P rounded to dt for the P.V product, O rounded from float32.
+   Rows with no visible key are zero. */
 int bs_attention(bs_layout_t L, const void* Q, const void* K, const void* V,
                  void* O, int Z, int d, float scale, int flags, bs_dtype dt,
                  void* stream);
@@ -175,8 +179,8 @@ int bs_softmax_backward(bs_layout_t L, const float* P, const float* dP,
    C[z,h,c-block,:] = sum over stored (h,r,c) of S[z,k]^T . B[z,h,r-block,:]
    (in attention's backward dK = dS^T Q and dV = P^T dO).
    S: float32 [Z][nnz][b][b]; B: [Z][H][nbr*b][Nd], C: [Z][H][nbc*b][Nd] of
-   dtype dt (bf16: S is rounded to bf16 for the product, C is rounded from
-   the float32 accumulator). Block columns with no stored block are written
+   dtype dt (16-bit types: S is rounded to dt for the product, C is rounded
+   from the float32 accumulator). Block columns with no stored block are written
    as zero. Nd in {64, 128}. */
 int bs_dsd_t(bs_layout_t L, const float* S, const void* B, void* C, int Z,
              int Nd, bs_dtype dt, void* stream);
