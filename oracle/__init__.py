@@ -28,10 +28,16 @@ design notes):
     each block row-major, in that order.
   * SDD computes A @ B^T on the blocks (attention's Q K^T); DSD computes
     S @ B; DDS computes A @ S.
-  * softmax applies ``scale`` to the raw SDD values, then the mask (causal:
-    -inf where the global key index exceeds the global query index), then a
-    row softmax over every stored entry of the row. A row with no visible
-    entry gives zeros.
+  * softmax applies ``scale`` to the raw SDD values, adds the optional dense
+    additive masks (below), then the causal mask (-inf where the global key
+    index exceeds the global query index), then a row softmax over every
+    stored entry of the row. A row with no visible entry gives zeros.
+  * dense masks ("you can also pass dense masks", question on blocksparse;
+    the page gives no format): attn_mask, float [Nq, Nk] over the global
+    query and key indices, shared by every batch element and head, and
+    kp_mask (key padding), float [Z, Nk] per batch element and key; both
+    are added to scale * S. -inf hides an entry. Entries outside the
+    layout's blocks stay hidden whatever the masks hold.
 """
 from __future__ import annotations
 
@@ -151,6 +157,22 @@ def element_mask(layout, block: int, causal: bool) -> np.ndarray:
     return m
 
 
+def _bias(attn_mask, kp_mask, z: int, qi, kj) -> np.ndarray:
+    """The additive dense masks at global query rows qi and key columns kj of
+    batch element z: attn_mask[qi, kj] + kp_mask[z, kj] (0 for a mask that
+    is None). Masks are float64 arrays here."""
+    out = np.zeros((len(qi), len(kj)))
+    if attn_mask is not None:
+        out = out + attn_mask[np.ix_(qi, kj)]
+    if kp_mask is not None:
+        out = out + kp_mask[z, kj][None, :]
+    return out
+
+
+def _masks(attn_mask, kp_mask):
+    return (None if attn_mask is None else _f64(attn_mask)), (None if kp_mask is None else _f64(kp_mask))
+
+
 # ---------------------------------------------------------------------------
 # the three matmul modes and the block-sparse softmax
 # ---------------------------------------------------------------------------
@@ -175,16 +197,19 @@ def sdd(A, B, layout, block: int) -> np.ndarray:
     return S
 
 
-def softmax(S, layout, block: int, scale: float, causal: bool = False) -> np.ndarray:
+def softmax(S, layout, block: int, scale: float, causal: bool = False, attn_mask=None,
+            kp_mask=None) -> np.ndarray:
     """Block-sparse row softmax of SDD output (question on blocksparse: it
     reduces the rows of the SDD output and equals full-attention softmax).
 
     For query row i of block row r of head h, the row holds the entries of
-    every stored block (h, r, c). x = scale*S, masked to -inf where causal
-    hides the key, then P = exp(x - max) / sum exp(x - max); a row whose
-    entries are all hidden (or that stores no block) is all zeros.
+    every stored block (h, r, c). x = scale*S plus the dense masks, set to
+    -inf where causal hides the key, then P = exp(x - max) / sum exp(x -
+    max); a row whose entries are all hidden (or that stores no block) is
+    all zeros.
     """
     S = _f64(S)
+    am, kpm = _masks(attn_mask, kp_mask)
     lut = lut_from_layout(layout)
     lay = check_layout(layout)
     H, nbr, _ = lay.shape
@@ -197,8 +222,11 @@ def softmax(S, layout, block: int, scale: float, causal: bool = False) -> np.nda
         if not ks:
             continue
         cols = lut["col_idx"][ks]
+        qrows = r * b + np.arange(b)
+        kcols = np.concatenate([c * b + np.arange(b) for c in cols])
         for z in range(Z):
             x = np.concatenate([scale * S[z, k] for k in ks], axis=1)   # [b, len*b]
+            x = x + _bias(am, kpm, z, qrows, kcols)
             if causal:
                 qi = r * b + np.arange(b)[:, None]
                 kj = np.concatenate([c * b + np.arange(b) for c in cols])[None, :]
@@ -246,17 +274,21 @@ def dds(A, S, layout, block: int) -> np.ndarray:
 # attention: two independent routes
 # ---------------------------------------------------------------------------
 
-def attention_dense(Q, K, V, layout, block: int, scale: float, causal: bool = False) -> np.ndarray:
-    """Route (i): dense masked attention, O = softmax(scale Q K^T + M) V with
-    M = 0 where element_mask is True and -inf elsewhere; rows with no visible
-    key give zeros."""
+def attention_dense(Q, K, V, layout, block: int, scale: float, causal: bool = False, attn_mask=None,
+                    kp_mask=None) -> np.ndarray:
+    """Route (i): dense masked attention, O = softmax(scale Q K^T + B + M) V
+    with B the dense additive masks and M = 0 where element_mask is True and
+    -inf elsewhere; rows with no visible key give zeros."""
     Q, K, V = _f64(Q), _f64(K), _f64(V)
+    am, kpm = _masks(attn_mask, kp_mask)
     mask = element_mask(layout, block, causal)
     Z, H = Q.shape[:2]
     O = np.zeros_like(Q)
+    qall, kall = np.arange(Q.shape[2]), np.arange(K.shape[2])
     for z in range(Z):
         for h in range(H):
             x = scale * (Q[z, h] @ K[z, h].T)
+            x = x + _bias(am, kpm, z, qall, kall)
             x = np.where(mask[h], x, -np.inf)
             m = x.max(axis=1, keepdims=True)
             ok = np.isfinite(m)
@@ -267,10 +299,11 @@ def attention_dense(Q, K, V, layout, block: int, scale: float, causal: bool = Fa
     return O
 
 
-def attention_blocks(Q, K, V, layout, block: int, scale: float, causal: bool = False) -> np.ndarray:
+def attention_blocks(Q, K, V, layout, block: int, scale: float, causal: bool = False, attn_mask=None,
+                     kp_mask=None) -> np.ndarray:
     """Route (ii): the pages' composition, SDD -> block-sparse softmax -> DSD."""
     S = sdd(Q, K, layout, block)
-    P = softmax(S, layout, block, scale, causal)
+    P = softmax(S, layout, block, scale, causal, attn_mask, kp_mask)
     return dsd(P, V, layout, block)
 
 
@@ -306,11 +339,12 @@ def attention_blockrow(Q, K, V, layout, block: int, scale: float, causal: bool,
 
 
 def attention_rows(Q, K, V, layout, block: int, scale: float, causal: bool,
-                   rows: Iterable[Tuple[int, int, int]]) -> np.ndarray:
+                   rows: Iterable[Tuple[int, int, int]], attn_mask=None, kp_mask=None) -> np.ndarray:
     """Route (i) on selected block rows: for each (z, h, r), the b x d slice
     of dense masked attention, computed from the full key range of head h.
     Used to check large problems on sampled outputs."""
     Q, K, V = _f64(Q), _f64(K), _f64(V)
+    am, kpm = _masks(attn_mask, kp_mask)
     lay = check_layout(layout)
     b = block
     out = []
@@ -320,6 +354,7 @@ def attention_rows(Q, K, V, layout, block: int, scale: float, causal: bool,
             qi = r * b + np.arange(b)[:, None]
             mask = mask & (np.arange(mask.shape[1])[None, :] <= qi)
         x = scale * (Q[z, h, r * b:(r + 1) * b] @ K[z, h].T)
+        x = x + _bias(am, kpm, z, r * b + np.arange(b), np.arange(K.shape[2]))
         x = np.where(mask, x, -np.inf)
         m = x.max(axis=1, keepdims=True)
         ok = np.isfinite(m)
@@ -387,16 +422,21 @@ def dsd_t(S, B, layout, block: int) -> np.ndarray:
     return C
 
 
-def attention_backward_dense(Q, K, V, dO, layout, block: int, scale: float, causal: bool = False):
+def attention_backward_dense(Q, K, V, dO, layout, block: int, scale: float, causal: bool = False, attn_mask=None,
+                             kp_mask=None):
     """Route (i) of the gradient: dense matrices with the element mask.
-    Returns (dQ, dK, dV) for the forward of attention_dense."""
+    Returns (dQ, dK, dV) for the forward of attention_dense (the additive
+    masks are constants: they shape P and get no gradient)."""
     Q, K, V, dO = _f64(Q), _f64(K), _f64(V), _f64(dO)
+    am, kpm = _masks(attn_mask, kp_mask)
     mask = element_mask(layout, block, causal)
     Z, H = Q.shape[:2]
     dQ, dK, dV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
+    qall, kall = np.arange(Q.shape[2]), np.arange(K.shape[2])
     for z in range(Z):
         for h in range(H):
-            x = np.where(mask[h], scale * (Q[z, h] @ K[z, h].T), -np.inf)
+            x = scale * (Q[z, h] @ K[z, h].T) + _bias(am, kpm, z, qall, kall)
+            x = np.where(mask[h], x, -np.inf)
             m = x.max(axis=1, keepdims=True)
             e = np.where(np.isfinite(m), np.exp(x - np.where(np.isfinite(m), m, 0.0)), 0.0)
             s = e.sum(axis=1, keepdims=True)
@@ -409,11 +449,12 @@ def attention_backward_dense(Q, K, V, dO, layout, block: int, scale: float, caus
     return dQ, dK, dV
 
 
-def attention_backward_blocks(Q, K, V, dO, layout, block: int, scale: float, causal: bool = False):
+def attention_backward_blocks(Q, K, V, dO, layout, block: int, scale: float, causal: bool = False, attn_mask=None,
+                              kp_mask=None):
     """Route (ii) of the gradient, on the block-sparse operators: P by SDD
     and softmax (recomputed), dP = SDD(dO, V), dS = softmax_backward(P, dP),
     dQ = DSD(dS, K), dK = DSD^T(dS, Q), dV = DSD^T(P, dO)."""
-    P = softmax(sdd(Q, K, layout, block), layout, block, scale, causal)
+    P = softmax(sdd(Q, K, layout, block), layout, block, scale, causal, attn_mask, kp_mask)
     dS = softmax_backward(P, sdd(dO, V, layout, block), layout, block, scale)
     return dsd(dS, K, layout, block), dsd_t(dS, Q, layout, block), dsd_t(P, dO, layout, block)
 

@@ -68,6 +68,21 @@ MUTANTS = {
     "dense_backward_dv_untransposed": (
         "dV[z, h] = P.T @ dO[z, h]",
         "dV[z, h] = P @ dO[z, h]"),
+    "mask_attn_transposed": (
+        "out = out + attn_mask[np.ix_(qi, kj)]",
+        "out = out + attn_mask[np.ix_(kj, qi)].T"),
+    "mask_key_padding_on_queries": (
+        "out = out + kp_mask[z, kj][None, :]",
+        "out = out + kp_mask[z, qi][:, None]"),
+    "mask_key_padding_wrong_batch": (
+        "out = out + kp_mask[z, kj][None, :]",
+        "out = out + kp_mask[0, kj][None, :]"),
+    "softmax_dense_mask_dropped": (
+        "x = x + _bias(am, kpm, z, qrows, kcols)",
+        "x = x"),
+    "dense_backward_mask_dropped": (
+        "x = scale * (Q[z, h] @ K[z, h].T) + _bias(am, kpm, z, qall, kall)",
+        "x = scale * (Q[z, h] @ K[z, h].T)"),
     "rows_wrong_head_mask": (
         "mask = np.repeat(lay[h, r].astype(bool), b)[None, :].repeat(b, axis=0)",
         "mask = np.repeat(lay[0, r].astype(bool), b)[None, :].repeat(b, axis=0)"),
@@ -80,7 +95,8 @@ def _run_pins(mutant):
     cmd = [sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
            os.path.join(ROOT, "tests", "test_oracle_lut.py"),
            os.path.join(ROOT, "tests", "test_oracle_ops.py"),
-           os.path.join(ROOT, "tests", "test_oracle_backward.py")]
+           os.path.join(ROOT, "tests", "test_oracle_backward.py"),
+           os.path.join(ROOT, "tests", "test_oracle_masks.py")]
     return subprocess.run(cmd, cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
 
 
