@@ -174,15 +174,43 @@ def sdd(L: Layout, a, b, out=None):
     return out
 
 
-def softmax(L: Layout, s, scale: float, causal: bool = False, out=None, inplace: bool = False):
-    """Block-sparse row softmax of SDD output (scale, then causal mask)."""
+def _mask_ptrs(L: Layout, Z: int, device, attn_mask, key_padding_mask):
+    """Validated pointers of the optional dense additive masks: attn_mask
+    float32 [nbr*b, nbc*b] (shared by batch and heads), key_padding_mask
+    float32 [Z, nbc*b]; None for an absent mask."""
+    torch = _torch()
+    ptrs = []
+    for name, m, shape in (("attn_mask", attn_mask, (L.nbr * L.block, L.nbc * L.block)),
+                           ("key_padding_mask", key_padding_mask, (Z, L.nbc * L.block))):
+        if m is None:
+            ptrs.append(None)
+            continue
+        _check_dense(name, m, ndim=2)
+        if m.dtype != torch.float32 or tuple(m.shape) != shape:
+            raise ValueError(f"{name} must be float32 {list(shape)}")
+        if m.device != device:
+            raise ValueError(f"{name} must be on {device}")
+        ptrs.append(_ptr(m))
+    return ptrs
+
+
+def softmax(L: Layout, s, scale: float, causal: bool = False, out=None, inplace: bool = False, attn_mask=None,
+            key_padding_mask=None):
+    """Block-sparse row softmax of SDD output: scale, plus the optional dense
+    additive masks (attn_mask [nbr*b, nbc*b], key_padding_mask [Z, nbc*b],
+    float32, -inf hides), then the causal mask."""
     torch = _torch()
     _check_dense("s", s)
     if s.dtype != torch.float32 or s.shape[1:] != (L.nnz, L.block, L.block):
         raise ValueError("s must be float32 [Z, nnz, b, b]")
+    am, kp = _mask_ptrs(L, s.shape[0], s.device, attn_mask, key_padding_mask)
     out = s if inplace else _out(out, s.shape, torch.float32, s.device)
-    check(lib().bs_softmax(L.handle, _ptr(s), _ptr(out), s.shape[0], float(scale),
-                           BS_CAUSAL if causal else 0, _stream(s.device)))
+    flags = BS_CAUSAL if causal else 0
+    if am is None and kp is None:
+        check(lib().bs_softmax(L.handle, _ptr(s), _ptr(out), s.shape[0], float(scale), flags, _stream(s.device)))
+    else:
+        check(lib().bs_softmax_masked(L.handle, _ptr(s), _ptr(out), s.shape[0], float(scale), flags, am, kp,
+                                      _stream(s.device)))
     return out
 
 
@@ -216,8 +244,11 @@ def dds(L: Layout, a, s, out=None):
     return out
 
 
-def attention(L: Layout, q, k, v, scale: Optional[float] = None, causal: bool = False, out=None):
-    """Fused block-sparse attention O = softmax(scale q k^T + mask) v."""
+def attention(L: Layout, q, k, v, scale: Optional[float] = None, causal: bool = False, out=None, attn_mask=None,
+              key_padding_mask=None):
+    """Fused block-sparse attention O = softmax(scale q k^T + mask) v; the
+    mask is the layout's, the optional dense additive masks (see softmax)
+    and the causal one."""
     for n, t in (("q", q), ("k", k), ("v", v)):
         _check_dense(n, t)
     Z, H, Nq, d = q.shape
@@ -227,9 +258,15 @@ def attention(L: Layout, q, k, v, scale: Optional[float] = None, causal: bool = 
         raise ValueError("q must be [Z, H, nbr*b, d]; k, v [Z, H, nbc*b, d]")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    am, kp = _mask_ptrs(L, Z, q.device, attn_mask, key_padding_mask)
     out = _out(out, q.shape, q.dtype, q.device)
-    check(lib().bs_attention(L.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(out), Z, d, float(scale),
-                             BS_CAUSAL if causal else 0, _dtype_code(q), _stream(q.device)))
+    flags = BS_CAUSAL if causal else 0
+    if am is None and kp is None:
+        check(lib().bs_attention(L.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(out), Z, d, float(scale), flags,
+                                 _dtype_code(q), _stream(q.device)))
+    else:
+        check(lib().bs_attention_masked(L.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(out), Z, d, float(scale), flags,
+                                        am, kp, _dtype_code(q), _stream(q.device)))
     return out
 
 
@@ -266,10 +303,11 @@ def dsd_t(L: Layout, s, b, out=None):
 
 
 def attention_backward(L: Layout, q, k, v, do, scale: Optional[float] = None, causal: bool = False,
-                       workspace: Optional[Tuple] = None):
+                       workspace: Optional[Tuple] = None, attn_mask=None, key_padding_mask=None):
     """(dq, dk, dv) of attention() for the output gradient do, in one library
-    call: P recomputed by SDD and softmax, dP = SDD(do, v), dS = softmax
-    gradient, dq = DSD(dS, k), dk = DSD^T(dS, q), dv = DSD^T(P, do).
+    call: P recomputed by SDD and softmax (under the same dense masks),
+    dP = SDD(do, v), dS = softmax gradient, dq = DSD(dS, k),
+    dk = DSD^T(dS, q), dv = DSD^T(P, do).
     workspace: optional pair of float32 [Z, nnz, b, b] tensors."""
     torch = _torch()
     for n, t in (("q", q), ("k", k), ("v", v), ("do", do)):
@@ -286,10 +324,17 @@ def attention_backward(L: Layout, q, k, v, do, scale: Optional[float] = None, ca
     ws_s, ws_p = workspace if workspace is not None else (None, None)
     ws_s = _out(ws_s, ws_shape, torch.float32, q.device, "workspace")
     ws_p = _out(ws_p, ws_shape, torch.float32, q.device, "workspace")
+    am, kp = _mask_ptrs(L, Z, q.device, attn_mask, key_padding_mask)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    check(lib().bs_attention_backward(L.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
-                                      _ptr(ws_s), _ptr(ws_p), Z, d, float(scale), BS_CAUSAL if causal else 0,
-                                      _dtype_code(q), _stream(q.device)))
+    flags = BS_CAUSAL if causal else 0
+    if am is None and kp is None:
+        check(lib().bs_attention_backward(L.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), _ptr(dk),
+                                          _ptr(dv), _ptr(ws_s), _ptr(ws_p), Z, d, float(scale), flags,
+                                          _dtype_code(q), _stream(q.device)))
+    else:
+        check(lib().bs_attention_backward_masked(L.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq),
+                                                 _ptr(dk), _ptr(dv), _ptr(ws_s), _ptr(ws_p), Z, d, float(scale),
+                                                 flags, am, kp, _dtype_code(q), _stream(q.device)))
     return dq, dk, dv
 
 
@@ -306,25 +351,30 @@ def _autograd_fn():
 
         class BlockSparseAttention(torch.autograd.Function):
             @staticmethod
-            def forward(ctx, q, k, v, L, scale, causal):
+            def forward(ctx, q, k, v, L, scale, causal, attn_mask, key_padding_mask):
                 ctx.save_for_backward(q, k, v)
                 ctx.L, ctx.scale, ctx.causal = L, scale, causal
-                return attention(L, q, k, v, scale, causal)
+                ctx.masks = (attn_mask, key_padding_mask)
+                return attention(L, q, k, v, scale, causal, attn_mask=attn_mask, key_padding_mask=key_padding_mask)
 
             @staticmethod
             def backward(ctx, do):
                 q, k, v = ctx.saved_tensors
-                dq, dk, dv = attention_backward(ctx.L, q, k, v, do.contiguous(), ctx.scale, ctx.causal)
-                return dq, dk, dv, None, None, None
+                am, kp = ctx.masks
+                dq, dk, dv = attention_backward(ctx.L, q, k, v, do.contiguous(), ctx.scale, ctx.causal,
+                                                attn_mask=am, key_padding_mask=kp)
+                return dq, dk, dv, None, None, None, None, None
 
         _AUTOGRAD_FN = BlockSparseAttention
     return _AUTOGRAD_FN
 
 
-def attention_autograd(L: Layout, q, k, v, scale: Optional[float] = None, causal: bool = False):
+def attention_autograd(L: Layout, q, k, v, scale: Optional[float] = None, causal: bool = False, attn_mask=None,
+                       key_padding_mask=None):
     """attention() as a differentiable torch op (forward: the fused kernel;
-    backward: attention_backward)."""
+    backward: attention_backward). The dense masks are constants (no
+    gradient)."""
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
-    return _autograd_fn().apply(q, k, v, L, float(scale), bool(causal))
+    return _autograd_fn().apply(q, k, v, L, float(scale), bool(causal), attn_mask, key_padding_mask)
 

@@ -49,6 +49,10 @@ SIGNATURES = {
     "bs_softmax_backward": (_i, [_vp, _vp, _vp, _vp, _i, _f, _vp]),
     "bs_dsd_t": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _vp]),
     "bs_attention_backward": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _f, _i, _i, _vp]),
+    "bs_softmax_masked": (_i, [_vp, _vp, _vp, _i, _f, _i, _vp, _vp, _vp]),
+    "bs_attention_masked": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _f, _i, _vp, _vp, _i, _vp]),
+    "bs_attention_backward_masked": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _f, _i, _vp,
+                                          _vp, _i, _vp]),
     "bs_last_error": (C.c_char_p, []),
     "bs_version": (_i, []),
 }

@@ -70,6 +70,13 @@ int check_grid(const bs_layout* L, int Z) {
   return BS_OK;
 }
 
+// the dense masks are read as 16-byte vectors
+int check_masks(const float* attn_mask, const float* kp_mask) {
+  if ((reinterpret_cast<uintptr_t>(attn_mask) & 15) || (reinterpret_cast<uintptr_t>(kp_mask) & 15))
+    return fail(BS_ERR_INVALID_ARG, "mask pointers must be 16-byte aligned");
+  return BS_OK;
+}
+
 int check_dtype(bs_dtype dt) {
   if (dt != BS_F32 && dt != BS_BF16 && dt != BS_F16)
     return fail(BS_ERR_INVALID_ARG, "dtype must be BS_F32, BS_BF16 or BS_F16");
@@ -286,7 +293,13 @@ int bs_sdd(bs_layout_t L, const void* A, const void* B, float* S, int Z, int K, 
 }
 
 int bs_softmax(bs_layout_t L, const float* S, float* P, int Z, float scale, int flags, void* stream) {
+  return bs_softmax_masked(L, S, P, Z, scale, flags, nullptr, nullptr, stream);
+}
+
+int bs_softmax_masked(bs_layout_t L, const float* S, float* P, int Z, float scale, int flags, const float* attn_mask,
+                      const float* kp_mask, void* stream) {
   if (int rc = check_handle(L)) return rc;
+  if (int rc = check_masks(attn_mask, kp_mask)) return rc;
   if (flags & ~BS_CAUSAL) return fail(BS_ERR_INVALID_ARG, "unknown flag");
   if (Z < 0) return fail(BS_ERR_INVALID_ARG, "Z must be >= 0");
   const bool causal = flags & BS_CAUSAL;
@@ -297,7 +310,7 @@ int bs_softmax(bs_layout_t L, const float* S, float* P, int Z, float scale, int 
   if ((int64_t)L->H * L->nbr * L->block > std::numeric_limits<int32_t>::max() - 4)
     return fail(BS_ERR_SHAPE, "too many query rows");
   log_call("softmax", L, Z, flags);
-  return bsa::launch_softmax(L, S, P, Z, scale, causal, (hipStream_t)stream);
+  return bsa::launch_softmax(L, S, P, Z, scale, causal, attn_mask, kp_mask, (hipStream_t)stream);
 }
 
 int bs_dsd(bs_layout_t L, const float* P, const void* B, void* C, int Z, int Nd, bs_dtype dt, void* stream) {
@@ -347,7 +360,16 @@ int bs_dsd_t(bs_layout_t L, const float* S, const void* B, void* C, int Z, int N
 int bs_attention_backward(bs_layout_t L, const void* Q, const void* K, const void* V, const void* dO, void* dQ,
                           void* dK, void* dV, float* ws_s, float* ws_p, int Z, int d, float scale, int flags,
                           bs_dtype dt, void* stream) {
+  return bs_attention_backward_masked(L, Q, K, V, dO, dQ, dK, dV, ws_s, ws_p, Z, d, scale, flags, nullptr, nullptr,
+                                      dt, stream);
+}
+
+int bs_attention_backward_masked(bs_layout_t L, const void* Q, const void* K, const void* V, const void* dO,
+                                 void* dQ, void* dK, void* dV, float* ws_s, float* ws_p, int Z, int d, float scale,
+                                 int flags, const float* attn_mask, const float* kp_mask, bs_dtype dt,
+                                 void* stream) {
   if (int rc = check_handle(L)) return rc;
+  if (int rc = check_masks(attn_mask, kp_mask)) return rc;
   if (int rc = check_dtype(dt)) return rc;
   if (flags & ~BS_CAUSAL) return fail(BS_ERR_INVALID_ARG, "unknown flag");
   if (Z < 0) return fail(BS_ERR_INVALID_ARG, "Z must be >= 0");
@@ -368,7 +390,7 @@ int bs_attention_backward(bs_layout_t L, const void* Q, const void* K, const voi
   log_call("attention_backward", L, Z, d);
   hipStream_t s = (hipStream_t)stream;
   if (int rc = bsa::launch_sdd(L, Q, K, ws_s, Z, d, dt, s)) return rc;                  // S = Q K^T
-  if (int rc = bsa::launch_softmax(L, ws_s, ws_p, Z, scale, causal, s)) return rc;     // P
+  if (int rc = bsa::launch_softmax(L, ws_s, ws_p, Z, scale, causal, attn_mask, kp_mask, s)) return rc;  // P
   if (int rc = bsa::launch_sdd(L, dO, V, ws_s, Z, d, dt, s)) return rc;                 // dP = dO V^T
   if (int rc = bsa::launch_softmax_backward(L, ws_p, ws_s, ws_s, Z, scale, s)) return rc;  // dS
   if (int rc = bsa::launch_dsd(L, ws_s, K, dQ, Z, d, dt, s)) return rc;                 // dQ = dS K
@@ -394,7 +416,14 @@ int bs_dds(bs_layout_t L, const void* A, const float* S, void* C, int Z, int M, 
 
 int bs_attention(bs_layout_t L, const void* Q, const void* K, const void* V, void* O, int Z, int d, float scale,
                  int flags, bs_dtype dt, void* stream) {
+  return bs_attention_masked(L, Q, K, V, O, Z, d, scale, flags, nullptr, nullptr, dt, stream);
+}
+
+int bs_attention_masked(bs_layout_t L, const void* Q, const void* K, const void* V, void* O, int Z, int d,
+                        float scale, int flags, const float* attn_mask, const float* kp_mask, bs_dtype dt,
+                        void* stream) {
   if (int rc = check_handle(L)) return rc;
+  if (int rc = check_masks(attn_mask, kp_mask)) return rc;
   if (int rc = check_dtype(dt)) return rc;
   if (flags & ~BS_CAUSAL) return fail(BS_ERR_INVALID_ARG, "unknown flag");
   if (Z < 0) return fail(BS_ERR_INVALID_ARG, "Z must be >= 0");
@@ -406,7 +435,7 @@ int bs_attention(bs_layout_t L, const void* Q, const void* K, const void* V, voi
   if (!work) return BS_OK;
   if (int rc = check_grid(L, Z)) return rc;
   log_call("attention", L, Z, d);
-  return bsa::launch_attention(L, Q, K, V, O, Z, d, scale, causal, dt, (hipStream_t)stream);
+  return bsa::launch_attention(L, Q, K, V, O, Z, d, scale, causal, attn_mask, kp_mask, dt, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -309,7 +309,9 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
           const bool upd = m_blk > m_run[t] + kTauB;
           if (__builtin_amdgcn_ballot_w64(upd) != 0) {  // wave-uniform
             const float m_new = upd ? m_blk : m_run[t];
-            const float alpha = __builtin_amdgcn_exp2f(m_run[t] - m_new);  // 0 when m_run = -inf
+            // 1 for lanes that keep their max (no -inf - -inf); 0 when an
+            // update leaves m_run = -inf
+            const float alpha = upd ? __builtin_amdgcn_exp2f(m_run[t] - m_new) : 1.f;
             l_run[t] *= alpha;
 #pragma unroll
             for (int nt = 0; nt < NNT; ++nt) o[t][nt] *= alpha;

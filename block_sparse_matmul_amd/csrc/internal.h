@@ -66,21 +66,30 @@ int expand_acsr(const bs_acsr_term* terms_dev, int n_terms, int H, int nbr,
                 int nbc, uint8_t* layout_dev, hipStream_t s);
 
 // ---- operator launchers (one per translation unit) ----
+// am, kp: the optional dense additive masks of the softmax and the fused
+// attention (float32 [nbr*b][nbc*b] and [Z][nbc*b]; null when absent).
 int launch_sdd(const bs_layout* L, const void* A, const void* B, float* S,
                int Z, int K, bs_dtype dt, hipStream_t s);
 int launch_softmax(const bs_layout* L, const float* S, float* P, int Z,
-                   float scale, bool causal, hipStream_t s);
+                   float scale, bool causal, const float* am, const float* kp,
+                   hipStream_t s);
 int launch_dsd(const bs_layout* L, const float* P, const void* B, void* C,
                int Z, int Nd, bs_dtype dt, hipStream_t s);
 int launch_dds(const bs_layout* L, const void* A, const float* S, void* C,
                int Z, int M, bs_dtype dt, hipStream_t s);
 int launch_attention(const bs_layout* L, const void* Q, const void* K,
                      const void* V, void* O, int Z, int d, float scale,
-                     bool causal, bs_dtype dt, hipStream_t s);
+                     bool causal, const float* am, const float* kp, bs_dtype dt,
+                     hipStream_t s);
 int launch_softmax_backward(const bs_layout* L, const float* P, const float* dP, float* dS, int Z, float scale,
                             hipStream_t s);
 int launch_dsd_t(const bs_layout* L, const float* S, const void* B, void* C, int Z, int Nd, bs_dtype dt,
                  hipStream_t s);
+
+// launch_attention with at least one dense mask (attention_masked.hip)
+int launch_attention_masked(const bs_layout* L, const void* Q, const void* K, const void* V, void* O, int Z, int d,
+                            float scale, bool causal, const float* am, const float* kp, bs_dtype dt,
+                            hipStream_t s);
 
 // SDD and DSD on the fused kernel's row-block machinery (LDS-staged
 // operands); they apply when the contraction (SDD) or output width (DSD) is
@@ -92,8 +101,8 @@ int launch_dsd_rowblock(const bs_layout* L, const float* P, const void* B,
                         void* C, int Z, int Nd, bs_dtype dt, hipStream_t s);
 
 // 16-bit (bf16, fp16) fused attention on the 32-rows-per-wave kernel
-// (blocks of 32, 64, 128); returns kNotApplicable for other blocks, head
-// sizes or types.
+// (blocks of 32, 64, 128; no dense masks); returns kNotApplicable for other
+// blocks, head sizes or types.
 int launch_attention_wide(const bs_layout* L, const void* Q, const void* K, const void* V, void* O, int Z, int d,
                           float scale, bool causal, bs_dtype dt, hipStream_t s);
 

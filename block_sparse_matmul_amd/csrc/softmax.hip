@@ -4,10 +4,12 @@
 // diagonal blocks).
 //
 // For query row i of block row r: x = scale * S over the stored blocks of
-// the row (causal: -inf where key c*b+j > query r*b+i), P = exp(x - max) /
-// sum exp(x - max), zeros when nothing is visible. exp is evaluated as
-// exp2(x * log2(e)) on the hardware's base-2 exponential (the identity the
-// Triton tutorial's Puzzle 8 uses).
+// the row, plus the optional dense additive masks (the issue's dense masks:
+// am[query][key], shared by batch and heads, and kp[z][key]), causal: -inf
+// where key c*b+j > query r*b+i; P = exp(x - max) / sum exp(x - max), zeros
+// when nothing is visible. exp is evaluated as exp2(x * log2(e)) on the
+// hardware's base-2 exponential (the identity the Triton tutorial's Puzzle 8
+// uses), so the masks enter as log2(e) * mask.
 //
 // One wave per query row. The row's stored entries (len blocks x b floats,
 // b contiguous floats per block) are read as 16-byte vectors, 256 floats per
@@ -43,7 +45,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 template <int R, bool CAUSAL>
 __global__ __launch_bounds__(256) void k_softmax(const int32_t* __restrict__ row_ptr,
                                                  const int32_t* __restrict__ col_idx, const float* S, float* P,
-                                                 int rows, int nbr, int b, int64_t nnz, float c) {
+                                                 int rows, int nbr, int b, int64_t nnz, float c,
+                                                 const float* __restrict__ am, const float* __restrict__ kp,
+                                                 int64_t Nk) {
   const int lane = threadIdx.x & 63;
   const int qrow = blockIdx.x * 4 + (threadIdx.x >> 6);  // (h, r, i) flattened
   if (qrow >= rows * b) return;
@@ -65,12 +69,24 @@ __global__ __launch_bounds__(256) void k_softmax(const int32_t* __restrict__ row
     if (e < n) {
       x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + addr(e)));
       x *= c;
-      if (CAUSAL) {
+      if (CAUSAL || am != nullptr || kp != nullptr) {
         const int kl = e / b, j = e % b;
-        const int key = col_idx[k0 + kl] * b + j;
+        const int key = col_idx[k0 + kl] * b + j;  // 4 consecutive keys in one block
+        if (am != nullptr) {
+          const f32x4 mv = *reinterpret_cast<const f32x4*>(am + (int64_t)q_index * Nk + key);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (key + q > q_index) x[q] = NEG;
+          for (int q = 0; q < 4; ++q) x[q] = fmaf(mv[q], kLog2e, x[q]);
+        }
+        if (kp != nullptr) {
+          const f32x4 mv = *reinterpret_cast<const f32x4*>(kp + (int64_t)z * Nk + key);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) x[q] = fmaf(mv[q], kLog2e, x[q]);
+        }
+        if (CAUSAL) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (key + q > q_index) x[q] = NEG;
+        }
       }
     }
     return x;
@@ -132,15 +148,17 @@ __global__ __launch_bounds__(256) void k_softmax(const int32_t* __restrict__ row
 }
 
 template <int R>
-void launch_r(const bs_layout* L, const float* S, float* P, int Z, float c, bool causal, hipStream_t s) {
+void launch_r(const bs_layout* L, const float* S, float* P, int Z, float c, bool causal, const float* am,
+              const float* kp, hipStream_t s) {
   const int rows = L->H * L->nbr;
   const dim3 grid((unsigned)(((int64_t)rows * L->block + 3) / 4), Z);
+  const int64_t Nk = (int64_t)L->nbc * L->block;
   if (causal)
     hipLaunchKernelGGL((k_softmax<R, true>), grid, dim3(256), 0, s, L->row_ptr, L->col_idx, S, P, rows, L->nbr,
-                       L->block, L->nnz, c);
+                       L->block, L->nnz, c, am, kp, Nk);
   else
     hipLaunchKernelGGL((k_softmax<R, false>), grid, dim3(256), 0, s, L->row_ptr, L->col_idx, S, P, rows, L->nbr,
-                       L->block, L->nnz, c);
+                       L->block, L->nnz, c, am, kp, Nk);
 }
 
 // Gradient of the softmax above with respect to its input S, given P and
@@ -225,17 +243,18 @@ int launch_softmax_backward(const bs_layout* L, const float* P, const float* dP,
   return BS_OK;
 }
 
-int launch_softmax(const bs_layout* L, const float* S, float* P, int Z, float scale, bool causal, hipStream_t s) {
+int launch_softmax(const bs_layout* L, const float* S, float* P, int Z, float scale, bool causal, const float* am,
+                   const float* kp, hipStream_t s) {
   const int64_t longest = (int64_t)L->max_row_len * L->block;  // floats in the longest row
   const float c = scale * kLog2e;
   if (longest <= 4 * 256)
-    launch_r<4>(L, S, P, Z, c, causal, s);
+    launch_r<4>(L, S, P, Z, c, causal, am, kp, s);
   else if (longest <= 8 * 256)
-    launch_r<8>(L, S, P, Z, c, causal, s);
+    launch_r<8>(L, S, P, Z, c, causal, am, kp, s);
   else if (longest <= 16 * 256)
-    launch_r<16>(L, S, P, Z, c, causal, s);
+    launch_r<16>(L, S, P, Z, c, causal, am, kp, s);
   else
-    launch_r<32>(L, S, P, Z, c, causal, s);
+    launch_r<32>(L, S, P, Z, c, causal, am, kp, s);
   BSA_HIP(hipGetLastError());
   return BS_OK;
 }

@@ -129,6 +129,25 @@ int bs_sdd(bs_layout_t L, const void* A, const void* B, float* S, int Z,
 int bs_softmax(bs_layout_t L, const float* S, float* P, int Z, float scale,
                int flags, void* stream);
 
+/* ---- dense masks (question on blocksparse: dense masks may be passed
+   alongside the layout; the format is not given there, the one below is
+   this library's) ----
+   attn_mask: float32 [nbr*b][nbc*b], indexed by global query and key,
+     shared by every batch element and head; may be NULL.
+   kp_mask (key padding): float32 [Z][nbc*b], per batch element and key;
+     may be NULL.
+   Both are added to scale*S before the causal mask and the row softmax;
+   -inf hides an entry, a row with every entry hidden gives zeros. Entries
+   outside the layout's blocks stay hidden whatever the masks hold. +inf or
+   NaN in a mask gives NaN outputs. Both pointers must be 16-byte aligned
+   (BS_ERR_INVALID_ARG otherwise); the caller keeps ownership. With both
+   NULL each masked call is its unmasked counterpart. */
+
+/* bs_softmax with the dense masks above. */
+int bs_softmax_masked(bs_layout_t L, const float* S, float* P, int Z,
+                      float scale, int flags, const float* attn_mask,
+                      const float* kp_mask, void* stream);
+
 /* DSD: C[z,h,r-block,:] = sum over stored (h,r,c) of P[z,k] . B[z,h,c-block,:]
    (the issue's second mode; in attention O = P V).
    P: float32 [Z][nnz][b][b]; B: [Z][H][nbc*b][Nd], C: [Z][H][nbr*b][Nd] of
@@ -158,6 +177,13 @@ int bs_dds(bs_layout_t L, const void* A, const float* S, void* C, int Z,
 int bs_attention(bs_layout_t L, const void* Q, const void* K, const void* V,
                  void* O, int Z, int d, float scale, int flags, bs_dtype dt,
                  void* stream);
+
+/* bs_attention with the dense masks above (fused: the masks are read at the
+   stored blocks only). */
+int bs_attention_masked(bs_layout_t L, const void* Q, const void* K,
+                        const void* V, void* O, int Z, int d, float scale,
+                        int flags, const float* attn_mask,
+                        const float* kp_mask, bs_dtype dt, void* stream);
 
 /* ---- backward (the exact gradient of the forward above) ----
    The attention gradient is made of the same three modes (the issue's
@@ -195,6 +221,16 @@ int bs_attention_backward(bs_layout_t L, const void* Q, const void* K,
                           const void* V, const void* dO, void* dQ, void* dK,
                           void* dV, float* ws_s, float* ws_p, int Z, int d,
                           float scale, int flags, bs_dtype dt, void* stream);
+
+/* Backward of bs_attention_masked: as bs_attention_backward, with P
+   recomputed under the same dense masks (the masks are constants: they get
+   no gradient). */
+int bs_attention_backward_masked(bs_layout_t L, const void* Q, const void* K,
+                                 const void* V, const void* dO, void* dQ,
+                                 void* dK, void* dV, float* ws_s, float* ws_p,
+                                 int Z, int d, float scale, int flags,
+                                 const float* attn_mask, const float* kp_mask,
+                                 bs_dtype dt, void* stream);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* bs_last_error(void);
