@@ -62,7 +62,8 @@ def _source_hash(files):
 
 
 ATTN_SOURCES = ["block_sparse_matmul_amd/csrc/attention.hip", "block_sparse_matmul_amd/csrc/attention_wide.hip",
-                "block_sparse_matmul_amd/csrc/tile.h", "block_sparse_matmul_amd/csrc/internal.h"]
+                "block_sparse_matmul_amd/csrc/rowblock.h", "block_sparse_matmul_amd/csrc/tile.h",
+                "block_sparse_matmul_amd/csrc/internal.h"]
 
 
 def _traffic(workload, launches_flops):
