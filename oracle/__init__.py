@@ -48,7 +48,7 @@ import numpy as np
 __all__ = [
     "check_layout", "lut_from_layout", "layout_from_lut", "acsr_expand",
     "element_mask", "sdd", "softmax", "dsd", "dds",
-    "attention_dense", "attention_blocks", "attention_rows",
+    "attention_dense", "attention_blocks", "attention_rows", "attention_lse",
     "attention_blockrow", "nnz_flops_attention", "nnz_flops_dds",
     "softmax_backward", "dsd_t", "attention_backward_dense", "attention_backward_blocks",
 ]
@@ -297,6 +297,31 @@ def attention_dense(Q, K, V, layout, block: int, scale: float, causal: bool = Fa
             p = np.divide(e, s, out=np.zeros_like(e), where=s > 0)
             O[z, h] = p @ V[z, h]
     return O
+
+
+def attention_lse(Q, K, layout, block: int, scale: float, causal: bool = False, attn_mask=None,
+                  kp_mask=None) -> np.ndarray:
+    """Natural log of the softmax denominator of every query row,
+    log sum_j exp(x_ij) over the visible entries of x = scale Q K^T + B (the
+    dense masks), [Z, H, Nq]; -inf for a row with no visible key. With it,
+    P = exp(x - lse) on the visible entries (what a backward pass needs to
+    rebuild P without the row max and sum)."""
+    Q, K = _f64(Q), _f64(K)
+    am, kpm = _masks(attn_mask, kp_mask)
+    mask = element_mask(layout, block, causal)
+    Z, H = Q.shape[:2]
+    out = np.full(Q.shape[:3], -np.inf)
+    qall, kall = np.arange(Q.shape[2]), np.arange(K.shape[2])
+    for z in range(Z):
+        for h in range(H):
+            x = scale * (Q[z, h] @ K[z, h].T) + _bias(am, kpm, z, qall, kall)
+            x = np.where(mask[h], x, -np.inf)
+            m = x.max(axis=1)
+            ok = np.isfinite(m)
+            mm = np.where(ok, m, 0.0)
+            tot = np.exp(x - mm[:, None]).sum(axis=1)   # >= 1 where ok (the max term)
+            out[z, h] = np.where(ok, mm + np.log(np.where(ok, tot, 1.0)), -np.inf)
+    return out
 
 
 def attention_blocks(Q, K, V, layout, block: int, scale: float, causal: bool = False, attn_mask=None,

@@ -161,3 +161,39 @@ def test_masked_rows_route_equals_dense_route():
     got = oracle.attention_rows(Q, K, V, lay, b, 0.3, True, rows, am, kp)
     for n, (z, h, r) in enumerate(rows):
         assert np.abs(got[n] - dense[z, h, r * b:(r + 1) * b]).max() < 1e-12
+
+
+# ------------------------------------------------------------ row log-sum-exp
+
+def test_lse_all_ones_is_torch_logsumexp():
+    Z, H, nb, b, d = 2, 2, 3, 16, 8
+    N = nb * b
+    lay = np.ones((H, nb, nb), np.uint8)
+    Q, K = _rand((Z, H, N, d), 40), _rand((Z, H, N, d), 41)
+    am = _rand((N, N), 42)
+    ref = torch.logsumexp(torch.tensor(0.3 * (Q @ np.swapaxes(K, 2, 3)) + am), dim=-1).numpy()
+    assert np.abs(oracle.attention_lse(Q, K, lay, b, 0.3, False, am) - ref).max() < 1e-12
+
+
+def test_lse_rebuilds_p_and_the_output():
+    """exp(x - lse) over the visible entries sums to one per row and, times
+    V, gives the attention output; an empty row has lse = -inf; under causal
+    the first query sees only key 0, so its lse is that one score."""
+    Z, H, nb, b, d = 2, 2, 4, 16, 8
+    N = nb * b
+    lay = W.small_random_layout(H, nb, nb, 0.5, 43, force_diagonal=True)
+    lay[1, 2, :] = 0
+    Q, K, V = (_rand((Z, H, N, d), s) for s in (44, 45, 46))
+    kp = _rand((Z, N), 47)
+    lse = oracle.attention_lse(Q, K, lay, b, 0.4, True, kp_mask=kp)
+    mask = oracle.element_mask(lay, b, True)
+    O = oracle.attention_dense(Q, K, V, lay, b, 0.4, True, kp_mask=kp)
+    for z in range(Z):
+        for h in range(H):
+            x = 0.4 * Q[z, h] @ K[z, h].T + kp[z][None, :]
+            ok = np.isfinite(lse[z, h])
+            P = np.where(mask[h] & ok[:, None], np.exp(x - np.where(ok, lse[z, h], 0.0)[:, None]), 0.0)
+            assert np.abs(P.sum(axis=1) - ok).max() < 1e-12
+            assert np.abs(P @ V[z, h] - O[z, h]).max() < 1e-12
+    assert np.all(np.isneginf(lse[:, 1, 2 * b:3 * b]))
+    assert np.abs(lse[:, :, 0] - (0.4 * (Q[:, :, 0] * K[:, :, 0]).sum(-1) + kp[:, None, 0])).max() < 1e-12

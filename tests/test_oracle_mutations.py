@@ -83,6 +83,9 @@ MUTANTS = {
     "dense_backward_mask_dropped": (
         "x = scale * (Q[z, h] @ K[z, h].T) + _bias(am, kpm, z, qall, kall)",
         "x = scale * (Q[z, h] @ K[z, h].T)"),
+    "lse_max_term_dropped": (
+        "out[z, h] = np.where(ok, mm + np.log(np.where(ok, tot, 1.0)), -np.inf)",
+        "out[z, h] = np.where(ok, np.log(np.where(ok, tot, 1.0)), -np.inf)"),
     "rows_wrong_head_mask": (
         "mask = np.repeat(lay[h, r].astype(bool), b)[None, :].repeat(b, axis=0)",
         "mask = np.repeat(lay[0, r].astype(bool), b)[None, :].repeat(b, axis=0)"),
