@@ -28,7 +28,7 @@ from . import _lib
 from ._lib import AcsrTerm, BsError, BS_BF16, BS_CAUSAL, BS_F16, BS_F32, check, lib
 
 __all__ = ["Layout", "sdd", "softmax", "dsd", "dds", "attention", "softmax_backward", "dsd_t",
-           "attention_backward", "attention_autograd", "BsError", "lib"]
+           "attention_backward", "attention_backward_fused", "attention_autograd", "BsError", "lib"]
 
 
 def _torch():
@@ -245,10 +245,12 @@ def dds(L: Layout, a, s, out=None):
 
 
 def attention(L: Layout, q, k, v, scale: Optional[float] = None, causal: bool = False, out=None, attn_mask=None,
-              key_padding_mask=None):
+              key_padding_mask=None, return_lse: bool = False, lse=None):
     """Fused block-sparse attention O = softmax(scale q k^T + mask) v; the
     mask is the layout's, the optional dense additive masks (see softmax)
-    and the causal one."""
+    and the causal one. With return_lse, also the float32 [Z, H, Nq] row
+    log-sum-exp of the masked scaled scores (-inf for empty rows), written
+    by the same kernel: returns (out, lse)."""
     for n, t in (("q", q), ("k", k), ("v", v)):
         _check_dense(n, t)
     Z, H, Nq, d = q.shape
@@ -261,6 +263,11 @@ def attention(L: Layout, q, k, v, scale: Optional[float] = None, causal: bool = 
     am, kp = _mask_ptrs(L, Z, q.device, attn_mask, key_padding_mask)
     out = _out(out, q.shape, q.dtype, q.device)
     flags = BS_CAUSAL if causal else 0
+    if return_lse:
+        lse = _out(lse, (Z, H, Nq), _torch().float32, q.device, "lse")
+        check(lib().bs_attention_fwd(L.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), Z, d, float(scale),
+                                     flags, am, kp, _dtype_code(q), _stream(q.device)))
+        return out, lse
     if am is None and kp is None:
         check(lib().bs_attention(L.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(out), Z, d, float(scale), flags,
                                  _dtype_code(q), _stream(q.device)))
@@ -338,6 +345,37 @@ def attention_backward(L: Layout, q, k, v, do, scale: Optional[float] = None, ca
     return dq, dk, dv
 
 
+def attention_backward_fused(L: Layout, q, k, v, o, lse, do, scale: Optional[float] = None, causal: bool = False,
+                             attn_mask=None, key_padding_mask=None, workspace=None):
+    """(dq, dk, dv) of attention() from its inputs, its output o and row
+    log-sum-exp lse (attention(..., return_lse=True)) and the output
+    gradient do, on the fused backward kernels (S and P never reach
+    memory). Same scale, causal flag and masks as the forward.
+    workspace: optional float32 [Z, H, Nq] tensor (the D = rowsum(do * o)
+    buffer)."""
+    torch = _torch()
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check_dense(n, t)
+    _check_dense("lse", lse, ndim=3)
+    Z, H, Nq, d = q.shape
+    if not (q.dtype == k.dtype == v.dtype == o.dtype == do.dtype):
+        raise ValueError("q, k, v, o, do must share a dtype")
+    if (H, Nq) != (L.H, L.nbr * L.block) or k.shape != (Z, H, L.nbc * L.block, d) or v.shape != k.shape \
+            or o.shape != q.shape or do.shape != q.shape:
+        raise ValueError("q, o, do must be [Z, H, nbr*b, d]; k, v [Z, H, nbc*b, d]")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (Z, H, Nq):
+        raise ValueError("lse must be float32 [Z, H, nbr*b]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    am, kp = _mask_ptrs(L, Z, q.device, attn_mask, key_padding_mask)
+    ws = _out(workspace, (Z, H, Nq), torch.float32, q.device, "workspace")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    check(lib().bs_attention_bwd(L.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
+                                 _ptr(dk), _ptr(dv), _ptr(ws), Z, d, float(scale), BS_CAUSAL if causal else 0, am, kp,
+                                 _dtype_code(q), _stream(q.device)))
+    return dq, dk, dv
+
+
 _AUTOGRAD_FN = None
 
 
@@ -352,17 +390,19 @@ def _autograd_fn():
         class BlockSparseAttention(torch.autograd.Function):
             @staticmethod
             def forward(ctx, q, k, v, L, scale, causal, attn_mask, key_padding_mask):
-                ctx.save_for_backward(q, k, v)
+                o, lse = attention(L, q, k, v, scale, causal, attn_mask=attn_mask,
+                                   key_padding_mask=key_padding_mask, return_lse=True)
+                ctx.save_for_backward(q, k, v, o, lse)
                 ctx.L, ctx.scale, ctx.causal = L, scale, causal
                 ctx.masks = (attn_mask, key_padding_mask)
-                return attention(L, q, k, v, scale, causal, attn_mask=attn_mask, key_padding_mask=key_padding_mask)
+                return o
 
             @staticmethod
             def backward(ctx, do):
-                q, k, v = ctx.saved_tensors
+                q, k, v, o, lse = ctx.saved_tensors
                 am, kp = ctx.masks
-                dq, dk, dv = attention_backward(ctx.L, q, k, v, do.contiguous(), ctx.scale, ctx.causal,
-                                                attn_mask=am, key_padding_mask=kp)
+                dq, dk, dv = attention_backward_fused(ctx.L, q, k, v, o, lse, do.contiguous(), ctx.scale,
+                                                      ctx.causal, attn_mask=am, key_padding_mask=kp)
                 return dq, dk, dv, None, None, None, None, None
 
         _AUTOGRAD_FN = BlockSparseAttention
@@ -371,9 +411,9 @@ def _autograd_fn():
 
 def attention_autograd(L: Layout, q, k, v, scale: Optional[float] = None, causal: bool = False, attn_mask=None,
                        key_padding_mask=None):
-    """attention() as a differentiable torch op (forward: the fused kernel;
-    backward: attention_backward). The dense masks are constants (no
-    gradient)."""
+    """attention() as a differentiable torch op (forward: the fused kernel,
+    which also writes the row log-sum-exp; backward: the fused backward
+    kernels). The dense masks are constants (no gradient)."""
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
     return _autograd_fn().apply(q, k, v, L, float(scale), bool(causal), attn_mask, key_padding_mask)

@@ -53,6 +53,9 @@ SIGNATURES = {
     "bs_attention_masked": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _f, _i, _vp, _vp, _i, _vp]),
     "bs_attention_backward_masked": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _f, _i, _vp,
                                           _vp, _i, _vp]),
+    "bs_attention_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _f, _i, _vp, _vp, _i, _vp]),
+    "bs_attention_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _f, _i, _vp, _vp, _i,
+                              _vp]),
     "bs_last_error": (C.c_char_p, []),
     "bs_version": (_i, []),
 }

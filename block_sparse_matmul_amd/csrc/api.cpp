@@ -398,6 +398,28 @@ int bs_attention_backward_masked(bs_layout_t L, const void* Q, const void* K, co
   return bsa::launch_dsd_t(L, ws_p, dO, dV, Z, d, dt, s);                               // dV = P^T dO
 }
 
+int bs_attention_bwd(bs_layout_t L, const void* Q, const void* K, const void* V, const void* O, const float* lse,
+                     const void* dO, void* dQ, void* dK, void* dV, float* ws_d, int Z, int d, float scale, int flags,
+                     const float* attn_mask, const float* kp_mask, bs_dtype dt, void* stream) {
+  if (int rc = check_handle(L)) return rc;
+  if (int rc = check_dtype(dt)) return rc;
+  if (int rc = check_masks(attn_mask, kp_mask)) return rc;
+  if (flags & ~BS_CAUSAL) return fail(BS_ERR_INVALID_ARG, "unknown flag");
+  if (Z < 0) return fail(BS_ERR_INVALID_ARG, "Z must be >= 0");
+  if (d != 64 && d != 128) return fail(BS_ERR_UNSUPPORTED, "head size d must be 64 or 128");
+  const bool causal = flags & BS_CAUSAL;
+  if (causal && L->nbr != L->nbc) return fail(BS_ERR_INVALID_ARG, "causal attention needs a square layout");
+  const bool work = Z > 0;
+  if (int rc = check_ptrs(work, {Q, K, V, O, lse, dO, dQ, dK, dV, ws_d})) return rc;
+  if (!work) return BS_OK;
+  if (int rc = check_grid(L, Z)) return rc;
+  log_call("attention_bwd", L, Z, d);
+  bsa::BwdArgs a{Q, K, V, O, lse, dO, dQ, dK, dV, ws_d, Z, d, scale, causal, dt};
+  a.am = attn_mask;
+  a.kp = kp_mask;
+  return bsa::launch_attention_bwd(L, a, (hipStream_t)stream);
+}
+
 int bs_dds(bs_layout_t L, const void* A, const float* S, void* C, int Z, int M, bs_dtype dt, void* stream) {
   if (int rc = check_handle(L)) return rc;
   if (int rc = check_dtype(dt)) return rc;
@@ -416,12 +438,18 @@ int bs_dds(bs_layout_t L, const void* A, const float* S, void* C, int Z, int M, 
 
 int bs_attention(bs_layout_t L, const void* Q, const void* K, const void* V, void* O, int Z, int d, float scale,
                  int flags, bs_dtype dt, void* stream) {
-  return bs_attention_masked(L, Q, K, V, O, Z, d, scale, flags, nullptr, nullptr, dt, stream);
+  return bs_attention_fwd(L, Q, K, V, O, nullptr, Z, d, scale, flags, nullptr, nullptr, dt, stream);
 }
 
 int bs_attention_masked(bs_layout_t L, const void* Q, const void* K, const void* V, void* O, int Z, int d,
                         float scale, int flags, const float* attn_mask, const float* kp_mask, bs_dtype dt,
                         void* stream) {
+  return bs_attention_fwd(L, Q, K, V, O, nullptr, Z, d, scale, flags, attn_mask, kp_mask, dt, stream);
+}
+
+int bs_attention_fwd(bs_layout_t L, const void* Q, const void* K, const void* V, void* O, float* lse, int Z, int d,
+                     float scale, int flags, const float* attn_mask, const float* kp_mask, bs_dtype dt,
+                     void* stream) {
   if (int rc = check_handle(L)) return rc;
   if (int rc = check_masks(attn_mask, kp_mask)) return rc;
   if (int rc = check_dtype(dt)) return rc;
@@ -435,7 +463,11 @@ int bs_attention_masked(bs_layout_t L, const void* Q, const void* K, const void*
   if (!work) return BS_OK;
   if (int rc = check_grid(L, Z)) return rc;
   log_call("attention", L, Z, d);
-  return bsa::launch_attention(L, Q, K, V, O, Z, d, scale, causal, attn_mask, kp_mask, dt, (hipStream_t)stream);
+  bsa::AttnArgs a{Q, K, V, O, Z, d, scale, causal, dt};
+  a.am = attn_mask;
+  a.kp = kp_mask;
+  a.lse = lse;
+  return bsa::launch_attention(L, a, (hipStream_t)stream);
 }
 
 }  // extern "C"

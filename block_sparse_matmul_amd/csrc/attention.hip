@@ -7,16 +7,16 @@
 
 namespace bsa {
 
-int launch_attention(const bs_layout* L, const void* Q, const void* K, const void* V, void* O, int Z, int d,
-                     float scale, bool causal, const float* am, const float* kp, bs_dtype dt, hipStream_t s) {
-  if (am != nullptr || kp != nullptr) return launch_attention_masked(L, Q, K, V, O, Z, d, scale, causal, am, kp, dt, s);
-  if (dt != BS_F32) {
-    const int rc = launch_attention_wide(L, Q, K, V, O, Z, d, scale, causal, dt, s);
+int launch_attention(const bs_layout* L, const AttnArgs& at, hipStream_t s) {
+  if (at.am != nullptr || at.kp != nullptr) return launch_attention_masked(L, at, s);
+  if (at.dt != BS_F32) {
+    const int rc = launch_attention_wide(L, at, s);
     if (rc != kNotApplicable) return rc;
   }
-  Args a{Q, K, V, O, nullptr, Z, scale * kLog2e, causal};
+  Args a{at.Q, at.K, at.V, at.O, nullptr, at.Z, at.scale * kLog2e, at.causal};
   a.use_band = L->band_off != nullptr;
-  return run_mode<MODE_ATTN>(L, a, d, dt, s);
+  a.lse = at.lse;
+  return run_mode<MODE_ATTN>(L, a, at.d, at.dt, s);
 }
 
 int launch_sdd_rowblock(const bs_layout* L, const void* A, const void* B, float* S, int Z, int K, bs_dtype dt,

@@ -11,13 +11,13 @@
 
 namespace bsa {
 
-int launch_attention_masked(const bs_layout* L, const void* Q, const void* K, const void* V, void* O, int Z, int d,
-                            float scale, bool causal, const float* am, const float* kp, bs_dtype dt, hipStream_t s) {
-  Args a{Q, K, V, O, nullptr, Z, scale * kLog2e, causal};
+int launch_attention_masked(const bs_layout* L, const AttnArgs& at, hipStream_t s) {
+  Args a{at.Q, at.K, at.V, at.O, nullptr, at.Z, at.scale * kLog2e, at.causal};
   a.use_band = L->band_off != nullptr;
-  a.am = am;
-  a.kp = kp;
-  return run_mode<MODE_ATTN_MASKED>(L, a, d, dt, s);
+  a.am = at.am;
+  a.kp = at.kp;
+  a.lse = at.lse;
+  return run_mode<MODE_ATTN_MASKED>(L, a, at.d, at.dt, s);
 }
 
 }  // namespace bsa

@@ -34,6 +34,7 @@ namespace bsa {
 namespace {
 
 constexpr float kLog2eB = 1.4426950408889634f;
+constexpr float kLn2B = 0.6931471805599453f;
 constexpr float kTauB = 8.0f;  // lazy-rescale headroom, log2 units
 
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
@@ -75,7 +76,8 @@ template <typename E, int BLK, int D, bool CAUSAL, int NS>
 __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, const int32_t* __restrict__ row_order,
     const int32_t* __restrict__ row_order_h, const u16* __restrict__ Q, const u16* __restrict__ K,
-    const u16* __restrict__ V, u16* __restrict__ O, int Z, int H, int nbr, int nbc, float c, int grouped) {
+    const u16* __restrict__ V, u16* __restrict__ O, int Z, int H, int nbr, int nbc, float c, int grouped,
+    float* __restrict__ lse) {
   using Cfg = WideCfg<BLK, D>;
   using HT = H16<E>;
   using V8 = typename HT::V8;
@@ -408,6 +410,9 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
   for (int t = 0; t < 2; ++t) {
     const float l = rows4_sum(l_run[t]);
     const float inv = (l > 0.f) ? 1.0f / l : 0.f;
+    // row log-sum-exp, natural-log units (l >= 1 when the row saw anything)
+    if (lse != nullptr && g == 0)
+      lse[zh * Nq + q_lo + 16 * t + li] = (l > 0.f) ? (m_run[t] + __builtin_amdgcn_logf(l)) * kLn2B : -INFINITY;
     u16* po = O + (zh * Nq + q_lo + 16 * t + li) * D + 4 * g;
 #pragma unroll
     for (int nt = 0; nt < NNT; ++nt)
@@ -417,22 +422,24 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
 }
 
 template <typename E, int BLK, int D, int NS>
-int launch_ns(const bs_layout* L, const void* Q, const void* K, const void* V, void* O, int Z, float c, bool causal,
-              hipStream_t s) {
+int launch_ns(const bs_layout* L, const AttnArgs& a, float c, hipStream_t s) {
+  const void *Q = a.Q, *K = a.K, *V = a.V;
+  void* O = a.O;
+  const int Z = a.Z;
   const dim3 grid(L->H * L->nbr * Z), block(BLK * 2 * NS);
   // head-grouped order when the longest row (split over NS key groups) is
   // at most a quarter of the work of one workgroup slot (two per CU): then
   // even a long row that starts late adds little to the end of the kernel
   const double per_slot = (double)Z * (double)L->nnz / (2.0 * L->num_cus);
   const int grouped = (4.0 * L->max_row_len / NS <= per_slot) ? 1 : 0;
-  if (causal)
+  if (a.causal)
     hipLaunchKernelGGL((k_attn_wide<E, BLK, D, true, NS>), grid, block, 0, s, L->row_ptr, L->col_idx, L->row_order,
                        L->row_order_h, (const u16*)Q, (const u16*)K, (const u16*)V, (u16*)O, Z, L->H, L->nbr, L->nbc,
-                       c, grouped);
+                       c, grouped, a.lse);
   else
     hipLaunchKernelGGL((k_attn_wide<E, BLK, D, false, NS>), grid, block, 0, s, L->row_ptr, L->col_idx, L->row_order,
                        L->row_order_h, (const u16*)Q, (const u16*)K, (const u16*)V, (u16*)O, Z, L->H, L->nbr, L->nbc,
-                       c, grouped);
+                       c, grouped, a.lse);
   BSA_HIP(hipGetLastError());
   return BS_OK;
 }
@@ -441,8 +448,8 @@ int launch_ns(const bs_layout* L, const void* Q, const void* K, const void* V, v
 // longest row alone (about two workgroups share a CU) outlasts a CU's share
 // of the job.
 template <typename E, int BLK, int D>
-int run(const bs_layout* L, const void* Q, const void* K, const void* V, void* O, int Z, float c, bool causal,
-        hipStream_t s) {
+int run(const bs_layout* L, const AttnArgs& a, float c, hipStream_t s) {
+  const int Z = a.Z;
   using Cfg = WideCfg<BLK, D>;
   constexpr size_t cap = 160 * 1024;
   constexpr int max_ns = (Cfg::bytes(4) <= cap && Cfg::merge_fits(4) && BLK * 8 <= 1024)
@@ -452,36 +459,34 @@ int run(const bs_layout* L, const void* Q, const void* K, const void* V, void* O
   int ns = 1;
   while (ns < max_ns && 2.0 * L->max_row_len / ns > per_cu) ns *= 2;
   if constexpr (max_ns >= 4) {
-    if (ns >= 4) return launch_ns<E, BLK, D, 4>(L, Q, K, V, O, Z, c, causal, s);
+    if (ns >= 4) return launch_ns<E, BLK, D, 4>(L, a, c, s);
   }
   if constexpr (max_ns >= 2) {
-    if (ns >= 2) return launch_ns<E, BLK, D, 2>(L, Q, K, V, O, Z, c, causal, s);
+    if (ns >= 2) return launch_ns<E, BLK, D, 2>(L, a, c, s);
   }
-  return launch_ns<E, BLK, D, 1>(L, Q, K, V, O, Z, c, causal, s);
+  return launch_ns<E, BLK, D, 1>(L, a, c, s);
 }
 
 template <typename E, int D>
-int run_b(const bs_layout* L, const void* Q, const void* K, const void* V, void* O, int Z, float c, bool causal,
-          hipStream_t s) {
+int run_b(const bs_layout* L, const AttnArgs& a, float c, hipStream_t s) {
   switch (L->block) {
-    case 32: return run<E, 32, D>(L, Q, K, V, O, Z, c, causal, s);
-    case 64: return run<E, 64, D>(L, Q, K, V, O, Z, c, causal, s);
-    case 128: return run<E, 128, D>(L, Q, K, V, O, Z, c, causal, s);
+    case 32: return run<E, 32, D>(L, a, c, s);
+    case 64: return run<E, 64, D>(L, a, c, s);
+    case 128: return run<E, 128, D>(L, a, c, s);
   }
   return kNotApplicable;
 }
 
 }  // namespace
 
-int launch_attention_wide(const bs_layout* L, const void* Q, const void* K, const void* V, void* O, int Z, int d,
-                          float scale, bool causal, bs_dtype dt, hipStream_t s) {
-  const float c = scale * kLog2eB;
-  if (dt == BS_BF16) {
-    if (d == 64) return run_b<bf16_t, 64>(L, Q, K, V, O, Z, c, causal, s);
-    if (d == 128) return run_b<bf16_t, 128>(L, Q, K, V, O, Z, c, causal, s);
-  } else if (dt == BS_F16) {
-    if (d == 64) return run_b<f16_t, 64>(L, Q, K, V, O, Z, c, causal, s);
-    if (d == 128) return run_b<f16_t, 128>(L, Q, K, V, O, Z, c, causal, s);
+int launch_attention_wide(const bs_layout* L, const AttnArgs& a, hipStream_t s) {
+  const float c = a.scale * kLog2eB;
+  if (a.dt == BS_BF16) {
+    if (a.d == 64) return run_b<bf16_t, 64>(L, a, c, s);
+    if (a.d == 128) return run_b<bf16_t, 128>(L, a, c, s);
+  } else if (a.dt == BS_F16) {
+    if (a.d == 64) return run_b<f16_t, 64>(L, a, c, s);
+    if (a.d == 128) return run_b<f16_t, 128>(L, a, c, s);
   }
   return kNotApplicable;
 }

@@ -77,19 +77,56 @@ int launch_dsd(const bs_layout* L, const float* P, const void* B, void* C,
                int Z, int Nd, bs_dtype dt, hipStream_t s);
 int launch_dds(const bs_layout* L, const void* A, const float* S, void* C,
                int Z, int M, bs_dtype dt, hipStream_t s);
-int launch_attention(const bs_layout* L, const void* Q, const void* K,
-                     const void* V, void* O, int Z, int d, float scale,
-                     bool causal, const float* am, const float* kp, bs_dtype dt,
-                     hipStream_t s);
+// Fused attention operands: Q [Z][H][nbr*b][d], K, V [Z][H][nbc*b][d], O
+// like Q (dtype dt); optional dense masks am, kp; optional lse, float32
+// [Z][H][nbr*b]: the natural-log softmax denominator of every query row
+// (-inf where nothing is visible).
+struct AttnArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  int Z;
+  int d;
+  float scale;
+  bool causal;
+  bs_dtype dt;
+  const float* am = nullptr;
+  const float* kp = nullptr;
+  float* lse = nullptr;
+};
+int launch_attention(const bs_layout* L, const AttnArgs& a, hipStream_t s);
 int launch_softmax_backward(const bs_layout* L, const float* P, const float* dP, float* dS, int Z, float scale,
                             hipStream_t s);
 int launch_dsd_t(const bs_layout* L, const float* S, const void* B, void* C, int Z, int Nd, bs_dtype dt,
                  hipStream_t s);
 
+// Fused attention backward (backward.hip): dQ, dK, dV from Q, K, V, the
+// forward's O and lse, and dO (all dense operands of dtype dt); Dws: float32
+// [Z][H][nbr*b] workspace for D = rowsum(dO * O); optional dense masks.
+struct BwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* O;
+  const float* lse;
+  const void* dO;
+  void* dQ;
+  void* dK;
+  void* dV;
+  float* Dws;
+  int Z;
+  int d;
+  float scale;
+  bool causal;
+  bs_dtype dt;
+  const float* am = nullptr;
+  const float* kp = nullptr;
+};
+int launch_attention_bwd(const bs_layout* L, const BwdArgs& a, hipStream_t s);
+
 // launch_attention with at least one dense mask (attention_masked.hip)
-int launch_attention_masked(const bs_layout* L, const void* Q, const void* K, const void* V, void* O, int Z, int d,
-                            float scale, bool causal, const float* am, const float* kp, bs_dtype dt,
-                            hipStream_t s);
+int launch_attention_masked(const bs_layout* L, const AttnArgs& a, hipStream_t s);
 
 // SDD and DSD on the fused kernel's row-block machinery (LDS-staged
 // operands); they apply when the contraction (SDD) or output width (DSD) is
@@ -103,8 +140,7 @@ int launch_dsd_rowblock(const bs_layout* L, const float* P, const void* B,
 // 16-bit (bf16, fp16) fused attention on the 32-rows-per-wave kernel
 // (blocks of 32, 64, 128; no dense masks); returns kNotApplicable for other
 // blocks, head sizes or types.
-int launch_attention_wide(const bs_layout* L, const void* Q, const void* K, const void* V, void* O, int Z, int d,
-                          float scale, bool causal, bs_dtype dt, hipStream_t s);
+int launch_attention_wide(const bs_layout* L, const AttnArgs& a, hipStream_t s);
 
 bool log_enabled();
 

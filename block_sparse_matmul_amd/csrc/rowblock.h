@@ -65,6 +65,7 @@ namespace bsa {
 namespace {  // each including translation unit instantiates its own modes
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTau = 8.0f;  // lazy-rescale headroom, log2 units
 
 // MODE_DSDT is the DSD of the transposed block matrix (C = S^T-blocks x B):
@@ -123,7 +124,7 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_rowblock(
     const typename Elem<E>::storage* __restrict__ V, typename Elem<E>::storage* __restrict__ O,
     float* __restrict__ S, const int32_t* __restrict__ blk_id, const int32_t* __restrict__ band, int band_n, int Z,
     int H, int nbr, int nbc, int64_t nnz, float c, const float* __restrict__ amask,
-    const float* __restrict__ kpmask) {
+    const float* __restrict__ kpmask, float* __restrict__ lse) {
   using St = typename Elem<E>::storage;
   using Vec = typename Cfg<E>::Vec;
   constexpr bool BF = !std::is_same<E, float>::value;  // a 16-bit element type (bf16, fp16)
@@ -579,6 +580,11 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_rowblock(
   if constexpr (ATTN) {
     l_run = rows4_sum(l_run);
     inv = (l_run > 0.f) ? 1.0f / l_run : 0.f;
+    // the row's log-sum-exp in natural-log units: l is a sum of
+    // exp2(x - m_run) with x and m_run in log2 units, l >= 1 when the row
+    // saw anything (its largest term is at least 1)
+    if (lse != nullptr && g == 0)
+      lse[zh * Nq + q_index] = (l_run > 0.f) ? (m_run + __builtin_amdgcn_logf(l_run)) * kLn2 : -INFINITY;
   }
   St* po = O + (zh * Nq + q_index) * D + 4 * g;
 #pragma unroll
@@ -605,6 +611,7 @@ struct Args {
   bool use_band = false;  // attention on a slope-1 ACSR layout: computed columns
   const float* am = nullptr;  // dense additive masks (attention)
   const float* kp = nullptr;
+  float* lse = nullptr;  // optional row log-sum-exp output (attention)
 };
 
 template <typename E, int BLK, int D, int NS, int MODE>
@@ -625,11 +632,11 @@ int launch_ns(const bs_layout* L, const Args& a, hipStream_t s) {
   if (is_attn(MODE) && a.causal)
     hipLaunchKernelGGL((k_rowblock<E, BLK, D, true, NS, MODE>), grid, block, 0, s, ptr, idx, order, (const St*)a.Q,
                        (const St*)a.K, (const St*)a.V, (St*)a.O, a.S, bid, band, band_n, a.Z, L->H, nb_out, nb_in,
-                       L->nnz, a.c, a.am, a.kp);
+                       L->nnz, a.c, a.am, a.kp, a.lse);
   else
     hipLaunchKernelGGL((k_rowblock<E, BLK, D, false, NS, MODE>), grid, block, 0, s, ptr, idx, order,
                        (const St*)a.Q, (const St*)a.K, (const St*)a.V, (St*)a.O, a.S, bid, band, band_n, a.Z, L->H,
-                       nb_out, nb_in, L->nnz, a.c, a.am, a.kp);
+                       nb_out, nb_in, L->nnz, a.c, a.am, a.kp, a.lse);
   BSA_HIP(hipGetLastError());
   return BS_OK;
 }

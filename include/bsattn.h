@@ -185,6 +185,16 @@ int bs_attention_masked(bs_layout_t L, const void* Q, const void* K,
                         int flags, const float* attn_mask,
                         const float* kp_mask, bs_dtype dt, void* stream);
 
+/* The forward of the fused backward below: bs_attention_masked that also
+   writes lse (may be NULL), float32 [Z][H][nbr*b]: for every query row the
+   natural log of its softmax denominator, log sum_j exp(x_j) over the
+   visible entries of x = scale*S + masks (-inf for a row with no visible
+   key), so that P = exp(x - lse). Caller-owned. */
+int bs_attention_fwd(bs_layout_t L, const void* Q, const void* K,
+                     const void* V, void* O, float* lse, int Z, int d,
+                     float scale, int flags, const float* attn_mask,
+                     const float* kp_mask, bs_dtype dt, void* stream);
+
 /* ---- backward (the exact gradient of the forward above) ----
    The attention gradient is made of the same three modes (the issue's
    SDD / DSD / DDS) plus the softmax gradient; the autograd pattern (forward
@@ -231,6 +241,24 @@ int bs_attention_backward_masked(bs_layout_t L, const void* Q, const void* K,
                                  int Z, int d, float scale, int flags,
                                  const float* attn_mask, const float* kp_mask,
                                  bs_dtype dt, void* stream);
+
+/* Fused backward: dQ, dK, dV of bs_attention_fwd from its inputs, its
+   output O and lse, and dO = dL/dO, without materialising S or P: with
+   x = scale*S + masks and D = rowsum(dO * O) (which equals rowsum(P * dP)),
+   P = exp(x - lse), dS = scale * P * (dO V^T - D), dQ = dS K, dK = dS^T Q,
+   dV = P^T dO (the same gradient as bs_attention_backward_masked). Two
+   kernels: one over block rows (dQ, and D into ws_d), one over block
+   columns (dK, dV). Q, O, dO, dQ: [Z][H][nbr*b][d]; K, V, dK, dV:
+   [Z][H][nbc*b][d], all of dtype dt; d in {64, 128}. lse: float32
+   [Z][H][nbr*b] as bs_attention_fwd wrote it, with the same scale, flags
+   and masks. ws_d: caller-owned float32 workspace of Z*H*nbr*b elements.
+   16-bit types: P and dS are rounded to dt for the products. */
+int bs_attention_bwd(bs_layout_t L, const void* Q, const void* K,
+                     const void* V, const void* O, const float* lse,
+                     const void* dO, void* dQ, void* dK, void* dV,
+                     float* ws_d, int Z, int d, float scale, int flags,
+                     const float* attn_mask, const float* kp_mask,
+                     bs_dtype dt, void* stream);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* bs_last_error(void);

@@ -131,6 +131,9 @@ def test_attention_backward(b, d, dt, causal):
 
 
 def test_autograd_wrapper_matches_backward_entry_point_and_oracle():
+    """The autograd function runs the forward with its row log-sum-exp and
+    the fused backward: its gradients are that entry point's, bit for bit,
+    and the oracle's."""
     b, d, H, nb, Z = 64, 64, 2, 4, 2
     lay = W.small_random_layout(H, nb, nb, 0.5, 90, force_diagonal=True)
     announce("attention autograd")
@@ -140,7 +143,9 @@ def test_autograd_wrapper_matches_backward_entry_point_and_oracle():
     o = bsa.attention_autograd(L, qd, kd, vd, 0.125, causal=True)
     assert max_abs(f64(o.detach()), oracle.attention_dense(q, k, v, lay, b, 0.125, True)) <= TOL["f32"]
     o.backward(to_dev(do))
-    dq, dk, dv = bsa.attention_backward(L, qd.detach(), kd.detach(), vd.detach(), to_dev(do), 0.125, True)
+    o2, lse = bsa.attention(L, qd.detach(), kd.detach(), vd.detach(), 0.125, True, return_lse=True)
+    dq, dk, dv = bsa.attention_backward_fused(L, qd.detach(), kd.detach(), vd.detach(), o2, lse, to_dev(do), 0.125,
+                                              True)
     for g_auto, g_direct in ((qd.grad, dq), (kd.grad, dk), (vd.grad, dv)):
         assert torch.equal(g_auto, g_direct)
     refs = oracle.attention_backward_dense(q, k, v, do, lay, b, 0.125, True)

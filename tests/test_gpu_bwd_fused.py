@@ -1,0 +1,166 @@
+"""GPU parity of the forward's row log-sum-exp and of the fused backward
+(bs_attention_fwd, bs_attention_bwd) against the oracle.
+
+lse bars: fp32 1e-4; 16-bit types sum the rounded P (relative error at
+most the unit roundoff u of the type), so |d log l| <= u: bf16 u = 2^-9,
+bar 4e-3; fp16 u = 2^-12, bar 1e-3. Gradient bars as for the composed
+backward: fp32 1e-4 absolute, 16-bit TOL[dt] * max(1, max |reference|).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_helpers import TOL, announce, f64, max_abs, to_dev
+
+import block_sparse_matmul_amd as bsa
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+LSE_TOL = {"f32": 1e-4, "bf16": 4e-3, "f16": 1e-3}
+
+
+def _t(shapes, seed, dt):
+    g = torch.Generator("cpu").manual_seed(seed)
+    return [torch.randn(s, generator=g).to(DT[dt]) for s in shapes]
+
+
+def _grad_tol(dt, ref):
+    return TOL["f32"] if dt == "f32" else TOL[dt] * max(1.0, float(np.abs(ref).max()))
+
+
+def _lse_close(got, ref, tol):
+    """Equal -inf where the row sees nothing, within tol elsewhere."""
+    got = f64(got)
+    inf = np.isneginf(ref)
+    assert np.array_equal(np.isneginf(got), inf)
+    return float(np.abs(got[~inf] - ref[~inf]).max()) if (~inf).any() else 0.0
+
+
+@pytest.mark.parametrize("b", [16, 32, 64, 128])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_lse(b, dt, causal):
+    H, nb, Z, d = 2, 4, 2, 64
+    lay = W.small_random_layout(H, nb, nb, 0.5, 400 + b, force_diagonal=True)
+    lay[1, 2, :] = 0
+    announce("forward lse", b, dt, causal)
+    q, k, v = _t([(Z, H, nb * b, d)] * 3, 401, dt)
+    L = bsa.Layout(torch.from_numpy(lay), b)
+    o, lse = bsa.attention(L, to_dev(q), to_dev(k), to_dev(v), 0.125, causal, return_lse=True)
+    o_plain = bsa.attention(L, to_dev(q), to_dev(k), to_dev(v), 0.125, causal)
+    assert torch.equal(o, o_plain)
+    assert _lse_close(lse, oracle.attention_lse(q, k, lay, b, 0.125, causal), LSE_TOL[dt]) <= LSE_TOL[dt]
+
+
+@pytest.mark.parametrize("b", [16, 64])
+def test_forward_lse_masked(b):
+    H, nb, Z, d = 2, 4, 2, 64
+    N = nb * b
+    lay = W.small_random_layout(H, nb, nb, 0.5, 402 + b, force_diagonal=True)
+    announce("forward lse masked", b)
+    q, k, v = _t([(Z, H, N, d)] * 3, 403, "f32")
+    g = torch.Generator("cpu").manual_seed(404)
+    am = torch.randn((N, N), generator=g)
+    am[3, :] = -float("inf")
+    kp = torch.randn((Z, N), generator=g)
+    L = bsa.Layout(torch.from_numpy(lay), b)
+    _, lse = bsa.attention(L, to_dev(q), to_dev(k), to_dev(v), 0.125, True, attn_mask=to_dev(am),
+                           key_padding_mask=to_dev(kp), return_lse=True)
+    ref = oracle.attention_lse(q, k, lay, b, 0.125, True, am, kp)
+    assert _lse_close(lse, ref, 1e-4) <= 1e-4
+
+
+BWD_CASES = [(b, d, dt, causal) for b in (16, 32, 64, 128) for d in (64, 128) for dt in ("f32", "bf16", "f16")
+             for causal in (False, True)]
+
+
+@pytest.mark.parametrize("b,d,dt,causal", BWD_CASES)
+def test_fused_backward(b, d, dt, causal):
+    H, nb, Z = 2, 4, 2
+    lay = W.small_random_layout(H, nb, nb, 0.5, 410 + b + d, force_diagonal=True)
+    lay[1, 2, :] = 0   # an empty row: zero dq, no contribution to dk, dv
+    lay[0, :, 1] = 0   # an empty column: zero dk, dv
+    lay[0, 1, 1] = 0
+    announce("fused backward", b, d, dt, causal)
+    q, k, v, do = _t([(Z, H, nb * b, d)] * 4, 411 + b, dt)
+    scale = 1.0 / np.sqrt(d)
+    L = bsa.Layout(torch.from_numpy(lay), b)
+    qd, kd, vd, dod = (to_dev(t) for t in (q, k, v, do))
+    o, lse = bsa.attention(L, qd, kd, vd, scale, causal, return_lse=True)
+    grads = bsa.attention_backward_fused(L, qd, kd, vd, o, lse, dod, scale, causal)
+    refs = oracle.attention_backward_dense(q, k, v, do, lay, b, scale, causal)
+    for name, got, ref in zip(("dq", "dk", "dv"), grads, refs):
+        assert got.dtype == q.dtype and not torch.isnan(got).any(), name
+        assert max_abs(f64(got), ref) <= _grad_tol(dt, ref), name
+
+
+@pytest.mark.parametrize("b", [16, 64])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_fused_backward_nonsquare(b, dt):
+    H, nbr, nbc, Z, d = 2, 3, 5, 2, 64
+    lay = W.small_random_layout(H, nbr, nbc, 0.5, 420 + b)
+    lay[:, :, 0] = 1
+    announce("fused backward non-square", b, dt)
+    g = torch.Generator("cpu").manual_seed(421)
+    q, do = (torch.randn((Z, H, nbr * b, d), generator=g).to(DT[dt]) for _ in range(2))
+    k, v = (torch.randn((Z, H, nbc * b, d), generator=g).to(DT[dt]) for _ in range(2))
+    L = bsa.Layout(torch.from_numpy(lay), b)
+    qd, kd, vd, dod = (to_dev(t) for t in (q, k, v, do))
+    o, lse = bsa.attention(L, qd, kd, vd, 0.125, return_lse=True)
+    grads = bsa.attention_backward_fused(L, qd, kd, vd, o, lse, dod, 0.125)
+    refs = oracle.attention_backward_dense(q, k, v, do, lay, b, 0.125, False)
+    for name, got, ref in zip(("dq", "dk", "dv"), grads, refs):
+        assert max_abs(f64(got), ref) <= _grad_tol(dt, ref), name
+
+
+@pytest.mark.parametrize("b", [16, 64, 128])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fused_backward_masked(b, dt, causal):
+    H, nb, Z, d = 2, 4, 2, 64
+    N = nb * b
+    lay = W.small_random_layout(H, nb, nb, 0.5, 430 + b, force_diagonal=True)
+    announce("fused backward masked", b, dt, causal)
+    q, k, v, do = _t([(Z, H, N, d)] * 4, 431, dt)
+    g = torch.Generator("cpu").manual_seed(432)
+    am = torch.randn((N, N), generator=g)
+    am[torch.rand((N, N), generator=g) < 0.1] = -float("inf")
+    am[3, :] = -float("inf")
+    kp = torch.randn((Z, N), generator=g) * 0.5
+    kp[Z - 1, N - N // 3:] = -float("inf")
+    L = bsa.Layout(torch.from_numpy(lay), b)
+    qd, kd, vd, dod = (to_dev(t) for t in (q, k, v, do))
+    amd, kpd = to_dev(am), to_dev(kp)
+    o, lse = bsa.attention(L, qd, kd, vd, 0.125, causal, attn_mask=amd, key_padding_mask=kpd, return_lse=True)
+    grads = bsa.attention_backward_fused(L, qd, kd, vd, o, lse, dod, 0.125, causal, attn_mask=amd,
+                                         key_padding_mask=kpd)
+    refs = oracle.attention_backward_dense(q, k, v, do, lay, b, 0.125, causal, am, kp)
+    for name, got, ref in zip(("dq", "dk", "dv"), grads, refs):
+        assert not torch.isnan(got).any(), name
+        assert max_abs(f64(got), ref) <= _grad_tol(dt, ref), name
+
+
+@pytest.mark.parametrize("idx", [1, 2])
+def test_fused_backward_full_size_sampled_heads(idx):
+    """causal_b64 and bigbird_b64 (fp32) at full size; the dense oracle
+    gradient of two (batch, head) pairs."""
+    w = W.WORKLOADS[idx]
+    lay = W.make_layout(w)
+    q, k, v = W.make_qkv(w)
+    g = torch.Generator("cpu").manual_seed(440)
+    do = torch.randn(q.shape, generator=g).to(q.dtype)
+    announce("fused backward full size", w.name)
+    L = bsa.Layout(torch.from_numpy(lay), w.block)
+    qd, kd, vd, dod = (to_dev(t) for t in (q, k, v, do))
+    o, lse = bsa.attention(L, qd, kd, vd, w.scale, w.causal, return_lse=True)
+    dq, dk, dv = bsa.attention_backward_fused(L, qd, kd, vd, o, lse, dod, w.scale, w.causal)
+    dt = "f32" if q.dtype == torch.float32 else "bf16"
+    for z, h in ((0, 0), (w.Z - 1, w.H - 1)):
+        sl = (slice(z, z + 1), slice(h, h + 1))
+        refs = oracle.attention_backward_dense(q[sl], k[sl], v[sl], do[sl], lay[h:h + 1], w.block, w.scale,
+                                               w.causal)
+        for name, got, ref in (("dq", dq, refs[0]), ("dk", dk, refs[1]), ("dv", dv, refs[2])):
+            assert max_abs(f64(got[sl]), ref) <= _grad_tol(dt, ref), (name, z, h)
