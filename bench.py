@@ -187,18 +187,30 @@ def run_workload(w, steps, warmup, with_ops=True, with_cpu=True):
                 "softmax_hbm_frac": round(2 * sbytes / (t_sm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             }
             del S, O2
-            # backward: P recomputed (SDD, softmax), dP = SDD(dO, V), softmax
-            # gradient, dQ = DSD(dS, K), dK and dV by DSD^T: five products
+            # backward, 10 b^2 d algorithmic flops per stored block (dP, dQ,
+            # dK, dV and the recomputed S). Fused: the dQ kernel and the dK dV
+            # kernel from the forward's O and row log-sum-exp (S and dP are
+            # formed in both, 14 b^2 d executed). Composed: P recomputed by
+            # SDD and softmax, dP = SDD(dO, V), softmax gradient, dQ = DSD,
+            # dK and dV by DSD^T, with S and P through HBM.
             g = torch.Generator("cpu").manual_seed(1)
             do = torch.randn(q.shape, generator=g).to(q.dtype).to(dev)
+            fb = 10 * w.block * w.block * w.d * L.nnz * w.Z
+            o, lse = bsa.attention(L, q, k, v, w.scale, w.causal, return_lse=True)
+            wsd = torch.empty(lse.shape, dtype=torch.float32, device=dev)
+            bsa.attention_backward_fused(L, q, k, v, o, lse, do, w.scale, w.causal, workspace=wsd)
+            t_fb = _events_time(lambda: bsa.attention_backward_fused(L, q, k, v, o, lse, do, w.scale, w.causal,
+                                                                     workspace=wsd), n, stream)
+            ops["backward"] = {"ms": round(t_fb, 4), "tflops": round(fb / (t_fb * 1e-3) / 1e12, 3),
+                               "flops": "10 b^2 d per stored block",
+                               "kernels": "fused: dQ over block rows, dK dV over block columns"}
+            del o, lse, wsd
             ws = (torch.empty((w.Z, L.nnz, w.block, w.block), dtype=torch.float32, device=dev),
                   torch.empty((w.Z, L.nnz, w.block, w.block), dtype=torch.float32, device=dev))
             bsa.attention_backward(L, q, k, v, do, w.scale, w.causal, workspace=ws)
             t_bwd = _events_time(lambda: bsa.attention_backward(L, q, k, v, do, w.scale, w.causal, workspace=ws),
                                  n, stream)
-            fb = 10 * w.block * w.block * w.d * L.nnz * w.Z
-            ops["backward"] = {"ms": round(t_bwd, 4), "tflops": round(fb / (t_bwd * 1e-3) / 1e12, 3),
-                               "flops": "10 b^2 d per stored block (5 products, P recomputed)"}
+            ops["backward_composed"] = {"ms": round(t_bwd, 4), "tflops": round(fb / (t_bwd * 1e-3) / 1e12, 3)}
             del do, ws
         if w.dds_m:
             A, Sd = W.make_dds_operands(w, L.nnz)
