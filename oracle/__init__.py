@@ -50,7 +50,7 @@ __all__ = [
     "element_mask", "sdd", "softmax", "dsd", "dds",
     "attention_dense", "attention_blocks", "attention_rows", "attention_lse",
     "attention_blockrow", "nnz_flops_attention", "nnz_flops_dds",
-    "softmax_backward", "dsd_t", "attention_backward_dense", "attention_backward_blocks",
+    "softmax_backward", "dsd_t", "dds_t", "attention_backward_dense", "attention_backward_blocks",
 ]
 
 ALLOWED_BLOCKS = (16, 32, 64, 128)
@@ -267,6 +267,22 @@ def dds(A, S, layout, block: int) -> np.ndarray:
     for k, (h, r, c) in enumerate(_blocks(lay)):
         for z in range(Z):
             C[z, h, :, c * b:(c + 1) * b] += A[z, h, :, r * b:(r + 1) * b] @ S[z, k]
+    return C
+
+
+def dds_t(A, S, layout, block: int) -> np.ndarray:
+    """Dense x transposed sparse: C[z, h, :, r-block] = sum over stored
+    (h, r, c) of A[z, h, :, c-block] @ S[z, k]^T (the DDS of the transposed
+    block matrix). Block rows with no stored block give zero columns."""
+    A, S = _f64(A), _f64(S)
+    lay = check_layout(layout)
+    H, nbr, _ = lay.shape
+    b = block
+    Z, M = A.shape[0], A.shape[2]
+    C = np.zeros((Z, H, M, nbr * b), dtype=np.float64)
+    for k, (h, r, c) in enumerate(_blocks(lay)):
+        for z in range(Z):
+            C[z, h, :, r * b:(r + 1) * b] += A[z, h, :, c * b:(c + 1) * b] @ S[z, k].T
     return C
 
 

@@ -150,3 +150,31 @@ def test_gradient_block_route_equals_dense_route(causal):
         assert np.abs(x - y).max() < 1e-12
     # the empty block row: no gradient reaches its queries
     assert np.all(dense[0][:, 0, b:2 * b] == 0)
+
+
+# ------------------------------------------------------------ dds_t
+
+@pytest.mark.parametrize("b", [16, 32])
+def test_dds_t_is_dds_of_the_transposed_block_matrix(b):
+    H, nbr, nbc, Z, M = 2, 3, 4, 2, 8
+    lay = W.small_random_layout(H, nbr, nbc, 0.5, 30 + b)
+    lay[1, 2, :] = 0  # an empty block row: zero columns of the output
+    nnz = int(lay.sum())
+    S = _rand((Z, nnz, b, b), 31)
+    A = _rand((Z, H, M, nbc * b), 32)
+    layT, ST = _transposed(lay, S)
+    C = oracle.dds_t(A, S, lay, b)
+    assert np.abs(C - oracle.dds(A, ST, layT, b)).max() < 1e-12
+    assert np.all(C[:, 1, :, 2 * b:3 * b] == 0)
+
+
+def test_dds_t_all_ones_is_dense_product_with_the_transpose():
+    H, nb, b, Z, M = 1, 3, 16, 1, 5
+    lay = np.ones((H, nb, nb), np.uint8)
+    S = _rand((Z, nb * nb, b, b), 33)
+    A = _rand((Z, H, M, nb * b), 34)
+    dense = np.zeros((nb * b, nb * b))
+    for k in range(nb * nb):
+        r, c = divmod(k, nb)
+        dense[r * b:(r + 1) * b, c * b:(c + 1) * b] = S[0, k]
+    assert np.abs(oracle.dds_t(A, S, lay, b)[0, 0] - A[0, 0] @ dense.T).max() < 1e-12

@@ -86,6 +86,9 @@ MUTANTS = {
     "lse_max_term_dropped": (
         "out[z, h] = np.where(ok, mm + np.log(np.where(ok, tot, 1.0)), -np.inf)",
         "out[z, h] = np.where(ok, np.log(np.where(ok, tot, 1.0)), -np.inf)"),
+    "dds_t_block_not_transposed": (
+        "C[z, h, :, r * b:(r + 1) * b] += A[z, h, :, c * b:(c + 1) * b] @ S[z, k].T",
+        "C[z, h, :, r * b:(r + 1) * b] += A[z, h, :, c * b:(c + 1) * b] @ S[z, k]"),
     "rows_wrong_head_mask": (
         "mask = np.repeat(lay[h, r].astype(bool), b)[None, :].repeat(b, axis=0)",
         "mask = np.repeat(lay[0, r].astype(bool), b)[None, :].repeat(b, axis=0)"),
