@@ -25,7 +25,7 @@ from typing import Dict, Optional, Sequence, Tuple
 import numpy as np
 
 from . import _lib
-from ._lib import AcsrTerm, BsError, BS_BF16, BS_CAUSAL, BS_F16, BS_F32, check, lib
+from ._lib import AcsrTerm, BsError, BS_BF16, BS_CAUSAL, BS_F16, BS_F32, BS_TRANS_A, BS_TRANS_B, check, lib
 
 __all__ = ["Layout", "sdd", "softmax", "dsd", "dds", "attention", "softmax_backward", "dsd_t",
            "attention_backward", "attention_backward_fused", "attention_autograd", "BsError", "lib"]
@@ -161,16 +161,31 @@ def _out(out, shape, dtype, device, name="out"):
     return out
 
 
-def sdd(L: Layout, a, b, out=None):
-    """S[z, k] = a[z, h, r-block, :] @ b[z, h, c-block, :]^T for each stored block."""
+def _trans(trans_a: bool, trans_b: bool) -> int:
+    return (BS_TRANS_A if trans_a else 0) | (BS_TRANS_B if trans_b else 0)
+
+
+def sdd(L: Layout, a, b, out=None, trans_a: bool = False, trans_b: bool = False):
+    """S[z, k] = a'[z, h, r-block, :] @ b'[z, h, c-block, :]^T for each stored
+    block, where a' = a ([Z, H, nbr*b, K]) or, with trans_a, a is stored as
+    [Z, H, K, nbr*b] and a' is its transpose; b' likewise ([Z, H, nbc*b, K],
+    or [Z, H, K, nbc*b] with trans_b)."""
     torch = _torch()
     _check_dense("a", a)
     _check_dense("b", b)
-    Z, H, Na, K = a.shape
-    if a.dtype != b.dtype or b.shape != (Z, H, L.nbc * L.block, K) or (H, Na) != (L.H, L.nbr * L.block):
-        raise ValueError("a must be [Z, H, nbr*b, K] and b [Z, H, nbc*b, K] of one dtype")
+    Z, H = a.shape[:2]
+    K = a.shape[2] if trans_a else a.shape[3]
+    Na, Nb = L.nbr * L.block, L.nbc * L.block
+    if a.dtype != b.dtype or tuple(a.shape) != ((Z, H, K, Na) if trans_a else (Z, H, Na, K)) \
+            or tuple(b.shape) != ((Z, H, K, Nb) if trans_b else (Z, H, Nb, K)) or H != L.H:
+        raise ValueError("a must be [Z, H, nbr*b, K] ([Z, H, K, nbr*b] with trans_a) and b [Z, H, nbc*b, K] "
+                         "([Z, H, K, nbc*b] with trans_b), of one dtype")
     out = _out(out, (Z, L.nnz, L.block, L.block), torch.float32, a.device)
-    check(lib().bs_sdd(L.handle, _ptr(a), _ptr(b), _ptr(out), Z, K, _dtype_code(a), _stream(a.device)))
+    if trans_a or trans_b:
+        check(lib().bs_sdd_ex(L.handle, _ptr(a), _ptr(b), _ptr(out), Z, K, _trans(trans_a, trans_b), _dtype_code(a),
+                              _stream(a.device)))
+    else:
+        check(lib().bs_sdd(L.handle, _ptr(a), _ptr(b), _ptr(out), Z, K, _dtype_code(a), _stream(a.device)))
     return out
 
 
@@ -214,33 +229,53 @@ def softmax(L: Layout, s, scale: float, causal: bool = False, out=None, inplace:
     return out
 
 
-def dsd(L: Layout, p, b, out=None):
-    """C[z, h, r-block, :] = sum over stored (h, r, c) of p[z, k] @ b[z, h, c-block, :]."""
+def dsd(L: Layout, p, b, out=None, trans_a: bool = False, trans_b: bool = False):
+    """C[z, h, r-block, :] = sum over stored (h, r, c) of p[z, k] @ b[z, h, c-block, :].
+    trans_a: the block matrix transposed (C[z, h, c-block, :] = sum of
+    p[z, k]^T @ b[z, h, r-block, :], as dsd_t); trans_b: b stored as
+    [Z, H, Nd, rows] and used transposed."""
     torch = _torch()
     _check_dense("p", p)
     _check_dense("b", b)
-    Z, H, Nb, Nd = b.shape
+    Z, H = b.shape[:2]
+    Nd = b.shape[2] if trans_b else b.shape[3]
+    n_in = (L.nbr if trans_a else L.nbc) * L.block
+    n_out = (L.nbc if trans_a else L.nbr) * L.block
     if p.dtype != torch.float32 or p.shape != (Z, L.nnz, L.block, L.block):
         raise ValueError("p must be float32 [Z, nnz, b, b]")
-    if (H, Nb) != (L.H, L.nbc * L.block):
-        raise ValueError("b must be [Z, H, nbc*b, Nd]")
-    out = _out(out, (Z, H, L.nbr * L.block, Nd), b.dtype, b.device)
-    check(lib().bs_dsd(L.handle, _ptr(p), _ptr(b), _ptr(out), Z, Nd, _dtype_code(b), _stream(b.device)))
+    if H != L.H or tuple(b.shape) != ((Z, H, Nd, n_in) if trans_b else (Z, H, n_in, Nd)):
+        raise ValueError(f"b must be [Z, H, {n_in}, Nd] ([Z, H, Nd, {n_in}] with trans_b)")
+    out = _out(out, (Z, H, n_out, Nd), b.dtype, b.device)
+    if trans_a or trans_b:
+        check(lib().bs_dsd_ex(L.handle, _ptr(p), _ptr(b), _ptr(out), Z, Nd, _trans(trans_a, trans_b),
+                              _dtype_code(b), _stream(b.device)))
+    else:
+        check(lib().bs_dsd(L.handle, _ptr(p), _ptr(b), _ptr(out), Z, Nd, _dtype_code(b), _stream(b.device)))
     return out
 
 
-def dds(L: Layout, a, s, out=None):
-    """C[z, h, :, c-block] = sum over stored (h, r, c) of a[z, h, :, r-block] @ s[z, k]."""
+def dds(L: Layout, a, s, out=None, trans_a: bool = False, trans_b: bool = False):
+    """C[z, h, :, c-block] = sum over stored (h, r, c) of a[z, h, :, r-block] @ s[z, k].
+    trans_a: a stored as [Z, H, rows, M] and used transposed; trans_b: the
+    block matrix transposed (C[z, h, :, r-block] = sum of
+    a[z, h, :, c-block] @ s[z, k]^T)."""
     torch = _torch()
     _check_dense("a", a)
     _check_dense("s", s)
-    Z, H, M, Na = a.shape
+    Z, H = a.shape[:2]
+    M = a.shape[3] if trans_a else a.shape[2]
+    n_in = (L.nbc if trans_b else L.nbr) * L.block
+    n_out = (L.nbr if trans_b else L.nbc) * L.block
     if s.dtype != torch.float32 or s.shape != (Z, L.nnz, L.block, L.block):
         raise ValueError("s must be float32 [Z, nnz, b, b]")
-    if (H, Na) != (L.H, L.nbr * L.block):
-        raise ValueError("a must be [Z, H, M, nbr*b]")
-    out = _out(out, (Z, H, M, L.nbc * L.block), a.dtype, a.device)
-    check(lib().bs_dds(L.handle, _ptr(a), _ptr(s), _ptr(out), Z, M, _dtype_code(a), _stream(a.device)))
+    if H != L.H or tuple(a.shape) != ((Z, H, n_in, M) if trans_a else (Z, H, M, n_in)):
+        raise ValueError(f"a must be [Z, H, M, {n_in}] ([Z, H, {n_in}, M] with trans_a)")
+    out = _out(out, (Z, H, M, n_out), a.dtype, a.device)
+    if trans_a or trans_b:
+        check(lib().bs_dds_ex(L.handle, _ptr(a), _ptr(s), _ptr(out), Z, M, _trans(trans_a, trans_b),
+                              _dtype_code(a), _stream(a.device)))
+    else:
+        check(lib().bs_dds(L.handle, _ptr(a), _ptr(s), _ptr(out), Z, M, _dtype_code(a), _stream(a.device)))
     return out
 
 

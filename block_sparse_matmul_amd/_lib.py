@@ -23,6 +23,8 @@ BS_F32 = 0
 BS_BF16 = 1
 BS_F16 = 2
 BS_CAUSAL = 1
+BS_TRANS_A = 1
+BS_TRANS_B = 2
 
 # every symbol the header declares, with (restype, argtypes)
 _vp, _i, _f, _i64p = C.c_void_p, C.c_int, C.c_float, C.POINTER(C.c_int64)
@@ -56,6 +58,9 @@ SIGNATURES = {
     "bs_attention_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _f, _i, _vp, _vp, _i, _vp]),
     "bs_attention_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _f, _i, _vp, _vp, _i,
                               _vp]),
+    "bs_sdd_ex": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
+    "bs_dsd_ex": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
+    "bs_dds_ex": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
     "bs_last_error": (C.c_char_p, []),
     "bs_version": (_i, []),
 }

@@ -278,7 +278,13 @@ void bs_layout_free(bs_layout_t L) {
 }
 
 int bs_sdd(bs_layout_t L, const void* A, const void* B, float* S, int Z, int K, bs_dtype dt, void* stream) {
+  return bs_sdd_ex(L, A, B, S, Z, K, 0, dt, stream);
+}
+
+int bs_sdd_ex(bs_layout_t L, const void* A, const void* B, float* S, int Z, int K, int trans, bs_dtype dt,
+              void* stream) {
   if (int rc = check_handle(L)) return rc;
+  if (trans & ~(BS_TRANS_A | BS_TRANS_B)) return fail(BS_ERR_INVALID_ARG, "unknown transpose flag");
   if (int rc = check_dtype(dt)) return rc;
   if (Z < 0 || K <= 0) return fail(BS_ERR_INVALID_ARG, "Z must be >= 0 and K > 0");
   if (K % 16) return fail(BS_ERR_UNSUPPORTED, "K must be a multiple of 16");
@@ -289,7 +295,7 @@ int bs_sdd(bs_layout_t L, const void* A, const void* B, float* S, int Z, int K, 
   if ((int64_t)Z * L->nnz * L->block * L->block > ((int64_t)1 << 46))
     return fail(BS_ERR_SHAPE, "block-sparse tensor too large");
   log_call("sdd", L, Z, K);
-  return bsa::launch_sdd(L, A, B, S, Z, K, dt, (hipStream_t)stream);
+  return bsa::launch_sdd(L, A, B, S, Z, K, trans, dt, (hipStream_t)stream);
 }
 
 int bs_softmax(bs_layout_t L, const float* S, float* P, int Z, float scale, int flags, void* stream) {
@@ -314,7 +320,13 @@ int bs_softmax_masked(bs_layout_t L, const float* S, float* P, int Z, float scal
 }
 
 int bs_dsd(bs_layout_t L, const float* P, const void* B, void* C, int Z, int Nd, bs_dtype dt, void* stream) {
+  return bs_dsd_ex(L, P, B, C, Z, Nd, 0, dt, stream);
+}
+
+int bs_dsd_ex(bs_layout_t L, const float* P, const void* B, void* C, int Z, int Nd, int trans, bs_dtype dt,
+              void* stream) {
   if (int rc = check_handle(L)) return rc;
+  if (trans & ~(BS_TRANS_A | BS_TRANS_B)) return fail(BS_ERR_INVALID_ARG, "unknown transpose flag");
   if (int rc = check_dtype(dt)) return rc;
   if (Z < 0 || Nd <= 0) return fail(BS_ERR_INVALID_ARG, "Z must be >= 0 and Nd > 0");
   if (Nd % 16) return fail(BS_ERR_UNSUPPORTED, "Nd must be a multiple of 16");
@@ -326,7 +338,7 @@ int bs_dsd(bs_layout_t L, const float* P, const void* B, void* C, int Z, int Nd,
   if (!work) return BS_OK;
   if (int rc = check_grid(L, Z)) return rc;
   log_call("dsd", L, Z, Nd);
-  return bsa::launch_dsd(L, P, B, C, Z, Nd, dt, (hipStream_t)stream);
+  return bsa::launch_dsd_ex(L, P, B, C, Z, Nd, trans, dt, (hipStream_t)stream);
 }
 
 int bs_softmax_backward(bs_layout_t L, const float* P, const float* dP, float* dS, int Z, float scale, void* stream) {
@@ -389,9 +401,9 @@ int bs_attention_backward_masked(bs_layout_t L, const void* Q, const void* K, co
     return fail(BS_ERR_SHAPE, "too many query rows");
   log_call("attention_backward", L, Z, d);
   hipStream_t s = (hipStream_t)stream;
-  if (int rc = bsa::launch_sdd(L, Q, K, ws_s, Z, d, dt, s)) return rc;                  // S = Q K^T
+  if (int rc = bsa::launch_sdd(L, Q, K, ws_s, Z, d, 0, dt, s)) return rc;               // S = Q K^T
   if (int rc = bsa::launch_softmax(L, ws_s, ws_p, Z, scale, causal, attn_mask, kp_mask, s)) return rc;  // P
-  if (int rc = bsa::launch_sdd(L, dO, V, ws_s, Z, d, dt, s)) return rc;                 // dP = dO V^T
+  if (int rc = bsa::launch_sdd(L, dO, V, ws_s, Z, d, 0, dt, s)) return rc;              // dP = dO V^T
   if (int rc = bsa::launch_softmax_backward(L, ws_p, ws_s, ws_s, Z, scale, s)) return rc;  // dS
   if (int rc = bsa::launch_dsd(L, ws_s, K, dQ, Z, d, dt, s)) return rc;                 // dQ = dS K
   if (int rc = bsa::launch_dsd_t(L, ws_s, Q, dK, Z, d, dt, s)) return rc;               // dK = dS^T Q
@@ -421,7 +433,13 @@ int bs_attention_bwd(bs_layout_t L, const void* Q, const void* K, const void* V,
 }
 
 int bs_dds(bs_layout_t L, const void* A, const float* S, void* C, int Z, int M, bs_dtype dt, void* stream) {
+  return bs_dds_ex(L, A, S, C, Z, M, 0, dt, stream);
+}
+
+int bs_dds_ex(bs_layout_t L, const void* A, const float* S, void* C, int Z, int M, int trans, bs_dtype dt,
+              void* stream) {
   if (int rc = check_handle(L)) return rc;
+  if (trans & ~(BS_TRANS_A | BS_TRANS_B)) return fail(BS_ERR_INVALID_ARG, "unknown transpose flag");
   if (int rc = check_dtype(dt)) return rc;
   if (Z < 0 || M <= 0) return fail(BS_ERR_INVALID_ARG, "Z must be >= 0 and M > 0");
   if (M % 16) return fail(BS_ERR_UNSUPPORTED, "M must be a multiple of 16");
@@ -433,7 +451,7 @@ int bs_dds(bs_layout_t L, const void* A, const float* S, void* C, int Z, int M, 
   if (!work) return BS_OK;
   if (int rc = check_grid(L, Z)) return rc;
   log_call("dds", L, Z, M);
-  return bsa::launch_dds(L, A, S, C, Z, M, dt, (hipStream_t)stream);
+  return bsa::launch_dds_ex(L, A, S, C, Z, M, trans, dt, (hipStream_t)stream);
 }
 
 int bs_attention(bs_layout_t L, const void* Q, const void* K, const void* V, void* O, int Z, int d, float scale,

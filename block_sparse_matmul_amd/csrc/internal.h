@@ -69,7 +69,7 @@ int expand_acsr(const bs_acsr_term* terms_dev, int n_terms, int H, int nbr,
 // am, kp: the optional dense additive masks of the softmax and the fused
 // attention (float32 [nbr*b][nbc*b] and [Z][nbc*b]; null when absent).
 int launch_sdd(const bs_layout* L, const void* A, const void* B, float* S,
-               int Z, int K, bs_dtype dt, hipStream_t s);
+               int Z, int K, int trans, bs_dtype dt, hipStream_t s);
 int launch_softmax(const bs_layout* L, const float* S, float* P, int Z,
                    float scale, bool causal, const float* am, const float* kp,
                    hipStream_t s);
@@ -124,6 +124,26 @@ struct BwdArgs {
   const float* kp = nullptr;
 };
 int launch_attention_bwd(const bs_layout* L, const BwdArgs& a, hipStream_t s);
+
+// DSD and DDS with the BS_TRANS_A / BS_TRANS_B flags (dsd.hip): the plain
+// and fast paths where they apply, otherwise the general strided kernel
+// (GenArgs: P the block values, B the dense operand, C the output; N the
+// output width; TP: walk block columns with the blocks transposed; BT / CT:
+// B / C addressed [n][j] instead of [j][n]; ld*: row strides; *_head: the
+// (batch, head) strides).
+struct GenArgs {
+  const float* P;
+  const void* B;
+  void* C;
+  int Z;
+  int N;
+  bool TP, BT, CT;
+  int64_t ldb, b_head, ldc, c_head;
+};
+int launch_dsd_ex(const bs_layout* L, const float* P, const void* B, void* C, int Z, int Nd, int trans, bs_dtype dt,
+                  hipStream_t s);
+int launch_dds_ex(const bs_layout* L, const void* A, const float* S, void* C, int Z, int M, int trans, bs_dtype dt,
+                  hipStream_t s);
 
 // launch_attention with at least one dense mask (attention_masked.hip)
 int launch_attention_masked(const bs_layout* L, const AttnArgs& a, hipStream_t s);

@@ -3,6 +3,10 @@
 // For every stored block k = (h, r, c):
 //   S[z, k] = A[z, h, r-block, :] . B[z, h, c-block, :]^T      (fp32 out)
 //
+// Either dense operand may be stored transposed (BS_TRANS_A: A as
+// [Z][H][K][nbr*b]; BS_TRANS_B: B as [Z][H][K][nbc*b]); those take the
+// generic kernel below with gathered fragments.
+//
 // K = 64 or 128 runs on the fused attention's row-block kernel (B blocks
 // staged through LDS, scores stored from the score registers). Other K take
 // the kernel below: one workgroup (4 waves) per (batch, block row), block
@@ -16,7 +20,10 @@
 namespace bsa {
 namespace {
 
-template <typename E, int BLK, int T>
+// TA / TB: A stored [Z][H][K][nbr*b] / B stored [Z][H][K][nbc*b] (the
+// operand transposed in memory): its fragments are gathered with the row
+// length as stride, consecutive lanes reading consecutive addresses.
+template <typename E, int BLK, int T, bool TA, bool TB>
 __global__ __launch_bounds__(256) void k_sdd(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
                                              const int32_t* __restrict__ row_order,
                                              const typename Elem<E>::storage* __restrict__ A,
@@ -35,20 +42,24 @@ __global__ __launch_bounds__(256) void k_sdd(const int32_t* __restrict__ row_ptr
   const int k0 = row_ptr[hr], k1 = row_ptr[hr + 1];
   const int items = (k1 - k0) * TPB * TPB;
   const int64_t zh = (int64_t)z * H + h;
-  const St* a_row = A + (zh * nbr * BLK + (int64_t)r * BLK) * K + g * VEC;
+  const int64_t NaT = (int64_t)nbr * BLK, NbT = (int64_t)nbc * BLK;
   for (int it = wave; it < items; it += 4) {
     const int kk = k0 + it / (TPB * TPB);
     const int t = it % (TPB * TPB);
     const int ti = t / TPB, tj = t % TPB;
     const int c = col_idx[kk];
-    const St* pa = a_row + (int64_t)(ti * T + li) * K;
-    const St* pb = B + (zh * nbc * BLK + (int64_t)c * BLK + tj * T + li) * K + g * VEC;
+    const int64_t ia = (int64_t)r * BLK + ti * T + li;  // this lane's row of A
+    const int64_t jb = (int64_t)c * BLK + tj * T + li;  // and of B
+    const St* pa = TA ? A + zh * NaT * K + ia + (int64_t)g * VEC * NaT : A + (zh * NaT + ia) * K + g * VEC;
+    const St* pb = TB ? B + zh * NbT * K + jb + (int64_t)g * VEC * NbT : B + (zh * NbT + jb) * K + g * VEC;
     AccT acc = {};
     for (int k = 0; k < K; k += KC) {
       Frag<E> fa, fb;
       if (k + g * VEC < K) {
-        fa.load(pa + k);
-        fb.load(pb + k);
+        if constexpr (TA) fa.load_strided(pa + (int64_t)k * NaT, NaT);
+        else fa.load(pa + k);
+        if constexpr (TB) fb.load_strided(pb + (int64_t)k * NbT, NbT);
+        else fb.load(pb + k);
       } else {
         fa.zero();
         fb.zero();
@@ -61,36 +72,48 @@ __global__ __launch_bounds__(256) void k_sdd(const int32_t* __restrict__ row_ptr
   }
 }
 
-template <typename E, int BLK>
+template <typename E, int BLK, bool TA, bool TB>
 int run(const bs_layout* L, const void* A, const void* B, float* S, int Z, int K, hipStream_t s) {
   using St = typename Elem<E>::storage;
   constexpr int T = BLK >= 32 ? 32 : 16;
-  hipLaunchKernelGGL((k_sdd<E, BLK, T>), dim3(L->H * L->nbr * Z), dim3(256), 0, s, L->row_ptr, L->col_idx,
+  hipLaunchKernelGGL((k_sdd<E, BLK, T, TA, TB>), dim3(L->H * L->nbr * Z), dim3(256), 0, s, L->row_ptr, L->col_idx,
                      L->row_order, (const St*)A, (const St*)B, S, Z, L->H, L->nbr, L->nbc, K, L->nnz);
   BSA_HIP(hipGetLastError());
   return BS_OK;
 }
 
-template <typename E>
+template <typename E, bool TA, bool TB>
 int run_e(const bs_layout* L, const void* A, const void* B, float* S, int Z, int K, hipStream_t s) {
   switch (L->block) {
-    case 16: return run<E, 16>(L, A, B, S, Z, K, s);
-    case 32: return run<E, 32>(L, A, B, S, Z, K, s);
-    case 64: return run<E, 64>(L, A, B, S, Z, K, s);
-    case 128: return run<E, 128>(L, A, B, S, Z, K, s);
+    case 16: return run<E, 16, TA, TB>(L, A, B, S, Z, K, s);
+    case 32: return run<E, 32, TA, TB>(L, A, B, S, Z, K, s);
+    case 64: return run<E, 64, TA, TB>(L, A, B, S, Z, K, s);
+    case 128: return run<E, 128, TA, TB>(L, A, B, S, Z, K, s);
   }
   return fail(BS_ERR_UNSUPPORTED, "block must be 16, 32, 64 or 128");
 }
 
+template <typename E>
+int run_t(const bs_layout* L, const void* A, const void* B, float* S, int Z, int K, int trans, hipStream_t s) {
+  switch (trans & (BS_TRANS_A | BS_TRANS_B)) {
+    case 0: return run_e<E, false, false>(L, A, B, S, Z, K, s);
+    case BS_TRANS_A: return run_e<E, true, false>(L, A, B, S, Z, K, s);
+    case BS_TRANS_B: return run_e<E, false, true>(L, A, B, S, Z, K, s);
+  }
+  return run_e<E, true, true>(L, A, B, S, Z, K, s);
+}
+
 }  // namespace
 
-int launch_sdd(const bs_layout* L, const void* A, const void* B, float* S, int Z, int K, bs_dtype dt,
+int launch_sdd(const bs_layout* L, const void* A, const void* B, float* S, int Z, int K, int trans, bs_dtype dt,
                hipStream_t s) {
-  const int rc = launch_sdd_rowblock(L, A, B, S, Z, K, dt, s);
-  if (rc != kNotApplicable) return rc;
-  if (dt == BS_BF16) return run_e<bf16_t>(L, A, B, S, Z, K, s);
-  if (dt == BS_F16) return run_e<f16_t>(L, A, B, S, Z, K, s);
-  return run_e<float>(L, A, B, S, Z, K, s);
+  if (trans == 0) {
+    const int rc = launch_sdd_rowblock(L, A, B, S, Z, K, dt, s);
+    if (rc != kNotApplicable) return rc;
+  }
+  if (dt == BS_BF16) return run_t<bf16_t>(L, A, B, S, Z, K, trans, s);
+  if (dt == BS_F16) return run_t<f16_t>(L, A, B, S, Z, K, trans, s);
+  return run_t<float>(L, A, B, S, Z, K, trans, s);
 }
 
 }  // namespace bsa

@@ -174,12 +174,22 @@ template <>
 struct Frag<float> {
   f32x4 v;
   __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const f32x4*>(p); }
+  // elements p[0], p[s], p[2 s], p[3 s] (an operand stored the other way round)
+  __device__ __forceinline__ void load_strided(const float* p, int64_t s) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = p[q * s];
+  }
   __device__ __forceinline__ void zero() { v = f32x4{0.f, 0.f, 0.f, 0.f}; }
 };
 template <typename E>
 struct Frag16 {
   typename H16<E>::V8 v;
   __device__ __forceinline__ void load(const u16* p) { v = *reinterpret_cast<const typename H16<E>::V8*>(p); }
+  // elements p[0], p[s], ..., p[7 s]
+  __device__ __forceinline__ void load_strided(const u16* p, int64_t s) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = __builtin_bit_cast(typename H16<E>::T, p[q * s]);
+  }
   __device__ __forceinline__ void zero() {
     const typename H16<E>::T z = H16<E>::cvt(0.f);
     v = typename H16<E>::V8{z, z, z, z, z, z, z, z};

@@ -57,6 +57,9 @@ typedef enum { BS_F32 = 0, BS_BF16 = 1, BS_F16 = 2 } bs_dtype;
 /* flags for bs_softmax / bs_attention */
 enum { BS_CAUSAL = 1 };
 
+/* operand flags for bs_sdd_ex / bs_dsd_ex / bs_dds_ex */
+enum { BS_TRANS_A = 1, BS_TRANS_B = 2 };
+
 typedef enum {
   BS_OK = 0,
   BS_ERR_INVALID_ARG = -1, /* null pointer with work to do, negative size,
@@ -259,6 +262,33 @@ int bs_attention_bwd(bs_layout_t L, const void* Q, const void* K,
                      float* ws_d, int Z, int d, float scale, int flags,
                      const float* attn_mask, const float* kp_mask,
                      bs_dtype dt, void* stream);
+
+/* ---- the three modes with transposed operands (question on blocksparse:
+   the three modes; the flags follow the usual matmul convention of
+   operands used transposed) ----
+   bs_sdd_ex: S[z,k] = A'[z,h,r-block,:] . B'[z,h,c-block,:]^T with
+     A' = A stored [Z][H][nbr*b][K], or, with BS_TRANS_A, stored as
+     [Z][H][K][nbr*b] (A' is its transpose); B' likewise with BS_TRANS_B:
+     [Z][H][nbc*b][K] or [Z][H][K][nbc*b]. trans = 0 is bs_sdd.
+   bs_dsd_ex: C = S' B' over the block matrix S' = S (block rows walked) or,
+     with BS_TRANS_A, its transpose (block columns walked, blocks
+     transposed: bs_dsd_t). B' is [Z][H][nb_in*b][Nd], or with BS_TRANS_B
+     stored as [Z][H][Nd][nb_in*b]; C: [Z][H][nb_out*b][Nd], where
+     (nb_in, nb_out) = (nbc, nbr), or (nbr, nbc) with BS_TRANS_A.
+   bs_dds_ex: C = A' S' with S' = S or, with BS_TRANS_B, its transpose;
+     A' is [Z][H][M][nb_in*b], or with BS_TRANS_A stored as
+     [Z][H][nb_in*b][M]; C: [Z][H][M][nb_out*b], where (nb_in, nb_out) =
+     (nbr, nbc), or (nbc, nbr) with BS_TRANS_B.
+   Dtypes, sizes (K, Nd, M multiples of 16), empty rows / columns and errors
+   as the plain calls; other flag bits are BS_ERR_INVALID_ARG. Layouts the
+   plain calls cover run on their kernels; the others on a general kernel
+   that gathers the transposed operands. */
+int bs_sdd_ex(bs_layout_t L, const void* A, const void* B, float* S, int Z,
+              int K, int trans, bs_dtype dt, void* stream);
+int bs_dsd_ex(bs_layout_t L, const float* S, const void* B, void* C, int Z,
+              int Nd, int trans, bs_dtype dt, void* stream);
+int bs_dds_ex(bs_layout_t L, const void* A, const float* S, void* C, int Z,
+              int M, int trans, bs_dtype dt, void* stream);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* bs_last_error(void);
