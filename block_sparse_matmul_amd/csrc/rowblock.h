@@ -641,15 +641,18 @@ int launch_ns(const bs_layout* L, const Args& a, hipStream_t s) {
   return BS_OK;
 }
 
-// Key groups per workgroup. With one group, about four workgroups share a
-// CU, so a row of n blocks needs ~4n block-times of its CU while the CU's
+// Key groups per workgroup. With one group, several workgroups share a CU,
+// so a row of n blocks needs ~share*n block-times of its CU while the CU's
 // whole share of the job is Z*nnz/CUs block-times: once the longest row
 // exceeds that, it sets the end of the kernel. NS groups cut the row's own
 // time by NS (the groups run its blocks side by side and merge at the end).
-inline int pick_key_groups(const bs_layout* L, int Z, int max_ns, int max_len) {
+// The share was set by measurement: 2 for the fused attention (causal_b64
+// NS = 1 and bigbird_b64 NS = 2 came out 4% and 13% faster than with 4),
+// 4 for the SDD and DSD modes (2 made the DSD up to 18% slower).
+inline int pick_key_groups(const bs_layout* L, int Z, int max_ns, int max_len, double share) {
   const double per_cu = (double)Z * (double)L->nnz / L->num_cus;
   int ns = 1;
-  while (ns < max_ns && 4.0 * max_len / ns > per_cu) ns *= 2;
+  while (ns < max_ns && share * max_len / ns > per_cu) ns *= 2;
   return ns;
 }
 
@@ -658,7 +661,8 @@ int run(const bs_layout* L, const Args& a, hipStream_t s) {
   // largest key-group count (up to 4, and 1024 threads) whose LDS fits in 160 KiB
   constexpr size_t stage = Lds<E, BLK, D, MODE>::STAGE;
   constexpr int max_ns = (BLK <= 64 && 4 * stage <= 160 * 1024) ? 4 : ((BLK <= 64 && 2 * stage <= 160 * 1024) ? 2 : 1);
-  const int ns = pick_key_groups(L, a.Z, max_ns, MODE == MODE_DSDT ? L->max_col_len : L->max_row_len);
+  const int ns = pick_key_groups(L, a.Z, max_ns, MODE == MODE_DSDT ? L->max_col_len : L->max_row_len,
+                                 is_attn(MODE) ? 2.0 : 4.0);
   if constexpr (max_ns >= 4) {
     if (ns >= 4) return launch_ns<E, BLK, D, 4, MODE>(L, a, s);
   }
