@@ -60,8 +60,9 @@ __global__ __launch_bounds__(256) void k_softmax(const int32_t* __restrict__ row
   const int q_index = r * b + i;
   const float NEG = -INFINITY;
 
+  const int lb = __builtin_ctz(b);  // b is a power of two
   auto addr = [&](int e) -> int64_t {  // element e of the row -> offset in S
-    const int kl = e / b, j = e % b;
+    const int kl = e >> lb, j = e & (b - 1);
     return ((zbase + k0 + kl) * b + i) * (int64_t)b + j;
   };
   auto load = [&](int e) -> f32x4 {  // scaled, masked values of entries e..e+3
@@ -70,7 +71,7 @@ __global__ __launch_bounds__(256) void k_softmax(const int32_t* __restrict__ row
       x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + addr(e)));
       x *= c;
       if (CAUSAL || am != nullptr || kp != nullptr) {
-        const int kl = e / b, j = e % b;
+        const int kl = e >> lb, j = e & (b - 1);
         const int key = col_idx[k0 + kl] * b + j;  // 4 consecutive keys in one block
         if (am != nullptr) {
           const f32x4 mv = *reinterpret_cast<const f32x4*>(am + (int64_t)q_index * Nk + key);
@@ -180,19 +181,24 @@ __global__ __launch_bounds__(256) void k_softmax_bwd(const int32_t* __restrict__
   const int k0 = row_ptr[hr], k1 = row_ptr[hr + 1];
   const int n = (k1 - k0) * b;
   const int64_t zbase = (int64_t)z * nnz;
+  const int lb = __builtin_ctz(b);  // b is a power of two
   auto addr = [&](int e) -> int64_t {
-    const int kl = e / b, j = e % b;
+    const int kl = e >> lb, j = e & (b - 1);
     return ((zbase + k0 + kl) * b + i) * (int64_t)b + j;
   };
   auto load = [&](const float* X, int e) -> f32x4 {
     return e < n ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(X + addr(e))) : f32x4{0.f, 0.f, 0.f, 0.f};
   };
   const int passes = (n + 255) / 256;
+  // up to 8 cached vectors are loaded unconditionally (zeros past the
+  // row's end), which keeps them in fixed registers (measured 3x faster on
+  // rows of 32 64-blocks than loading under p < passes); 16 are loaded
+  // under the condition (unconditional, the extra registers cost 8%)
   f32x4 cp[R], cd[R];
   float acc = 0.f;
 #pragma unroll
   for (int p = 0; p < R; ++p) {
-    if (p < passes) {
+    if (R <= 8 || p < passes) {
       const int e = p * 256 + lane * 4;
       cp[p] = load(P, e);
       cd[p] = load(dP, e);
@@ -200,6 +206,7 @@ __global__ __launch_bounds__(256) void k_softmax_bwd(const int32_t* __restrict__
       for (int q = 0; q < 4; ++q) acc = fmaf(cp[p][q], cd[p][q], acc);
     }
   }
+#pragma unroll 1
   for (int p = R; p < passes; ++p) {
     const int e = p * 256 + lane * 4;
     const f32x4 x = load(P, e), y = load(dP, e);
@@ -210,9 +217,10 @@ __global__ __launch_bounds__(256) void k_softmax_bwd(const int32_t* __restrict__
 #pragma unroll
   for (int p = 0; p < R; ++p) {
     const int e = p * 256 + lane * 4;
-    if (p < passes && e < n)
+    if ((R <= 8 || p < passes) && e < n)
       __builtin_nontemporal_store(scale * cp[p] * (cd[p] - D), reinterpret_cast<f32x4*>(dS + addr(e)));
   }
+#pragma unroll 1
   for (int p = R; p < passes; ++p) {
     const int e = p * 256 + lane * 4;
     const f32x4 x = load(P, e), y = load(dP, e);

@@ -164,3 +164,21 @@ def test_fused_backward_full_size_sampled_heads(idx):
                                                w.causal)
         for name, got, ref in (("dq", dq, refs[0]), ("dk", dk, refs[1]), ("dv", dv, refs[2])):
             assert max_abs(f64(got[sl]), ref) <= _grad_tol(dt, ref), (name, z, h)
+
+
+def test_fused_backward_empty_layout_and_empty_batch():
+    """No stored block: zero gradients (and -inf lse); Z = 0: nothing to do."""
+    b, d, H, nb = 32, 64, 2, 3
+    lay = np.zeros((H, nb, nb), np.uint8)
+    announce("fused backward empty layout")
+    L = bsa.Layout(torch.from_numpy(lay), b)
+    q, k, v, do = (to_dev(t) for t in _t([(2, H, nb * b, d)] * 4, 450, "f32"))
+    o, lse = bsa.attention(L, q, k, v, 0.125, return_lse=True)
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+    for g in bsa.attention_backward_fused(L, q, k, v, o, lse, do, 0.125):
+        assert torch.all(g == 0)
+    e = torch.empty((0, H, nb * b, d), device="cuda")
+    o0, lse0 = bsa.attention(L, e, e, e, 0.125, return_lse=True)
+    assert o0.shape == e.shape and lse0.shape == (0, H, nb * b)
+    for g in bsa.attention_backward_fused(L, e, e, e, o0, lse0, e, 0.125):
+        assert g.shape == e.shape

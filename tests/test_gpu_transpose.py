@@ -115,3 +115,19 @@ def test_transpose_flag_errors():
     assert _lib.lib().bs_sdd_ex(L.handle, p(a), p(a), p(s), 1, 64, 4, _lib.BS_F32, None) == _lib.BS_ERR_INVALID_ARG
     with pytest.raises(ValueError):
         bsa.sdd(L, a, a, trans_a=True)  # a would have to be [1, 1, K, 32]
+
+
+def test_transposed_modes_on_an_empty_layout():
+    """No stored block: SDD writes nothing, DSD and DDS write zeros."""
+    b, H, nb, Z = 16, 2, 3, 2
+    lay = np.zeros((H, nb, nb), np.uint8)
+    announce("transposed modes empty layout")
+    L = bsa.Layout(torch.from_numpy(lay), b)
+    B = to_dev(_dense((Z, H, 48, nb * b), 540, "f32"))
+    P = torch.zeros((Z, 0, b, b), device="cuda")
+    for ta in (False, True):
+        C = bsa.dsd(L, P, B, trans_a=ta, trans_b=True)
+        assert C.shape == (Z, H, nb * b, 48) and torch.all(C == 0)
+        D = bsa.dds(L, B, P, trans_a=False, trans_b=True) if not ta else bsa.dds(L, B.transpose(-1, -2).contiguous(),
+                                                                                   P, trans_a=True)
+        assert torch.all(D == 0)
