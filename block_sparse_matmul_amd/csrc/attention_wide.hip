@@ -452,7 +452,9 @@ int run(const bs_layout* L, const AttnArgs& a, float c, hipStream_t s) {
   const int Z = a.Z;
   using Cfg = WideCfg<BLK, D>;
   constexpr size_t cap = 160 * 1024;
-  constexpr int max_ns = (Cfg::bytes(4) <= cap && Cfg::merge_fits(4) && BLK * 8 <= 1024)
+  // four groups of a 128-block row would be 1024 threads, at most 128
+  // VGPRs a lane, which the causal variant exceeded (it spilled)
+  constexpr int max_ns = (Cfg::bytes(4) <= cap && Cfg::merge_fits(4) && BLK * 8 < 1024)
                              ? 4
                              : ((Cfg::bytes(2) <= cap && Cfg::merge_fits(2)) ? 2 : 1);
   const double per_cu = (double)Z * (double)L->nnz / L->num_cus;

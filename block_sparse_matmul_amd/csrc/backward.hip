@@ -269,13 +269,15 @@ __global__ __launch_bounds__(BLK * 4) void k_bwd(
     } else {
       const float* xb = &Xt[(kofs + 4 * g) * TSTR + li];
 #pragma unroll
-      for (int jt = 0; jt < NJT; ++jt)
+      for (int jt = 0; jt < NJT; ++jt) {
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
           for (int nt = 0; nt < NNT; ++nt)
             acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xb[(16 * jt + rr) * TSTR + nt * 16], w[jt][rr], acc[nt], 0,
                                                            0, 0);
+        __builtin_amdgcn_sched_barrier(0);  // bound the operands in flight (registers)
+      }
     }
   };
   // row-operand product out[jt] = X[rows][:] F[own][:]^T for the NJT tiles
@@ -295,6 +297,7 @@ __global__ __launch_bounds__(BLK * 4) void k_bwd(
           for (int e = 0; e < 4; ++e) out[jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], f[w][e], out[jt], 0, 0, 0);
         }
       }
+      if constexpr (!BF) __builtin_amdgcn_sched_barrier(0);  // fp32: bound the operands in flight (registers)
     }
   };
 

@@ -660,7 +660,13 @@ template <typename E, int BLK, int D, int MODE>
 int run(const bs_layout* L, const Args& a, hipStream_t s) {
   // largest key-group count (up to 4, and 1024 threads) whose LDS fits in 160 KiB
   constexpr size_t stage = Lds<E, BLK, D, MODE>::STAGE;
-  constexpr int max_ns = (BLK <= 64 && 4 * stage <= 160 * 1024) ? 4 : ((BLK <= 64 && 2 * stage <= 160 * 1024) ? 2 : 1);
+  // four groups of a 64-block row are 1024 threads, at most 128 VGPRs a
+  // lane: the 16-bit d = 128 attention and the masked attention need more
+  // (they spilled), so they stop at two
+  constexpr bool fits4 = !(MODE == MODE_ATTN && !std::is_same<E, float>::value && D == 128) && MODE != MODE_ATTN_MASKED;
+  constexpr int max_ns = (BLK <= 64 && 4 * stage <= 160 * 1024 && fits4)
+                             ? 4
+                             : ((BLK <= 64 && 2 * stage <= 160 * 1024) ? 2 : 1);
   const int ns = pick_key_groups(L, a.Z, max_ns, MODE == MODE_DSDT ? L->max_col_len : L->max_row_len,
                                  is_attn(MODE) ? 2.0 : 4.0);
   if constexpr (max_ns >= 4) {
