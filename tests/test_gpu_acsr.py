@@ -76,3 +76,31 @@ def test_strided_workload_acsr_path_bit_equal_to_table_path():
     Oa = bsa.attention(La, q, k, v, w.scale, w.causal)
     Od = bsa.attention(Ld, q, k, v, w.scale, w.causal)
     assert torch.equal(Oa, Od)
+
+
+@pytest.mark.parametrize("b", [16, 64])
+def test_slope1_acsr_with_masks_lse_and_fused_backward(b):
+    """The computed-column path with a key-padding mask and the row
+    log-sum-exp: the same bits as the dense layout's table path, and the
+    fused backward (which walks the tables) against the oracle."""
+    terms, nb = SLOPE1_CASES[0]
+    H, Z, d = 2, 2, 64
+    N = nb * b
+    lay = oracle.acsr_expand(terms, H, nb, nb)
+    announce("acsr masked lse backward", b)
+    q, k, v = _qkv(Z, H, N, d, 45)
+    g = torch.Generator("cpu").manual_seed(46)
+    kp = torch.randn((Z, N), generator=g)
+    kp[1, N // 2:] = -float("inf")
+    do = torch.randn((Z, H, N, d), generator=g)
+    La = bsa.Layout.acsr(terms, H, nb, nb, b)
+    Ld = bsa.Layout(torch.from_numpy(lay), b)
+    qd, kd, vd, kpd = to_dev(q), to_dev(k), to_dev(v), to_dev(kp)
+    Oa, la = bsa.attention(La, qd, kd, vd, 0.125, True, key_padding_mask=kpd, return_lse=True)
+    Od, ld = bsa.attention(Ld, qd, kd, vd, 0.125, True, key_padding_mask=kpd, return_lse=True)
+    assert torch.equal(Oa, Od) and torch.equal(la, ld)
+    assert max_abs(f64(Oa), oracle.attention_dense(q, k, v, lay, b, 0.125, True, kp_mask=kp)) <= TOL["f32"]
+    grads = bsa.attention_backward_fused(La, qd, kd, vd, Oa, la, to_dev(do), 0.125, True, key_padding_mask=kpd)
+    refs = oracle.attention_backward_dense(q, k, v, do, lay, b, 0.125, True, kp_mask=kp)
+    for name, got, ref in zip(("dq", "dk", "dv"), grads, refs):
+        assert max_abs(f64(got), ref) <= TOL["f32"], name
