@@ -8,11 +8,11 @@
 namespace bsa {
 
 int launch_attention(const bs_layout* L, const AttnArgs& at, hipStream_t s) {
-  if (at.am != nullptr || at.kp != nullptr) return launch_attention_masked(L, at, s);
   if (at.dt != BS_F32) {
     const int rc = launch_attention_wide(L, at, s);
     if (rc != kNotApplicable) return rc;
   }
+  if (at.am != nullptr || at.kp != nullptr) return launch_attention_masked(L, at, s);
   Args a{at.Q, at.K, at.V, at.O, nullptr, at.Z, at.scale * kLog2e, at.causal};
   a.use_band = L->band_off != nullptr;
   a.lse = at.lse;

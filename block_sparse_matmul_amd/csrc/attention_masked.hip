@@ -3,10 +3,9 @@
 // layout): the row-block kernel's MODE_ATTN_MASKED instantiation. After the
 // score product each lane adds log2(e) * (attn_mask[query][key] +
 // kp_mask[z][key]) to its scores (16-byte reads of 4 consecutive keys), then
-// the causal mask and the streaming softmax run as without masks. The
-// 32-rows-per-wave 16-bit kernel paces its LDS transfers by counting the
-// vector-memory operations in flight, which extra mask loads would upset,
-// so every type takes the row-block kernel here.
+// the causal mask and the streaming softmax run as without masks. The 16-bit
+// types with blocks of 32 to 128 take the 32-rows-per-wave kernel's masked
+// variant instead.
 #include "rowblock.h"
 
 namespace bsa {

@@ -72,12 +72,19 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wait_vmcnt0() { wait_vmcnt<0>(); }
 
-template <typename E, int BLK, int D, bool CAUSAL, int NS>
+// MASKED: the dense additive masks (amask [nbr*b][nbc*b], kpmask [Z][nbc*b],
+// either may be null) are read at the start of each sub-step, one 16-byte
+// vector per lane, 16-key tile and query tile, while the score product
+// runs. The transfers above are paced by counting the vector-memory
+// operations in flight; the mask reads join that count, which can only
+// make a wait wait for more (every operation completes in order), never
+// for less.
+template <typename E, int BLK, int D, bool CAUSAL, int NS, bool MASKED>
 __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, const int32_t* __restrict__ row_order,
     const int32_t* __restrict__ row_order_h, const u16* __restrict__ Q, const u16* __restrict__ K,
     const u16* __restrict__ V, u16* __restrict__ O, int Z, int H, int nbr, int nbc, float c, int grouped,
-    float* __restrict__ lse) {
+    float* __restrict__ lse, const float* __restrict__ amask, const float* __restrict__ kpmask) {
   using Cfg = WideCfg<BLK, D>;
   using HT = H16<E>;
   using V8 = typename HT::V8;
@@ -137,7 +144,9 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
   // only the sign of scale*log2(e) is folded in (exact in 16 bits)
   V8 qf[2][NQ];
   const float sgn = c > 0.f ? 1.f : (c < 0.f ? -1.f : 0.f);
-  const float cs = (c == 0.f) ? 1.f : fabsf(c);
+  const float cs_in = (c == 0.f) ? 1.f : fabsf(c);
+  // with dense masks the scores become s * |c| + log2(e) * mask (log2 units)
+  const float cs = MASKED ? 1.f : cs_in;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const u16* pq = Q + (zh * Nq + q_lo + 16 * t + li) * D + g * 8;
@@ -252,6 +261,25 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
         }
       }
       const unsigned char* const Kc = Kp[sub];
+      // dense masks of this sub-step, both query tiles (in flight during
+      // the score product)
+      f32x4 mv[MASKED ? 2 : 1][MASKED ? NJT : 1];
+      if constexpr (MASKED) {
+        if (compute) {
+          const int64_t Nk = (int64_t)nbc * BLK;
+          const int64_t key0 = (int64_t)cb * BLK + kofs + 4 * g;
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int jt = 0; jt < NJT; ++jt) {
+              f32x4 m = {0.f, 0.f, 0.f, 0.f};
+              if (amask != nullptr)
+                m = *reinterpret_cast<const f32x4*>(amask + (int64_t)(q_lo + 16 * t + li) * Nk + key0 + 16 * jt);
+              if (kpmask != nullptr) m += *reinterpret_cast<const f32x4*>(kpmask + z * Nk + key0 + 16 * jt);
+              mv[t][jt] = m;
+            }
+        }
+      }
       f32x4 s[2][NJT];
       // ---- S^T = K Q^T for both tiles
       if (compute) {
@@ -294,6 +322,12 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const int q_index = q_lo + 16 * t + li;
+          if constexpr (MASKED) {
+#pragma unroll
+            for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr) s[t][jt][rr] = fmaf(mv[t][jt][rr], kLog2eB, s[t][jt][rr] * cs_in);
+          }
           if (mask_block) {
 #pragma unroll
             for (int jt = 0; jt < NJT; ++jt)
@@ -432,14 +466,19 @@ int launch_ns(const bs_layout* L, const AttnArgs& a, float c, hipStream_t s) {
   // even a long row that starts late adds little to the end of the kernel
   const double per_slot = (double)Z * (double)L->nnz / (2.0 * L->num_cus);
   const int grouped = (4.0 * L->max_row_len / NS <= per_slot) ? 1 : 0;
-  if (a.causal)
-    hipLaunchKernelGGL((k_attn_wide<E, BLK, D, true, NS>), grid, block, 0, s, L->row_ptr, L->col_idx, L->row_order,
-                       L->row_order_h, (const u16*)Q, (const u16*)K, (const u16*)V, (u16*)O, Z, L->H, L->nbr, L->nbc,
-                       c, grouped, a.lse);
-  else
-    hipLaunchKernelGGL((k_attn_wide<E, BLK, D, false, NS>), grid, block, 0, s, L->row_ptr, L->col_idx, L->row_order,
-                       L->row_order_h, (const u16*)Q, (const u16*)K, (const u16*)V, (u16*)O, Z, L->H, L->nbr, L->nbc,
-                       c, grouped, a.lse);
+  const bool masked = a.am != nullptr || a.kp != nullptr;
+#define BSA_WIDE_LAUNCH(CA, MA)                                                                                   \
+  hipLaunchKernelGGL((k_attn_wide<E, BLK, D, CA, NS, MA>), grid, block, 0, s, L->row_ptr, L->col_idx,            \
+                     L->row_order, L->row_order_h, (const u16*)Q, (const u16*)K, (const u16*)V, (u16*)O, Z, L->H, \
+                     L->nbr, L->nbc, c, grouped, a.lse, a.am, a.kp)
+  if (a.causal) {
+    if (masked) BSA_WIDE_LAUNCH(true, true);
+    else BSA_WIDE_LAUNCH(true, false);
+  } else {
+    if (masked) BSA_WIDE_LAUNCH(false, true);
+    else BSA_WIDE_LAUNCH(false, false);
+  }
+#undef BSA_WIDE_LAUNCH
   BSA_HIP(hipGetLastError());
   return BS_OK;
 }

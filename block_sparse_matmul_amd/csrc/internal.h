@@ -158,8 +158,8 @@ int launch_dsd_rowblock(const bs_layout* L, const float* P, const void* B,
                         void* C, int Z, int Nd, bs_dtype dt, hipStream_t s);
 
 // 16-bit (bf16, fp16) fused attention on the 32-rows-per-wave kernel
-// (blocks of 32, 64, 128; no dense masks); returns kNotApplicable for other
-// blocks, head sizes or types.
+// (blocks of 32, 64, 128, with or without dense masks); returns
+// kNotApplicable for other blocks, head sizes or types.
 int launch_attention_wide(const bs_layout* L, const AttnArgs& a, hipStream_t s);
 
 bool log_enabled();
