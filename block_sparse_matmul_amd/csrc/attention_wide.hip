@@ -269,15 +269,19 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
           const int64_t Nk = (int64_t)nbc * BLK;
           const int64_t key0 = (int64_t)cb * BLK + kofs + 4 * g;
 #pragma unroll
-          for (int t = 0; t < 2; ++t)
+          for (int jt = 0; jt < NJT; ++jt) {
+            // the key-padding values depend on the key only: one read for
+            // both query tiles
+            f32x4 kpv = {0.f, 0.f, 0.f, 0.f};
+            if (kpmask != nullptr) kpv = *reinterpret_cast<const f32x4*>(kpmask + z * Nk + key0 + 16 * jt);
 #pragma unroll
-            for (int jt = 0; jt < NJT; ++jt) {
-              f32x4 m = {0.f, 0.f, 0.f, 0.f};
+            for (int t = 0; t < 2; ++t) {
+              f32x4 m = kpv;
               if (amask != nullptr)
-                m = *reinterpret_cast<const f32x4*>(amask + (int64_t)(q_lo + 16 * t + li) * Nk + key0 + 16 * jt);
-              if (kpmask != nullptr) m += *reinterpret_cast<const f32x4*>(kpmask + z * Nk + key0 + 16 * jt);
+                m += *reinterpret_cast<const f32x4*>(amask + (int64_t)(q_lo + 16 * t + li) * Nk + key0 + 16 * jt);
               mv[t][jt] = m;
             }
+          }
         }
       }
       f32x4 s[2][NJT];
