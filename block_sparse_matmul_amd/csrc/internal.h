@@ -34,7 +34,21 @@ struct bs_layout {
   // grid (own allocation; null otherwise)
   int32_t* band_off = nullptr;
   int band_n = 0;
+  // non-empty block rows grouped by softmax length class (see
+  // softmax_class), class 0 first, (head, row) order inside a class;
+  // class c is row_cls[cls_begin[c] .. cls_begin[c+1])
+  int32_t* row_cls = nullptr;  // [H*nbr] (in `mem`)
+  int cls_begin[4] = {0, 0, 0, 0};
+  int cls_max_len[3] = {0, 0, 0};  // longest row of each class (blocks)
 };
+
+// Length class of a block row of `len` blocks of edge b for the row-softmax
+// kernels, by the 16-byte vectors per lane a wave keeps of the row (256
+// floats per pass): 0 for more than 16 passes, 1 for 9 to 16, 2 for up to 8.
+inline int softmax_class(int64_t len, int b) {
+  const int64_t n = len * b;
+  return n > 16 * 256 ? 0 : (n > 8 * 256 ? 1 : 2);
+}
 
 // Workgroup -> work unit for kernels that walk a head's rows (or columns)
 // together: workgroup b runs on XCD b % 8 (round-robin dispatch), and each

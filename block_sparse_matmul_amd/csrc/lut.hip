@@ -262,8 +262,8 @@ int build_tables(bs_layout* L, const uint8_t* lay, hipStream_t s) {
   const int64_t cells = (int64_t)rows * nbc;
 
   // fixed-size tables: row_ptr, col_ptr, row_order, col_order,
-  // row_order_h, col_order_h
-  const size_t fixed = (size_t)(rows + 1) + (cols + 1) + 2 * (size_t)rows + 2 * (size_t)cols;
+  // row_order_h, col_order_h, row_cls
+  const size_t fixed = (size_t)(rows + 1) + (cols + 1) + 3 * (size_t)rows + 2 * (size_t)cols;
   // temporaries: counts, summary, two histograms, two head cursors, id map
   const size_t tmp_n = (size_t)rows + cols + SUM_N + (nbc + 2) + (nbr + 2) + 2 * (size_t)H + (size_t)cells;
   int32_t* fixed_mem = nullptr;
@@ -283,6 +283,7 @@ int build_tables(bs_layout* L, const uint8_t* lay, hipStream_t s) {
   int32_t* col_order = row_order + rows;
   int32_t* row_order_h = col_order + cols;
   int32_t* col_order_h = row_order_h + rows;
+  int32_t* row_cls = col_order_h + cols;
   int32_t* row_cnt = tmp;
   int32_t* col_cnt = row_cnt + rows;
   int32_t* summary = col_cnt + cols;
@@ -318,12 +319,34 @@ int build_tables(bs_layout* L, const uint8_t* lay, hipStream_t s) {
   BSA_TRY(hipGetLastError());
 
   int32_t sum_host[SUM_N];
+  std::vector<int32_t> rp_host((size_t)rows + 1);
   BSA_TRY(hipMemcpyAsync(sum_host, summary, sizeof(sum_host), hipMemcpyDeviceToHost, s));
+  BSA_TRY(hipMemcpyAsync(rp_host.data(), row_ptr, rp_host.size() * sizeof(int32_t), hipMemcpyDeviceToHost, s));
   BSA_TRY(hipStreamSynchronize(s));
   if (sum_host[SUM_BAD]) return cleanup(fail(BS_ERR_LAYOUT, "layout values must be 0 or 1"));
   if (sum_host[SUM_NNZ_ROWS] != sum_host[SUM_NNZ_COLS])
     return cleanup(fail(BS_ERR_HIP, "internal: row and column block counts differ"));
   const int64_t nnz = sum_host[SUM_NNZ_ROWS];
+
+  // non-empty rows grouped by softmax length class, a stable partition
+  std::vector<int32_t> cls_host;
+  cls_host.reserve(rows);
+  int cls_begin[4] = {0, 0, 0, 0}, cls_max_len[3] = {0, 0, 0};
+  for (int c = 0; c < 3; ++c) {
+    cls_begin[c] = (int)cls_host.size();
+    for (int hr = 0; hr < rows; ++hr) {
+      const int len = rp_host[hr + 1] - rp_host[hr];
+      if (len > 0 && softmax_class(len, L->block) == c) {
+        cls_host.push_back(hr);
+        cls_max_len[c] = len > cls_max_len[c] ? len : cls_max_len[c];
+      }
+    }
+  }
+  cls_begin[3] = (int)cls_host.size();
+  if (!cls_host.empty()) {
+    BSA_TRY(hipMemcpyAsync(row_cls, cls_host.data(), cls_host.size() * sizeof(int32_t), hipMemcpyHostToDevice, s));
+    BSA_TRY(hipStreamSynchronize(s));
+  }
 
   int32_t* nnz_mem = nullptr;
   if (nnz > 0) {
@@ -353,6 +376,9 @@ int build_tables(bs_layout* L, const uint8_t* lay, hipStream_t s) {
   L->nnz = nnz;
   L->max_row_len = sum_host[SUM_MAXROW];
   L->max_col_len = sum_host[SUM_MAXCOL];
+  L->row_cls = row_cls;
+  for (int c = 0; c < 4; ++c) L->cls_begin[c] = cls_begin[c];
+  for (int c = 0; c < 3; ++c) L->cls_max_len[c] = cls_max_len[c];
   L->mem = fixed_mem;
   L->row_ptr = row_ptr;
   L->col_ptr = col_ptr;

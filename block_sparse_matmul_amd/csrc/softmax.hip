@@ -11,7 +11,8 @@
 // hardware's base-2 exponential (the identity the Triton tutorial's Puzzle 8
 // uses), so the masks enter as log2(e) * mask.
 //
-// One wave per query row. The row's stored entries (len blocks x b floats,
+// One wave per query row; block rows are launched by length class (see
+// row_classes). The row's stored entries (len blocks x b floats,
 // b contiguous floats per block) are read as 16-byte vectors, 256 floats per
 // wave pass, and kept in registers (up to R vectors per lane) between the
 // max/sum pass and the write pass, so an in-register row costs one read and
@@ -44,15 +45,17 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 template <int R, bool CAUSAL>
 __global__ __launch_bounds__(256) void k_softmax(const int32_t* __restrict__ row_ptr,
-                                                 const int32_t* __restrict__ col_idx, const float* S, float* P,
+                                                 const int32_t* __restrict__ col_idx,
+                                                 const int32_t* __restrict__ rows_sel, const float* S, float* P,
                                                  int rows, int nbr, int b, int64_t nnz, float c,
                                                  const float* __restrict__ am, const float* __restrict__ kp,
                                                  int64_t Nk) {
   const int lane = threadIdx.x & 63;
-  const int qrow = blockIdx.x * 4 + (threadIdx.x >> 6);  // (h, r, i) flattened
+  const int qrow = blockIdx.x * 4 + (threadIdx.x >> 6);  // (selected block row, i) flattened
   if (qrow >= rows * b) return;
   const int z = blockIdx.y;
-  const int hr = qrow / b, i = qrow % b;
+  const int lb = __builtin_ctz(b);  // b is a power of two
+  const int hr = rows_sel[qrow >> lb], i = qrow & (b - 1);
   const int r = hr % nbr;
   const int k0 = row_ptr[hr], k1 = row_ptr[hr + 1];
   const int n = (k1 - k0) * b;  // stored entries of this row
@@ -60,7 +63,6 @@ __global__ __launch_bounds__(256) void k_softmax(const int32_t* __restrict__ row
   const int q_index = r * b + i;
   const float NEG = -INFINITY;
 
-  const int lb = __builtin_ctz(b);  // b is a power of two
   auto addr = [&](int e) -> int64_t {  // element e of the row -> offset in S
     const int kl = e >> lb, j = e & (b - 1);
     return ((zbase + k0 + kl) * b + i) * (int64_t)b + j;
@@ -149,17 +151,38 @@ __global__ __launch_bounds__(256) void k_softmax(const int32_t* __restrict__ row
 }
 
 template <int R>
-void launch_r(const bs_layout* L, const float* S, float* P, int Z, float c, bool causal, const float* am,
-              const float* kp, hipStream_t s) {
-  const int rows = L->H * L->nbr;
+void launch_r(const bs_layout* L, const int32_t* rows_sel, int rows, const float* S, float* P, int Z, float c,
+              bool causal, const float* am, const float* kp, hipStream_t s) {
   const dim3 grid((unsigned)(((int64_t)rows * L->block + 3) / 4), Z);
   const int64_t Nk = (int64_t)L->nbc * L->block;
   if (causal)
-    hipLaunchKernelGGL((k_softmax<R, true>), grid, dim3(256), 0, s, L->row_ptr, L->col_idx, S, P, rows, L->nbr,
-                       L->block, L->nnz, c, am, kp, Nk);
+    hipLaunchKernelGGL((k_softmax<R, true>), grid, dim3(256), 0, s, L->row_ptr, L->col_idx, rows_sel, S, P, rows,
+                       L->nbr, L->block, L->nnz, c, am, kp, Nk);
   else
-    hipLaunchKernelGGL((k_softmax<R, false>), grid, dim3(256), 0, s, L->row_ptr, L->col_idx, S, P, rows, L->nbr,
-                       L->block, L->nnz, c, am, kp, Nk);
+    hipLaunchKernelGGL((k_softmax<R, false>), grid, dim3(256), 0, s, L->row_ptr, L->col_idx, rows_sel, S, P, rows,
+                       L->nbr, L->block, L->nnz, c, am, kp, Nk);
+}
+
+// Block rows by length class. The number of vectors a wave keeps in
+// registers (R) sets the kernel's registers and so its occupancy, and one
+// long row would otherwise set R for every row: rows of up to 8 cached
+// vectors per lane run at 8 waves per SIMD, 16 at 4, 32 at 3. Each class
+// (softmax_class; a range of the layout's row_cls table) gets its own
+// launch, the longest class first. Inside a class the rows keep their
+// (head, row) order, which reads S and writes P in address order (measured
+// faster than longest first). Rows without blocks are not launched (they
+// have nothing to write).
+struct RowClass {
+  int begin, end, r;  // range in row_cls, cached vectors per lane
+};
+static int row_classes(const bs_layout* L, RowClass out[3]) {
+  int n = 0;
+  const int* cb = L->cls_begin;
+  if (cb[1] > cb[0]) out[n++] = {cb[0], cb[1], 32};
+  if (cb[2] > cb[1]) out[n++] = {cb[1], cb[2], 16};
+  // the short class caches 4 vectors when none of its rows needs more
+  if (cb[3] > cb[2]) out[n++] = {cb[2], cb[3], (int64_t)L->cls_max_len[2] * L->block > 4 * 256 ? 8 : 4};
+  return n;
 }
 
 // Gradient of the softmax above with respect to its input S, given P and
@@ -170,18 +193,19 @@ void launch_r(const bs_layout* L, const float* S, float* P, int Z, float c, bool
 // again. dS may alias dP (or P): every vector is read before the same lanes
 // write it.
 template <int R>
-__global__ __launch_bounds__(256) void k_softmax_bwd(const int32_t* __restrict__ row_ptr, const float* P,
+__global__ __launch_bounds__(256) void k_softmax_bwd(const int32_t* __restrict__ row_ptr,
+                                                     const int32_t* __restrict__ rows_sel, const float* P,
                                                      const float* dP, float* dS, int rows, int b, int64_t nnz,
                                                      float scale) {
   const int lane = threadIdx.x & 63;
-  const int qrow = blockIdx.x * 4 + (threadIdx.x >> 6);  // (h, r, i) flattened
+  const int qrow = blockIdx.x * 4 + (threadIdx.x >> 6);  // (selected block row, i) flattened
   if (qrow >= rows * b) return;
   const int z = blockIdx.y;
-  const int hr = qrow / b, i = qrow % b;
+  const int lb = __builtin_ctz(b);  // b is a power of two
+  const int hr = rows_sel[qrow >> lb], i = qrow & (b - 1);
   const int k0 = row_ptr[hr], k1 = row_ptr[hr + 1];
   const int n = (k1 - k0) * b;
   const int64_t zbase = (int64_t)z * nnz;
-  const int lb = __builtin_ctz(b);  // b is a power of two
   auto addr = [&](int e) -> int64_t {
     const int kl = e >> lb, j = e & (b - 1);
     return ((zbase + k0 + kl) * b + i) * (int64_t)b + j;
@@ -229,40 +253,52 @@ __global__ __launch_bounds__(256) void k_softmax_bwd(const int32_t* __restrict__
 }
 
 template <int R>
-void launch_bwd_r(const bs_layout* L, const float* P, const float* dP, float* dS, int Z, float scale, hipStream_t s) {
-  const int rows = L->H * L->nbr;
+void launch_bwd_r(const bs_layout* L, const int32_t* rows_sel, int rows, const float* P, const float* dP, float* dS,
+                  int Z, float scale, hipStream_t s) {
   const dim3 grid((unsigned)(((int64_t)rows * L->block + 3) / 4), Z);
-  hipLaunchKernelGGL((k_softmax_bwd<R>), grid, dim3(256), 0, s, L->row_ptr, P, dP, dS, rows, L->block, L->nnz,
-                     scale);
+  hipLaunchKernelGGL((k_softmax_bwd<R>), grid, dim3(256), 0, s, L->row_ptr, rows_sel, P, dP, dS, rows, L->block,
+                     L->nnz, scale);
 }
 
 }  // namespace
 
+// The gradient caches two vectors (P and dP) per entry, so its longest
+// class keeps 16 of each and reads longer rows again.
 int launch_softmax_backward(const bs_layout* L, const float* P, const float* dP, float* dS, int Z, float scale,
                             hipStream_t s) {
-  const int64_t longest = (int64_t)L->max_row_len * L->block;
-  if (longest <= 4 * 256)
-    launch_bwd_r<4>(L, P, dP, dS, Z, scale, s);
-  else if (longest <= 8 * 256)
-    launch_bwd_r<8>(L, P, dP, dS, Z, scale, s);
-  else
-    launch_bwd_r<16>(L, P, dP, dS, Z, scale, s);
+  RowClass cls[3];
+  const int n = row_classes(L, cls);
+  for (int k = 0; k < n; ++k) {
+    const int32_t* sel = L->row_cls + cls[k].begin;
+    const int rows = cls[k].end - cls[k].begin;
+    if (cls[k].r == 4)
+      launch_bwd_r<4>(L, sel, rows, P, dP, dS, Z, scale, s);
+    else if (cls[k].r == 8)
+      launch_bwd_r<8>(L, sel, rows, P, dP, dS, Z, scale, s);
+    else
+      launch_bwd_r<16>(L, sel, rows, P, dP, dS, Z, scale, s);
+  }
   BSA_HIP(hipGetLastError());
   return BS_OK;
 }
 
 int launch_softmax(const bs_layout* L, const float* S, float* P, int Z, float scale, bool causal, const float* am,
                    const float* kp, hipStream_t s) {
-  const int64_t longest = (int64_t)L->max_row_len * L->block;  // floats in the longest row
   const float c = scale * kLog2e;
-  if (longest <= 4 * 256)
-    launch_r<4>(L, S, P, Z, c, causal, am, kp, s);
-  else if (longest <= 8 * 256)
-    launch_r<8>(L, S, P, Z, c, causal, am, kp, s);
-  else if (longest <= 16 * 256)
-    launch_r<16>(L, S, P, Z, c, causal, am, kp, s);
-  else
-    launch_r<32>(L, S, P, Z, c, causal, am, kp, s);
+  RowClass cls[3];
+  const int n = row_classes(L, cls);
+  for (int k = 0; k < n; ++k) {
+    const int32_t* sel = L->row_cls + cls[k].begin;
+    const int rows = cls[k].end - cls[k].begin;
+    if (cls[k].r == 4)
+      launch_r<4>(L, sel, rows, S, P, Z, c, causal, am, kp, s);
+    else if (cls[k].r == 8)
+      launch_r<8>(L, sel, rows, S, P, Z, c, causal, am, kp, s);
+    else if (cls[k].r == 16)
+      launch_r<16>(L, sel, rows, S, P, Z, c, causal, am, kp, s);
+    else
+      launch_r<32>(L, sel, rows, S, P, Z, c, causal, am, kp, s);
+  }
   BSA_HIP(hipGetLastError());
   return BS_OK;
 }

@@ -140,6 +140,41 @@ def test_softmax_in_place_and_long_rows():
     assert max_abs(f64(P), oracle.softmax(S, lay, 16, 0.5)) <= TOL["f32"]
 
 
+def _length_class_layout(b, seed):
+    """Block rows of every register-cache class of the softmax (up to 8, 16
+    and more than 16 cached vectors per lane, i.e. 8*256/b, 16*256/b and
+    longer rows), some empty, interleaved over heads and rows: a
+    lower-triangular grid of 1.25*16*256/b block rows with rows thinned at
+    random and two rows emptied."""
+    nb = (16 * 256 // b) * 5 // 4
+    rng = np.random.default_rng(seed)
+    lay = np.tril(np.ones((2, nb, nb), np.uint8))
+    lay &= (rng.random((2, nb, nb)) < rng.uniform(0.3, 1.0, (2, nb, 1))).astype(np.uint8)
+    lay[0, nb - 1, :] = 1          # the longest row possible
+    lay[0, nb // 2, :] = 0         # empty rows
+    lay[1, nb - 3, :] = 0
+    return lay
+
+
+@pytest.mark.parametrize("b", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_softmax_length_classes(b, causal):
+    lay = _length_class_layout(b, 40 + b)
+    lens = lay.sum(axis=2)
+    assert lens.max() * b > 16 * 256 and ((lens > 0) & (lens * b <= 8 * 256)).any()
+    assert ((lens * b > 8 * 256) & (lens * b <= 16 * 256)).any()
+    nnz = int(lay.sum())
+    announce("softmax length classes", b, causal)
+    (S,) = _tensors([(2, nnz, b, b)], 41, "f32")
+    L = bsa.Layout(torch.from_numpy(lay), b)
+    P = bsa.softmax(L, to_dev(S), 0.4, causal)
+    ref = oracle.softmax(S, lay, b, 0.4, causal)
+    assert max_abs(f64(P), ref) <= TOL["f32"]
+    dP = _tensors([(2, nnz, b, b)], 42, "f32")[0]
+    dS = bsa.softmax_backward(L, P, to_dev(dP), 0.4)
+    assert max_abs(f64(dS), oracle.softmax_backward(f64(P), dP, lay, b, 0.4)) <= TOL["f32"]
+
+
 # --------------------------------------------------------------- DSD / DDS
 
 # Nd of 64 and 128 take the LDS-staged row-block kernel, other Nd the generic one
