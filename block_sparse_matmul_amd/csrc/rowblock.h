@@ -124,7 +124,8 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_rowblock(
     const typename Elem<E>::storage* __restrict__ V, typename Elem<E>::storage* __restrict__ O,
     float* __restrict__ S, const int32_t* __restrict__ blk_id, const int32_t* __restrict__ band, int band_n, int Z,
     int H, int nbr, int nbc, int64_t nnz, float c, const float* __restrict__ amask,
-    const float* __restrict__ kpmask, float* __restrict__ lse) {
+    const float* __restrict__ kpmask, float* __restrict__ lse, const int32_t* __restrict__ row_order_h,
+    int grouped) {
   using St = typename Elem<E>::storage;
   using Vec = typename Cfg<E>::Vec;
   constexpr bool BF = !std::is_same<E, float>::value;  // a 16-bit element type (bf16, fp16)
@@ -169,8 +170,21 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_rowblock(
   St* const Kg = Ks + sg * KBUF;
   St* const Vg = Vs + sg * VBUF;
   const int li = lane & 15, g = lane >> 4;
-  const int hr = row_order[blockIdx.x / Z];
-  const int z = blockIdx.x % Z;
+  // Which block row: with `grouped`, XCD-aware and grouped by (batch, head),
+  // the head's rows longest first (the head's K or V blocks, which its rows
+  // read again and again, stay in the XCD's L2 while its rows are in
+  // flight); otherwise longest first across the whole job, batch index
+  // fastest (the long rows start first).
+  int hr, z;
+  if (grouped) {
+    const int unit = xcd_unit(blockIdx.x, gridDim.x);
+    const int zhu = unit / nbr;
+    z = zhu / H;
+    hr = row_order_h[(zhu % H) * nbr + unit % nbr];
+  } else {
+    hr = row_order[blockIdx.x / Z];
+    z = blockIdx.x % Z;
+  }
   const int h = hr / nbr, r = hr % nbr;
   // The row's blocks: positions k0..k1-1 of the column table, or, for a
   // slope-1 ACSR layout (band != null, attention only), columns r + band[i]
@@ -623,6 +637,16 @@ int launch_ns(const bs_layout* L, const Args& a, hipStream_t s) {
   const int32_t* ptr = T ? L->col_ptr : L->row_ptr;
   const int32_t* idx = T ? L->row_idx : L->col_idx;
   const int32_t* order = T ? L->col_order : L->row_order;
+  const int32_t* order_h = T ? L->col_order_h : L->row_order_h;
+  // head-grouped XCD order for the SDD and DSD modes with 16-bit operands
+  // and rows (columns) of similar length: the longest, split over the NS
+  // groups, is at most a quarter of a workgroup slot's share (two slots per
+  // CU). Measured on random_b128_bf16: SDD +16%, DSD +5%; the fp32 workloads
+  // ran up to 55% slower with it (their longest-first order already reuses
+  // K or V across heads), so they keep longest first.
+  const double per_slot = (double)a.Z * (double)L->nnz / (2.0 * L->num_cus);
+  const int max_len = T ? L->max_col_len : L->max_row_len;
+  const int grouped = (!is_attn(MODE) && !std::is_same<E, float>::value && 4.0 * max_len / NS <= per_slot) ? 1 : 0;
   const int32_t* bid = T ? L->blk_id : nullptr;
   const int nb_out = T ? L->nbc : L->nbr, nb_in = T ? L->nbr : L->nbc;
   // the fused kernel computes slope-1 ACSR columns (the other modes index S by
@@ -632,11 +656,11 @@ int launch_ns(const bs_layout* L, const Args& a, hipStream_t s) {
   if (is_attn(MODE) && a.causal)
     hipLaunchKernelGGL((k_rowblock<E, BLK, D, true, NS, MODE>), grid, block, 0, s, ptr, idx, order, (const St*)a.Q,
                        (const St*)a.K, (const St*)a.V, (St*)a.O, a.S, bid, band, band_n, a.Z, L->H, nb_out, nb_in,
-                       L->nnz, a.c, a.am, a.kp, a.lse);
+                       L->nnz, a.c, a.am, a.kp, a.lse, order_h, grouped);
   else
     hipLaunchKernelGGL((k_rowblock<E, BLK, D, false, NS, MODE>), grid, block, 0, s, ptr, idx, order,
                        (const St*)a.Q, (const St*)a.K, (const St*)a.V, (St*)a.O, a.S, bid, band, band_n, a.Z, L->H,
-                       nb_out, nb_in, L->nnz, a.c, a.am, a.kp, a.lse);
+                       nb_out, nb_in, L->nnz, a.c, a.am, a.kp, a.lse, order_h, grouped);
   BSA_HIP(hipGetLastError());
   return BS_OK;
 }
