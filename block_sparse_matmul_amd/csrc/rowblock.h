@@ -145,6 +145,9 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_rowblock(
   constexpr int NSUB = BLK / KS;
   constexpr int NJT = KS / 16;             // 16-key tiles per sub-step
   constexpr int NNT = D / 16;              // 16-column tiles of O
+  // DSD with two sub-steps per block: P of the next sub-step is loaded one
+  // sub-step ahead into the other of two register sets
+  constexpr bool PFP = MODE == MODE_DSD && NSUB == 2 && BF;
   constexpr int KSTR = Lds<E, BLK, D, MODE>::KSTR;
   constexpr int VSTR = Lds<E, BLK, D, MODE>::VSTR;
   constexpr int KBUF = Lds<E, BLK, D, MODE>::KBUF, VBUF = Lds<E, BLK, D, MODE>::VBUF;
@@ -280,6 +283,17 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_rowblock(
     if constexpr (HASV) stage_store_from(HASK ? stv : stg, Vg, voff);
   };
 
+  // PFP: P of sub-step x of stored block kk in the score-register layout
+  // (this lane: query wave*16 + li, keys 64x + 16 jt + 4 g + rr)
+  f32x4 pset[PFP ? 2 : 1][PFP ? NJT : 1];
+  auto load_p = [&](int kk, int x, f32x4 (&dst)[PFP ? NJT : 1]) {
+    if constexpr (PFP) {
+      const float* src = S + ((int64_t)z * nnz + kk) * (BLK * BLK) + s_lane + x * KS;
+#pragma unroll
+      for (int jt = 0; jt < NJT; ++jt) dst[jt] = *reinterpret_cast<const f32x4*>(src + 16 * jt);
+    }
+  };
+
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 o[HASV ? NNT : 1];
 #pragma unroll
@@ -302,6 +316,12 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_rowblock(
     }
   }
   if constexpr (SPLIT) __syncthreads();
+  if constexpr (PFP) {
+    if (k0 + sg < k1) load_p(k0 + sg, 0, pset[0]);
+    // the loads so far have arrived before the loop, so that the compiler's
+    // waits inside it count only the loads of the loop
+    __builtin_amdgcn_s_waitcnt(kVmcntZero);
+  }
   for (int step = 0; step < nsteps; ++step) {
     const int kk = k0 + step * NS + sg;
     const bool valid = kk < k1;
@@ -311,7 +331,14 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_rowblock(
       __syncthreads();  // every wave is done with the previous blocks in LDS
       if (valid) store_next();
       __syncthreads();
-      if (has_next) load_next(cb_next);
+      if constexpr (PFP) {
+        // issued on every step, a block of this row standing in when there is
+        // no next one (never stored: the next step is not valid), so that
+        // the compiler counts the same loads on every path
+        load_next(has_next ? cb_next : col_of(valid ? kk : k0));
+      } else if (has_next) {
+        load_next(cb_next);
+      }
     } else {
       if (has_next) stage_load_to(stg, Kz, cb_next);
     }
@@ -408,7 +435,18 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_rowblock(
             for (int rr = 0; rr < 4; ++rr) s[jt][rr] = st_blk[(int64_t)(kofs + 16 * jt + rr) * BLK];
         }
       }
-      if constexpr (MODE == MODE_DSD) {
+      if constexpr (PFP) {
+        // P of the other sub-step into the other set (this block's second
+        // half, then the next block's first half, a block of this row
+        // standing in past the end), then this sub-step's P, loaded one
+        // sub-step ago
+        if (sub == 0) load_p(valid ? kk : k0, 1, pset[1]);
+        else load_p(has_next ? kk + NS : k0, 0, pset[0]);
+        if (compute) {
+#pragma unroll
+          for (int jt = 0; jt < NJT; ++jt) s[jt] = pset[sub][jt];
+        }
+      } else if constexpr (MODE == MODE_DSD) {
         // P block rows straight into the score-register layout
         if (compute) {
 #pragma unroll

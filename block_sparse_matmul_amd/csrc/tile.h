@@ -32,6 +32,11 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef uint16_t u16;
+
+// s_waitcnt immediate (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8) that waits for every vector-memory operation and
+// leaves the other counters at "no wait"
+constexpr int kVmcntZero = (7 << 4) | (15 << 8);
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
