@@ -11,6 +11,8 @@
 
 // Device-resident tables of one layout. One allocation (`mem`) holds every
 // array; all are int32.
+constexpr int kSoftmaxClasses = 4;  // see softmax_class
+
 struct bs_layout {
   int device = 0;
   int num_cus = 256;  // compute units of the device (scheduling heuristics)
@@ -38,16 +40,17 @@ struct bs_layout {
   // softmax_class), class 0 first, (head, row) order inside a class;
   // class c is row_cls[cls_begin[c] .. cls_begin[c+1])
   int32_t* row_cls = nullptr;  // [H*nbr] (in `mem`)
-  int cls_begin[4] = {0, 0, 0, 0};
-  int cls_max_len[3] = {0, 0, 0};  // longest row of each class (blocks)
+  int cls_begin[kSoftmaxClasses + 1] = {};
+  int cls_max_len[kSoftmaxClasses] = {};  // longest row of each class (blocks)
 };
 
 // Length class of a block row of `len` blocks of edge b for the row-softmax
 // kernels, by the 16-byte vectors per lane a wave keeps of the row (256
-// floats per pass): 0 for more than 16 passes, 1 for 9 to 16, 2 for up to 8.
+// floats per pass): 0 for more than 20 passes, 1 for 17 to 20, 2 for 9 to
+// 16, 3 for up to 8.
 inline int softmax_class(int64_t len, int b) {
   const int64_t n = len * b;
-  return n > 16 * 256 ? 0 : (n > 8 * 256 ? 1 : 2);
+  return n > 20 * 256 ? 0 : (n > 16 * 256 ? 1 : (n > 8 * 256 ? 2 : 3));
 }
 
 // Workgroup -> work unit for kernels that walk a head's rows (or columns)

@@ -331,8 +331,8 @@ int build_tables(bs_layout* L, const uint8_t* lay, hipStream_t s) {
   // non-empty rows grouped by softmax length class, a stable partition
   std::vector<int32_t> cls_host;
   cls_host.reserve(rows);
-  int cls_begin[4] = {0, 0, 0, 0}, cls_max_len[3] = {0, 0, 0};
-  for (int c = 0; c < 3; ++c) {
+  int cls_begin[kSoftmaxClasses + 1] = {}, cls_max_len[kSoftmaxClasses] = {};
+  for (int c = 0; c < kSoftmaxClasses; ++c) {
     cls_begin[c] = (int)cls_host.size();
     for (int hr = 0; hr < rows; ++hr) {
       const int len = rp_host[hr + 1] - rp_host[hr];
@@ -342,7 +342,7 @@ int build_tables(bs_layout* L, const uint8_t* lay, hipStream_t s) {
       }
     }
   }
-  cls_begin[3] = (int)cls_host.size();
+  cls_begin[kSoftmaxClasses] = (int)cls_host.size();
   if (!cls_host.empty()) {
     BSA_TRY(hipMemcpyAsync(row_cls, cls_host.data(), cls_host.size() * sizeof(int32_t), hipMemcpyHostToDevice, s));
     BSA_TRY(hipStreamSynchronize(s));
@@ -377,8 +377,8 @@ int build_tables(bs_layout* L, const uint8_t* lay, hipStream_t s) {
   L->max_row_len = sum_host[SUM_MAXROW];
   L->max_col_len = sum_host[SUM_MAXCOL];
   L->row_cls = row_cls;
-  for (int c = 0; c < 4; ++c) L->cls_begin[c] = cls_begin[c];
-  for (int c = 0; c < 3; ++c) L->cls_max_len[c] = cls_max_len[c];
+  for (int c = 0; c <= kSoftmaxClasses; ++c) L->cls_begin[c] = cls_begin[c];
+  for (int c = 0; c < kSoftmaxClasses; ++c) L->cls_max_len[c] = cls_max_len[c];
   L->mem = fixed_mem;
   L->row_ptr = row_ptr;
   L->col_ptr = col_ptr;

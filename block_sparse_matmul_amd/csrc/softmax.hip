@@ -166,8 +166,8 @@ void launch_r(const bs_layout* L, const int32_t* rows_sel, int rows, const float
 // Block rows by length class. The number of vectors a wave keeps in
 // registers (R) sets the kernel's registers and so its occupancy, and one
 // long row would otherwise set R for every row: rows of up to 8 cached
-// vectors per lane run at 8 waves per SIMD, 16 at 4, 32 at 3. Each class
-// (softmax_class; a range of the layout's row_cls table) gets its own
+// vectors per lane run at 8 waves per SIMD, 16 and 20 at 4, 32 at 3. Each
+// class (softmax_class; a range of the layout's row_cls table) gets its own
 // launch, the longest class first. Inside a class the rows keep their
 // (head, row) order, which reads S and writes P in address order (measured
 // faster than longest first). Rows without blocks are not launched (they
@@ -175,13 +175,13 @@ void launch_r(const bs_layout* L, const int32_t* rows_sel, int rows, const float
 struct RowClass {
   int begin, end, r;  // range in row_cls, cached vectors per lane
 };
-static int row_classes(const bs_layout* L, RowClass out[3]) {
-  int n = 0;
-  const int* cb = L->cls_begin;
-  if (cb[1] > cb[0]) out[n++] = {cb[0], cb[1], 32};
-  if (cb[2] > cb[1]) out[n++] = {cb[1], cb[2], 16};
+static int row_classes(const bs_layout* L, RowClass out[kSoftmaxClasses]) {
   // the short class caches 4 vectors when none of its rows needs more
-  if (cb[3] > cb[2]) out[n++] = {cb[2], cb[3], (int64_t)L->cls_max_len[2] * L->block > 4 * 256 ? 8 : 4};
+  const int r_short = (int64_t)L->cls_max_len[3] * L->block > 4 * 256 ? 8 : 4;
+  const int rs[kSoftmaxClasses] = {32, 20, 16, r_short};
+  int n = 0;
+  for (int c = 0; c < kSoftmaxClasses; ++c)
+    if (L->cls_begin[c + 1] > L->cls_begin[c]) out[n++] = {L->cls_begin[c], L->cls_begin[c + 1], rs[c]};
   return n;
 }
 
@@ -266,8 +266,17 @@ void launch_bwd_r(const bs_layout* L, const int32_t* rows_sel, int rows, const f
 // class keeps 16 of each and reads longer rows again.
 int launch_softmax_backward(const bs_layout* L, const float* P, const float* dP, float* dS, int Z, float scale,
                             hipStream_t s) {
-  RowClass cls[3];
-  const int n = row_classes(L, cls);
+  RowClass cls[kSoftmaxClasses];
+  int n = row_classes(L, cls);
+  // at most 16 cached vectors each: adjacent classes (contiguous in row_cls)
+  // that end up with the same count share one launch
+  int m = 0;
+  for (int k = 0; k < n; ++k) {
+    cls[k].r = cls[k].r > 16 ? 16 : cls[k].r;
+    if (m > 0 && cls[m - 1].r == cls[k].r && cls[m - 1].end == cls[k].begin) cls[m - 1].end = cls[k].end;
+    else cls[m++] = cls[k];
+  }
+  n = m;
   for (int k = 0; k < n; ++k) {
     const int32_t* sel = L->row_cls + cls[k].begin;
     const int rows = cls[k].end - cls[k].begin;
@@ -285,7 +294,7 @@ int launch_softmax_backward(const bs_layout* L, const float* P, const float* dP,
 int launch_softmax(const bs_layout* L, const float* S, float* P, int Z, float scale, bool causal, const float* am,
                    const float* kp, hipStream_t s) {
   const float c = scale * kLog2e;
-  RowClass cls[3];
+  RowClass cls[kSoftmaxClasses];
   const int n = row_classes(L, cls);
   for (int k = 0; k < n; ++k) {
     const int32_t* sel = L->row_cls + cls[k].begin;
@@ -296,6 +305,8 @@ int launch_softmax(const bs_layout* L, const float* S, float* P, int Z, float sc
       launch_r<8>(L, sel, rows, S, P, Z, c, causal, am, kp, s);
     else if (cls[k].r == 16)
       launch_r<16>(L, sel, rows, S, P, Z, c, causal, am, kp, s);
+    else if (cls[k].r == 20)
+      launch_r<20>(L, sel, rows, S, P, Z, c, causal, am, kp, s);
     else
       launch_r<32>(L, sel, rows, S, P, Z, c, causal, am, kp, s);
   }

@@ -141,12 +141,12 @@ def test_softmax_in_place_and_long_rows():
 
 
 def _length_class_layout(b, seed):
-    """Block rows of every register-cache class of the softmax (up to 8, 16
-    and more than 16 cached vectors per lane, i.e. 8*256/b, 16*256/b and
-    longer rows), some empty, interleaved over heads and rows: a
-    lower-triangular grid of 1.25*16*256/b block rows with rows thinned at
-    random and two rows emptied."""
-    nb = (16 * 256 // b) * 5 // 4
+    """Block rows of every register-cache class of the softmax (up to 8, 16,
+    20 and more than 20 cached vectors per lane, i.e. 8*256/b, 16*256/b,
+    20*256/b blocks and longer rows), some empty, interleaved over heads and
+    rows: a lower-triangular grid of 1.25*20*256/b block rows with rows
+    thinned at random and two rows emptied."""
+    nb = (20 * 256 // b) * 5 // 4
     rng = np.random.default_rng(seed)
     lay = np.tril(np.ones((2, nb, nb), np.uint8))
     lay &= (rng.random((2, nb, nb)) < rng.uniform(0.3, 1.0, (2, nb, 1))).astype(np.uint8)
@@ -161,8 +161,9 @@ def _length_class_layout(b, seed):
 def test_softmax_length_classes(b, causal):
     lay = _length_class_layout(b, 40 + b)
     lens = lay.sum(axis=2)
-    assert lens.max() * b > 16 * 256 and ((lens > 0) & (lens * b <= 8 * 256)).any()
+    assert lens.max() * b > 20 * 256 and ((lens > 0) & (lens * b <= 8 * 256)).any()
     assert ((lens * b > 8 * 256) & (lens * b <= 16 * 256)).any()
+    assert ((lens * b > 16 * 256) & (lens * b <= 20 * 256)).any()
     nnz = int(lay.sum())
     announce("softmax length classes", b, causal)
     (S,) = _tensors([(2, nnz, b, b)], 41, "f32")
