@@ -399,18 +399,19 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_rowblock(
         if (compute) {
           if constexpr (BLK <= 64) {
             // written once: streaming stores, 16 rows x 64 bytes per
-            // instruction (measured faster than plain stores up to
-            // 64-blocks, slower at 128)
+            // instruction (the lane exchange below measured 4-11% slower
+            // here)
 #pragma unroll
             for (int jt = 0; jt < NJT; ++jt)
               __builtin_nontemporal_store(s[jt], reinterpret_cast<f32x4*>(s_blk + kofs + 16 * jt));
           } else {
-            // 128-blocks: tiles 2jp and 2jp + 1 as two stores of 8 rows x 32
-            // keys, whole 128-byte lines: lanes li and li ^ 8 swap one tile
-            // (lane li < 8 keeps row li's first 16 keys and takes row li + 8's;
-            // lane li >= 8 keeps row li's last 16 and takes row li - 8's).
-            // Measured on random_b128_bf16: 1.86 against 2.08 ms with 16 rows
-            // x 64 bytes per instruction.
+            // 128-blocks: tiles 2jp and 2jp + 1 as two streaming stores of 8
+            // rows x 32 keys, whole 128-byte lines: lanes li and li ^ 8 swap
+            // one tile (lane li < 8 keeps row li's first 16 keys and takes row
+            // li + 8's; lane li >= 8 keeps row li's last 16 and takes row
+            // li - 8's). Measured on random_b128_bf16: 1.73 ms, against 1.84
+            // with plain stores of the same lines and 2.08 with plain stores
+            // of 16 rows x 64 bytes (streaming stores of those: 2.9).
             const bool lo = li < 8;
             float* const s_w = s_blk - (int64_t)li * BLK;  // row wave*16 of the block, column 4g
             const int row = li & 7;
@@ -420,8 +421,8 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_rowblock(
               const f32x4 x = lo ? b : a;
               const f32x4 y = {__shfl_xor(x[0], 8), __shfl_xor(x[1], 8), __shfl_xor(x[2], 8), __shfl_xor(x[3], 8)};
               const int col = kofs + 32 * jp + (lo ? 0 : 16);
-              *reinterpret_cast<f32x4*>(s_w + (int64_t)row * BLK + col) = lo ? a : y;
-              *reinterpret_cast<f32x4*>(s_w + (int64_t)(row + 8) * BLK + col) = lo ? y : b;
+              __builtin_nontemporal_store(lo ? a : y, reinterpret_cast<f32x4*>(s_w + (int64_t)row * BLK + col));
+              __builtin_nontemporal_store(lo ? y : b, reinterpret_cast<f32x4*>(s_w + (int64_t)(row + 8) * BLK + col));
             }
           }
         }
