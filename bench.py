@@ -108,21 +108,27 @@ def cpu_baseline(w, lay, q, k, v, budget_s=12.0, seed=0):
     lens = lay.sum(axis=2)
     # the oracle converts its inputs to float64 once per call; hand it the
     # per-head slices it needs so the sample measures the arithmetic
+    # block rows in a seeded order until the budget is spent; a workload
+    # that finishes sooner is run again from the start
     done_blocks, n_rows = 0, 0
     t0 = time.perf_counter()
-    for i in order:
-        z, h, r = rows[i]
-        oracle.attention_blockrow(q[z:z + 1, h:h + 1], k[z:z + 1, h:h + 1], v[z:z + 1, h:h + 1],
-                                  lay[h:h + 1], w.block, w.scale, w.causal, 0, 0, r)
-        done_blocks += int(lens[h, r])
-        n_rows += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
+    while time.perf_counter() - t0 <= budget_s:
+        for i in order:
+            z, h, r = rows[i]
+            oracle.attention_blockrow(q[z:z + 1, h:h + 1], k[z:z + 1, h:h + 1], v[z:z + 1, h:h + 1],
+                                      lay[h:h + 1], w.block, w.scale, w.causal, 0, 0, r)
+            done_blocks += int(lens[h, r])
+            n_rows += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
     el = time.perf_counter() - t0
     flops = 4 * w.block * w.block * w.d * done_blocks
+    if n_rows <= len(rows):
+        what = f"{n_rows} of {len(rows)} block rows of {w.name}"
+    else:
+        what = f"{n_rows} block-row evaluations, {n_rows / len(rows):.1f} passes over the {len(rows)} block rows of {w.name}"
     return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{n_rows} of {len(rows)} block rows of {w.name} ({done_blocks} stored blocks), "
-                      f"oracle per-block route in float64 numpy, {el:.1f} s"}
+            "sample": f"{what} ({done_blocks} stored blocks), oracle per-block route in float64 numpy, {el:.1f} s"}
 
 
 def run_workload(w, steps, warmup, with_ops=True, with_cpu=True):
