@@ -4,7 +4,9 @@
 
 One step is one fused block-sparse attention call (SDD -> block-sparse
 softmax -> DSD in the fused kernel) over the whole workload, inputs already
-resident in HBM and the layout tables built once beforehand. The value is
+resident in HBM and the layout tables built once beforehand. The default
+workload is the largest, random_b128_bf16 (Z=1, H=32, N=16384, d=128,
+128-blocks, per-head random layouts of density 0.25, bf16 operands). The value is
 TFLOP/s over the stored blocks only (4 b^2 d flops per stored block per batch
 element). Rank 0 prints one JSON line with, besides the contract fields:
   roofline      the fused kernel's achieved TFLOP/s against the MFMA peak of
@@ -16,7 +18,10 @@ element). Rank 0 prints one JSON line with, besides the contract fields:
                 host's cores on a bounded sample of block rows
   ops           the unfused three-call path (SDD, softmax, DSD), the
                 standalone DDS where the workload has one, and the one-time
-                layout build, each timed on its own
+                layout build, each timed on its own after two untimed calls
+  fused_other_workloads
+                the fused kernel's time, TFLOP/s and roofline fraction on
+                each of the other workloads
 Other modes:
   --calibrate-copy   a plain 1 GiB device copy (for scaling HBM counters)
   --all              also print one line per workload to stderr
@@ -36,7 +41,7 @@ sys.path.insert(0, ROOT)
 METRIC = "block-sparse attention TFLOP/s on nnz blocks + % of MFMA peak, 1 MI355X"
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}   # MI355X dense MFMA
 HBM_PEAK_GBS = 8000.0
-DEFAULT_WORKLOAD = "causal_b64"
+DEFAULT_WORKLOAD = "random_b128_bf16"
 
 
 def _events_time(fn, n, stream):
@@ -91,17 +96,31 @@ def attention_flops(nnz, Z, block, d):
     return 4 * block * block * d * nnz * Z
 
 
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, lay, q, k, v, budget_s=12.0, seed=0):
     """The oracle's per-block route on a seeded random sample of block rows,
-    for about budget_s seconds of CPU time; TFLOP/s over the sampled rows'
-    stored blocks."""
+    for about budget_s seconds of wall time; TFLOP/s over the sampled rows'
+    stored blocks. `cores` is the number of threads the sample kept busy on
+    average (process CPU time over wall time, rounded up), next to the
+    host's cores, its CPU model and the size of numpy's BLAS thread pool."""
+    import math
     import numpy as np
     import oracle
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+                           or [1])
     except Exception:  # pragma: no cover
-        cores = 1
+        blas_threads = None
     rng = np.random.default_rng(seed)
     rows = [(z, h, r) for z in range(w.Z) for h in range(w.H) for r in range(w.nb)]
     order = rng.permutation(len(rows))
@@ -111,6 +130,7 @@ def cpu_baseline(w, lay, q, k, v, budget_s=12.0, seed=0):
     # block rows in a seeded order until the budget is spent; a workload
     # that finishes sooner is run again from the start
     done_blocks, n_rows = 0, 0
+    c0 = time.process_time()
     t0 = time.perf_counter()
     while time.perf_counter() - t0 <= budget_s:
         for i in order:
@@ -122,13 +142,17 @@ def cpu_baseline(w, lay, q, k, v, budget_s=12.0, seed=0):
             if time.perf_counter() - t0 > budget_s:
                 break
     el = time.perf_counter() - t0
+    busy = (time.process_time() - c0) / el
     flops = 4 * w.block * w.block * w.d * done_blocks
     if n_rows <= len(rows):
         what = f"{n_rows} of {len(rows)} block rows of {w.name}"
     else:
         what = f"{n_rows} block-row evaluations, {n_rows / len(rows):.1f} passes over the {len(rows)} block rows of {w.name}"
-    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{what} ({done_blocks} stored blocks), oracle per-block route in float64 numpy, {el:.1f} s"}
+    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": max(1, math.ceil(busy - 0.05)),
+            "kind": "oracle",
+            "sample": f"{what} ({done_blocks} stored blocks), oracle per-block route in float64 numpy, {el:.1f} s",
+            "threads_busy": round(busy, 2), "host_cores": len(os.sched_getaffinity(0)),
+            "cpu_count": os.cpu_count(), "cpu_model": _cpu_model(), "blas_threads": blas_threads}
 
 
 def run_workload(w, steps, warmup, with_ops=True, with_cpu=True):
@@ -188,9 +212,16 @@ def run_workload(w, steps, warmup, with_ops=True, with_cpu=True):
             S = torch.empty((w.Z, L.nnz, w.block, w.block), dtype=torch.float32, device=dev)
             O2 = torch.empty_like(q)
             n = max(3, steps // 2)
-            bsa.sdd(L, q, k, out=S)
+            # every op is called twice before its timed window (code object
+            # load, first-touch of the buffers), then timed on its own
+            for _ in range(2):
+                bsa.sdd(L, q, k, out=S)
             t_sdd = _events_time(lambda: bsa.sdd(L, q, k, out=S), n, stream)
+            for _ in range(2):
+                bsa.softmax(L, S, w.scale, w.causal, out=S)
             t_sm = _events_time(lambda: bsa.softmax(L, S, w.scale, w.causal, out=S), n, stream)
+            for _ in range(2):
+                bsa.dsd(L, S, v, out=O2)
             t_dsd = _events_time(lambda: bsa.dsd(L, S, v, out=O2), n, stream)
             sbytes = 4 * w.block * w.block * L.nnz * w.Z
             ops["unfused"] = {
@@ -212,7 +243,8 @@ def run_workload(w, steps, warmup, with_ops=True, with_cpu=True):
             fb = 10 * w.block * w.block * w.d * L.nnz * w.Z
             o, lse = bsa.attention(L, q, k, v, w.scale, w.causal, return_lse=True)
             wsd = torch.empty(lse.shape, dtype=torch.float32, device=dev)
-            bsa.attention_backward_fused(L, q, k, v, o, lse, do, w.scale, w.causal, workspace=wsd)
+            for _ in range(2):
+                bsa.attention_backward_fused(L, q, k, v, o, lse, do, w.scale, w.causal, workspace=wsd)
             t_fb = _events_time(lambda: bsa.attention_backward_fused(L, q, k, v, o, lse, do, w.scale, w.causal,
                                                                      workspace=wsd), n, stream)
             ops["backward"] = {"ms": round(t_fb, 4), "tflops": round(fb / (t_fb * 1e-3) / 1e12, 3),
@@ -221,7 +253,8 @@ def run_workload(w, steps, warmup, with_ops=True, with_cpu=True):
             del o, lse, wsd
             ws = (torch.empty((w.Z, L.nnz, w.block, w.block), dtype=torch.float32, device=dev),
                   torch.empty((w.Z, L.nnz, w.block, w.block), dtype=torch.float32, device=dev))
-            bsa.attention_backward(L, q, k, v, do, w.scale, w.causal, workspace=ws)
+            for _ in range(2):
+                bsa.attention_backward(L, q, k, v, do, w.scale, w.causal, workspace=ws)
             t_bwd = _events_time(lambda: bsa.attention_backward(L, q, k, v, do, w.scale, w.causal, workspace=ws),
                                  n, stream)
             ops["backward_composed"] = {"ms": round(t_bwd, 4), "tflops": round(fb / (t_bwd * 1e-3) / 1e12, 3)}
@@ -231,7 +264,8 @@ def run_workload(w, steps, warmup, with_ops=True, with_cpu=True):
             A, Sd = A.to(dev), Sd.to(dev)
             C = torch.empty((w.Z, w.H, w.dds_m, w.N), dtype=A.dtype, device=dev)
             n = max(3, steps // 2)
-            bsa.dds(L, A, Sd, out=C)
+            for _ in range(2):
+                bsa.dds(L, A, Sd, out=C)
             t_dds = _events_time(lambda: bsa.dds(L, A, Sd, out=C), n, stream)
             fd = 2 * w.block * w.block * w.dds_m * L.nnz * w.Z
             ops["dds"] = {"ms": round(t_dds, 4), "tflops": round(fd / (t_dds * 1e-3) / 1e12, 3),
@@ -265,6 +299,7 @@ def main(argv=None):
     ap.add_argument("--all", action="store_true", help="also run every workload (lines on stderr)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
     ap.add_argument("--no-ops", action="store_true", help="skip the per-op breakdown")
+    ap.add_argument("--no-others", action="store_true", help="skip the fused kernel on the other workloads")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args(argv)
 
@@ -291,6 +326,17 @@ def main(argv=None):
                                                                           "ops") if k in r}}),
                   file=sys.stderr, flush=True)
     r = run_workload(w, args.steps, args.warmup, with_ops=not args.no_ops, with_cpu=not args.no_cpu)
+    # the fused kernel on every other workload, briefly (roofline fraction
+    # of each, so that one line records where every configuration stands)
+    others = {}
+    if not args.no_others:
+        for other in W.WORKLOADS:
+            if other.name == w.name:
+                continue
+            ro = run_workload(other, max(10, args.steps // 2), max(3, args.warmup), with_ops=False, with_cpu=False)
+            others[other.name] = {"dtype": other.dtype, "kernel_ms": round(ro["kernel_ms"], 4),
+                                  "tflops": ro["roofline"]["achieved"], "frac": ro["roofline"]["frac"],
+                                  "traffic": ro["roofline"]["traffic"], "nnz": ro["nnz"]}
     line = {
         "metric": METRIC,
         "value": round(r["tflops"], 3),
@@ -311,6 +357,7 @@ def main(argv=None):
         "mfma_peak_frac": r["roofline"]["frac"],
         "cpu_baseline": r.get("cpu_baseline"),
         "ops": r.get("ops"),
+        "fused_other_workloads": others or None,
         "lut_build_ms": r["lut_build_ms"],
         "lut_build_first_ms": r["lut_build_first_ms"],
     }

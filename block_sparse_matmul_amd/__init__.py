@@ -110,7 +110,8 @@ class Layout:
     def _read_info(self):
         H, nbr, nbc, b = C.c_int(), C.c_int(), C.c_int(), C.c_int()
         nnz = C.c_int64()
-        check(lib().bs_layout_info(self._h, C.byref(H), C.byref(nbr), C.byref(nbc), C.byref(b), C.byref(nnz)))
+        check(lib().bs_layout_info(self._h, C.byref(H), C.byref(nbr), C.byref(nbc), C.byref(b), None))
+        check(lib().bs_layout_nnz(self._h, C.byref(nnz)))
         self.H, self.nbr, self.nbc, self.block, self.nnz = H.value, nbr.value, nbc.value, b.value, nnz.value
 
     @property
@@ -381,13 +382,13 @@ def attention_backward(L: Layout, q, k, v, do, scale: Optional[float] = None, ca
 
 
 def attention_backward_fused(L: Layout, q, k, v, o, lse, do, scale: Optional[float] = None, causal: bool = False,
-                             attn_mask=None, key_padding_mask=None, workspace=None):
+                             attn_mask=None, key_padding_mask=None, workspace=None, out=None):
     """(dq, dk, dv) of attention() from its inputs, its output o and row
     log-sum-exp lse (attention(..., return_lse=True)) and the output
     gradient do, on the fused backward kernels (S and P never reach
     memory). Same scale, causal flag and masks as the forward.
     workspace: optional float32 [Z, H, Nq] tensor (the D = rowsum(do * o)
-    buffer)."""
+    buffer). out: optional (dq, dk, dv) tensors to write."""
     torch = _torch()
     for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
         _check_dense(n, t)
@@ -403,10 +404,15 @@ def attention_backward_fused(L: Layout, q, k, v, o, lse, do, scale: Optional[flo
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     am, kp = _mask_ptrs(L, Z, q.device, attn_mask, key_padding_mask)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = (_out(t, like.shape, like.dtype, like.device, n)
+                      for t, like, n in zip(out, (q, k, v), ("dq", "dk", "dv")))
+    flags = BS_CAUSAL if causal else 0
     ws = _out(workspace, (Z, H, Nq), torch.float32, q.device, "workspace")
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     check(lib().bs_attention_bwd(L.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
-                                 _ptr(dk), _ptr(dv), _ptr(ws), Z, d, float(scale), BS_CAUSAL if causal else 0, am, kp,
+                                 _ptr(dk), _ptr(dv), _ptr(ws), Z, d, float(scale), flags, am, kp,
                                  _dtype_code(q), _stream(q.device)))
     return dq, dk, dv
 

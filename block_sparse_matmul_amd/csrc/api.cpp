@@ -29,6 +29,15 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(oom ? BS_ERR_OOM : BS_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
+hipError_t dev_alloc(void** p, size_t bytes) {
+  const char* v = getenv("BS_FAULT_INJECT");
+  if (v && std::string(v) == "oom") {
+    *p = nullptr;
+    return hipErrorOutOfMemory;
+  }
+  return hipMalloc(p, bytes);
+}
+
 bool log_enabled() {
   static const bool on = [] {
     const char* v = getenv("BS_LOG");
@@ -176,9 +185,9 @@ static int analyse_band(bs_layout* L, const bs_acsr_term* terms, int n_terms) {
   d.erase(std::unique(d.begin(), d.end()), d.end());
   if (d.empty()) return BS_OK;
   int32_t* dev = nullptr;
-  if (hipMalloc(&dev, d.size() * sizeof(int32_t)) != hipSuccess) {
+  if (bsa::dev_alloc(&dev, d.size() * sizeof(int32_t)) != hipSuccess) {
     (void)hipGetLastError();
-    return fail(BS_ERR_OOM, "hipMalloc of the ACSR offsets failed");
+    return fail(BS_ERR_OOM, "device allocation of the ACSR offsets failed");
   }
   hipError_t e = hipMemcpy(dev, d.data(), d.size() * sizeof(int32_t), hipMemcpyHostToDevice);
   if (e != hipSuccess) {
@@ -206,14 +215,14 @@ int bs_layout_build_acsr(const bs_acsr_term* terms, int n_terms, int H, int nbr,
   const size_t cells = (size_t)H * nbr * nbc;
   uint8_t* lay = nullptr;
   bs_acsr_term* dterms = nullptr;
-  if (hipMalloc(&lay, cells) != hipSuccess) {
+  if (bsa::dev_alloc(&lay, cells) != hipSuccess) {
     (void)hipGetLastError();
-    return fail(BS_ERR_OOM, "hipMalloc of the expanded layout failed");
+    return fail(BS_ERR_OOM, "device allocation of the expanded layout failed");
   }
-  if (n_terms > 0 && hipMalloc(&dterms, sizeof(bs_acsr_term) * n_terms) != hipSuccess) {
+  if (n_terms > 0 && bsa::dev_alloc(&dterms, sizeof(bs_acsr_term) * n_terms) != hipSuccess) {
     (void)hipGetLastError();
     (void)hipFree(lay);
-    return fail(BS_ERR_OOM, "hipMalloc of the ACSR terms failed");
+    return fail(BS_ERR_OOM, "device allocation of the ACSR terms failed");
   }
   hipError_t e = hipSuccess;
   if (n_terms > 0)
@@ -238,6 +247,13 @@ int bs_layout_build_acsr(const bs_acsr_term* terms, int n_terms, int H, int nbr,
   (void)hipFree(dterms);
   (void)hipFree(lay);
   return rc;
+}
+
+int bs_layout_nnz(bs_layout_t L, int64_t* nnz) {
+  if (int rc = check_handle(L)) return rc;
+  if (!nnz) return fail(BS_ERR_INVALID_ARG, "nnz pointer is NULL");
+  *nnz = L->nnz;
+  return BS_OK;
 }
 
 int bs_layout_info(bs_layout_t L, int* H, int* nbr, int* nbc, int* block, int64_t* nnz) {

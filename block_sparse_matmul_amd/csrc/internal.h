@@ -181,4 +181,14 @@ int launch_attention_wide(const bs_layout* L, const AttnArgs& a, hipStream_t s);
 
 bool log_enabled();
 
+// Device allocation for the layout tables (the only allocations the library
+// makes). With the environment variable BS_FAULT_INJECT=oom it fails the way
+// an exhausted device does, without calling hipMalloc: a test hook for the
+// BS_ERR_OOM paths, read on every call.
+hipError_t dev_alloc(void** p, size_t bytes);
+template <typename T>
+hipError_t dev_alloc(T** p, size_t bytes) {
+  return dev_alloc(reinterpret_cast<void**>(p), bytes);
+}
+
 }  // namespace bsa

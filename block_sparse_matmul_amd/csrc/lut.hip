@@ -268,14 +268,14 @@ int build_tables(bs_layout* L, const uint8_t* lay, hipStream_t s) {
   const size_t tmp_n = (size_t)rows + cols + SUM_N + (nbc + 2) + (nbr + 2) + 2 * (size_t)H + (size_t)cells;
   int32_t* fixed_mem = nullptr;
   int32_t* tmp = nullptr;
-  if (hipMalloc(&fixed_mem, fixed * sizeof(int32_t)) != hipSuccess) {
+  if (dev_alloc(&fixed_mem, fixed * sizeof(int32_t)) != hipSuccess) {
     (void)hipGetLastError();
-    return fail(BS_ERR_OOM, "hipMalloc of the layout tables failed");
+    return fail(BS_ERR_OOM, "device allocation of the layout tables failed");
   }
-  if (hipMalloc(&tmp, tmp_n * sizeof(int32_t)) != hipSuccess) {
+  if (dev_alloc(&tmp, tmp_n * sizeof(int32_t)) != hipSuccess) {
     (void)hipGetLastError();
     (void)hipFree(fixed_mem);
-    return fail(BS_ERR_OOM, "hipMalloc of the layout build workspace failed");
+    return fail(BS_ERR_OOM, "device allocation of the layout build workspace failed");
   }
   int32_t* row_ptr = fixed_mem;
   int32_t* col_ptr = row_ptr + rows + 1;
@@ -350,9 +350,9 @@ int build_tables(bs_layout* L, const uint8_t* lay, hipStream_t s) {
 
   int32_t* nnz_mem = nullptr;
   if (nnz > 0) {
-    if (hipMalloc(&nnz_mem, (size_t)nnz * 3 * sizeof(int32_t)) != hipSuccess) {
+    if (dev_alloc(&nnz_mem, (size_t)nnz * 3 * sizeof(int32_t)) != hipSuccess) {
       (void)hipGetLastError();
-      return cleanup(fail(BS_ERR_OOM, "hipMalloc of the block tables failed"));
+      return cleanup(fail(BS_ERR_OOM, "device allocation of the block tables failed"));
     }
     int32_t* col_idx = nnz_mem;
     int32_t* row_idx = col_idx + nnz;

@@ -69,7 +69,9 @@ typedef enum {
   BS_ERR_LAYOUT = -3,      /* a layout value other than 0 or 1 */
   BS_ERR_SHAPE = -4,       /* sizes overflow the 32/64-bit index ranges */
   BS_ERR_HIP = -5,         /* a HIP runtime call failed */
-  BS_ERR_OOM = -6,         /* device allocation failed */
+  BS_ERR_OOM = -6,         /* device allocation failed (also forced, with
+                              no allocation attempted, when the environment
+                              variable BS_FAULT_INJECT is "oom") */
   BS_ERR_NO_DEVICE = -7    /* no HIP device is visible */
 } bs_status;
 
@@ -99,6 +101,11 @@ int bs_layout_build(const uint8_t* layout, int H, int nbr, int nbc, int block,
 int bs_layout_build_acsr(const bs_acsr_term* terms, int n_terms, int H,
                          int nbr, int nbc, int block, void* stream,
                          bs_layout_t* out);
+
+/* Number of stored blocks of a handle, summed over heads (the length of
+   the block-sparse tensors' nnz axis). nnz: host int64_t. Errors:
+   BS_ERR_INVALID_ARG for a NULL handle or output pointer. */
+int bs_layout_nnz(bs_layout_t L, int64_t* nnz);
 
 /* Sizes of a handle (any output pointer may be NULL). */
 int bs_layout_info(bs_layout_t L, int* H, int* nbr, int* nbc, int* block,

@@ -32,11 +32,11 @@ design notes):
     additive masks (below), then the causal mask (-inf where the global key
     index exceeds the global query index), then a row softmax over every
     stored entry of the row. A row with no visible entry gives zeros.
-  * dense masks ("you can also pass dense masks", question on blocksparse;
-    the page gives no format): attn_mask, float [Nq, Nk] over the global
-    query and key indices, shared by every batch element and head, and
-    kp_mask (key padding), float [Z, Nk] per batch element and key; both
-    are added to scale * S. -inf hides an entry. Entries outside the
+  * dense masks (question on blocksparse, the answer on dense masks for
+    block-triangular layouts; the page gives no format): attn_mask, float
+    [Nq, Nk] over the global query and key indices, shared by every batch
+    element and head, and kp_mask (key padding), float [Z, Nk] per batch
+    element and key; both are added to scale * S. -inf hides an entry. Entries outside the
     layout's blocks stay hidden whatever the masks hold.
 """
 from __future__ import annotations
@@ -49,7 +49,7 @@ __all__ = [
     "check_layout", "lut_from_layout", "layout_from_lut", "acsr_expand",
     "element_mask", "sdd", "softmax", "dsd", "dds",
     "attention_dense", "attention_blocks", "attention_rows", "attention_lse",
-    "attention_blockrow", "nnz_flops_attention", "nnz_flops_dds",
+    "attention_blockrow",
     "softmax_backward", "dsd_t", "dds_t", "attention_backward_dense", "attention_backward_blocks",
 ]
 
@@ -499,11 +499,3 @@ def attention_backward_blocks(Q, K, V, dO, layout, block: int, scale: float, cau
     dS = softmax_backward(P, sdd(dO, V, layout, block), layout, block, scale)
     return dsd(dS, K, layout, block), dsd_t(dS, Q, layout, block), dsd_t(P, dO, layout, block)
 
-
-def nnz_flops_attention(nnz: int, Z: int, block: int, d: int) -> int:
-    """2 b^2 d flops per stored block for SDD plus 2 b^2 d for DSD."""
-    return 4 * block * block * d * nnz * Z
-
-
-def nnz_flops_dds(nnz: int, Z: int, block: int, M: int) -> int:
-    return 2 * block * block * M * nnz * Z

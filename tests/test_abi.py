@@ -21,7 +21,7 @@ def _declared_functions():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    for n in ("bs_layout_build", "bs_layout_build_acsr", "bs_sdd", "bs_softmax", "bs_dsd", "bs_dds",
+    for n in ("bs_layout_build", "bs_layout_build_acsr", "bs_layout_nnz", "bs_sdd", "bs_softmax", "bs_dsd", "bs_dds",
               "bs_attention", "bs_last_error", "bs_layout_free", "bs_layout_export",
               "bs_softmax_backward", "bs_dsd_t", "bs_attention_backward"):
         assert n in names
@@ -90,6 +90,8 @@ def test_compute_calls_reject_null_handle():
     assert L.bs_attention_backward(None, None, None, None, None, None, None, None, None, None, 1, 64, 1.0, 0, 0,
                                    None) == _lib.BS_ERR_INVALID_ARG
     assert L.bs_layout_info(None, None, None, None, None, None) == _lib.BS_ERR_INVALID_ARG
+    n = C.c_int64(-1)
+    assert L.bs_layout_nnz(None, C.byref(n)) == _lib.BS_ERR_INVALID_ARG and n.value == -1
     assert L.bs_layout_export(None, None, None, None, None, None) == _lib.BS_ERR_INVALID_ARG
     L.bs_layout_free(None)  # ignored
 

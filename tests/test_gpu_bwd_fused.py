@@ -148,7 +148,8 @@ def test_fused_backward_full_size_sampled_heads(idx):
     """causal_b64 and bigbird_b64 (fp32) at full size, the dense oracle
     gradient of two (batch, head) pairs; random_b128_bf16 at full size (the
     head-grouped order of the 16-bit kernels), its last head (about 10 s of
-    float64 oracle)."""
+    float64 oracle). The gradients are written over NaN, and every element
+    must come back finite (nothing left unwritten)."""
     w = W.WORKLOADS[idx]
     lay = W.make_layout(w)
     q, k, v = W.make_qkv(w)
@@ -158,7 +159,11 @@ def test_fused_backward_full_size_sampled_heads(idx):
     L = bsa.Layout(torch.from_numpy(lay), w.block)
     qd, kd, vd, dod = (to_dev(t) for t in (q, k, v, do))
     o, lse = bsa.attention(L, qd, kd, vd, w.scale, w.causal, return_lse=True)
-    dq, dk, dv = bsa.attention_backward_fused(L, qd, kd, vd, o, lse, dod, w.scale, w.causal)
+    nan = tuple(torch.full_like(t, float("nan")) for t in (qd, kd, vd))
+    dq, dk, dv = bsa.attention_backward_fused(L, qd, kd, vd, o, lse, dod, w.scale, w.causal, out=nan)
+    torch.cuda.synchronize()
+    for name, g in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert bool(torch.isfinite(g).all()), ("unwritten gradient", name)
     dt = "f32" if q.dtype == torch.float32 else "bf16"
     pairs = ((0, 0), (w.Z - 1, w.H - 1)) if w.dtype == "f32" else ((w.Z - 1, w.H - 1),)
     for z, h in pairs:
