@@ -382,13 +382,16 @@ def attention_backward(L: Layout, q, k, v, do, scale: Optional[float] = None, ca
 
 
 def attention_backward_fused(L: Layout, q, k, v, o, lse, do, scale: Optional[float] = None, causal: bool = False,
-                             attn_mask=None, key_padding_mask=None, workspace=None, out=None):
+                             attn_mask=None, key_padding_mask=None, workspace=None, out=None, noalloc: bool = False):
     """(dq, dk, dv) of attention() from its inputs, its output o and row
     log-sum-exp lse (attention(..., return_lse=True)) and the output
     gradient do, on the fused backward kernels (S and P never reach
     memory). Same scale, causal flag and masks as the forward.
     workspace: optional float32 [Z, H, Nq] tensor (the D = rowsum(do * o)
-    buffer). out: optional (dq, dk, dv) tensors to write."""
+    buffer). out: optional (dq, dk, dv) tensors to write.
+    noalloc: call bs_attention_bwd_noalloc, which keeps D in the library's
+    static device buffer (at most 2^21 query rows) and allocates nothing;
+    with `out` given this call allocates no device memory at all."""
     torch = _torch()
     for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
         _check_dense(n, t)
@@ -410,6 +413,13 @@ def attention_backward_fused(L: Layout, q, k, v, o, lse, do, scale: Optional[flo
         dq, dk, dv = (_out(t, like.shape, like.dtype, like.device, n)
                       for t, like, n in zip(out, (q, k, v), ("dq", "dk", "dv")))
     flags = BS_CAUSAL if causal else 0
+    if noalloc:
+        if workspace is not None:
+            raise ValueError("noalloc takes no workspace (D lives in the library's static buffer)")
+        check(lib().bs_attention_bwd_noalloc(L.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                                             _ptr(dq), _ptr(dk), _ptr(dv), Z, d, float(scale), flags, am, kp,
+                                             _dtype_code(q), _stream(q.device)))
+        return dq, dk, dv
     ws = _out(workspace, (Z, H, Nq), torch.float32, q.device, "workspace")
     check(lib().bs_attention_bwd(L.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
                                  _ptr(dk), _ptr(dv), _ptr(ws), Z, d, float(scale), flags, am, kp,

@@ -59,6 +59,8 @@ SIGNATURES = {
     "bs_attention_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _f, _i, _vp, _vp, _i, _vp]),
     "bs_attention_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _f, _i, _vp, _vp, _i,
                               _vp]),
+    "bs_attention_bwd_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _f, _i, _vp, _vp,
+                                      _i, _vp]),
     "bs_sdd_ex": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
     "bs_dsd_ex": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
     "bs_dds_ex": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),

@@ -426,10 +426,21 @@ int bs_attention_backward_masked(bs_layout_t L, const void* Q, const void* K, co
   return bsa::launch_dsd_t(L, ws_p, dO, dV, Z, d, dt, s);                               // dV = P^T dO
 }
 
-int bs_attention_bwd(bs_layout_t L, const void* Q, const void* K, const void* V, const void* O, const float* lse,
-                     const void* dO, void* dQ, void* dK, void* dV, float* ws_d, int Z, int d, float scale, int flags,
-                     const float* attn_mask, const float* kp_mask, bs_dtype dt, void* stream) {
+}  // extern "C"
+
+// Shared body of bs_attention_bwd (D in the caller's ws_d) and
+// bs_attention_bwd_noalloc (D in the library's static device array, no
+// allocation of any kind).
+static int attention_bwd(bs_layout_t L, const void* Q, const void* K, const void* V, const void* O, const float* lse,
+                         const void* dO, void* dQ, void* dK, void* dV, float* ws_d, bool use_scratch, int Z, int d,
+                         float scale, int flags, const float* attn_mask, const float* kp_mask, bs_dtype dt,
+                         void* stream) {
   if (int rc = check_handle(L)) return rc;
+  if (use_scratch && Z > 0 && (int64_t)Z * L->H * L->nbr * L->block > bsa::kBwdScratchRows)
+    return fail(BS_ERR_SHAPE, "bs_attention_bwd_noalloc: Z*H*nbr*b = " +
+                                  std::to_string((int64_t)Z * L->H * L->nbr * L->block) +
+                                  " query rows exceed the static D buffer of " +
+                                  std::to_string(bsa::kBwdScratchRows) + " rows (use bs_attention_bwd)");
   if (int rc = check_dtype(dt)) return rc;
   if (int rc = check_masks(attn_mask, kp_mask)) return rc;
   if (flags & ~BS_CAUSAL) return fail(BS_ERR_INVALID_ARG, "unknown flag");
@@ -438,14 +449,37 @@ int bs_attention_bwd(bs_layout_t L, const void* Q, const void* K, const void* V,
   const bool causal = flags & BS_CAUSAL;
   if (causal && L->nbr != L->nbc) return fail(BS_ERR_INVALID_ARG, "causal attention needs a square layout");
   const bool work = Z > 0;
-  if (int rc = check_ptrs(work, {Q, K, V, O, lse, dO, dQ, dK, dV, ws_d})) return rc;
+  if (int rc = check_ptrs(work, {Q, K, V, O, lse, dO, dQ, dK, dV})) return rc;
+  if (!use_scratch) {
+    if (int rc = check_ptrs(work, {ws_d})) return rc;
+  }
   if (!work) return BS_OK;
   if (int rc = check_grid(L, Z)) return rc;
-  log_call("attention_bwd", L, Z, d);
+  if (use_scratch) {
+    if (int rc = bsa::bwd_scratch(&ws_d)) return rc;
+  }
+  log_call(use_scratch ? "attention_bwd_noalloc" : "attention_bwd", L, Z, d);
   bsa::BwdArgs a{Q, K, V, O, lse, dO, dQ, dK, dV, ws_d, Z, d, scale, causal, dt};
   a.am = attn_mask;
   a.kp = kp_mask;
   return bsa::launch_attention_bwd(L, a, (hipStream_t)stream);
+}
+
+extern "C" {
+
+int bs_attention_bwd(bs_layout_t L, const void* Q, const void* K, const void* V, const void* O, const float* lse,
+                     const void* dO, void* dQ, void* dK, void* dV, float* ws_d, int Z, int d, float scale, int flags,
+                     const float* attn_mask, const float* kp_mask, bs_dtype dt, void* stream) {
+  return attention_bwd(L, Q, K, V, O, lse, dO, dQ, dK, dV, ws_d, false, Z, d, scale, flags, attn_mask, kp_mask, dt,
+                       stream);
+}
+
+int bs_attention_bwd_noalloc(bs_layout_t L, const void* Q, const void* K, const void* V, const void* O,
+                             const float* lse, const void* dO, void* dQ, void* dK, void* dV, int Z, int d,
+                             float scale, int flags, const float* attn_mask, const float* kp_mask, bs_dtype dt,
+                             void* stream) {
+  return attention_bwd(L, Q, K, V, O, lse, dO, dQ, dK, dV, nullptr, true, Z, d, scale, flags, attn_mask, kp_mask,
+                       dt, stream);
 }
 
 int bs_dds(bs_layout_t L, const void* A, const float* S, void* C, int Z, int M, bs_dtype dt, void* stream) {

@@ -32,6 +32,7 @@
 // results from fp32 accumulators.
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "internal.h"
@@ -465,7 +466,34 @@ int run_e(const bs_layout* L, const BwdArgs& a, hipStream_t s) {
   return fail(BS_ERR_UNSUPPORTED, "head size d must be 64 or 128");
 }
 
+// D buffer of bs_attention_bwd_noalloc: a library-owned device array, one
+// copy per device for the life of the process. Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the
+// symbol); it passes the device address that hipGetSymbolAddress returns,
+// looked up once per device with that device current.
+static __device__ __align__(256) float scratch[kBwdScratchRows];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
 }  // namespace
+
+int bwd_scratch(float** out) {
+  *out = nullptr;
+  int dev = -1;
+  BSA_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(BS_ERR_UNSUPPORTED, "device ordinal beyond the scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return BS_OK;
+}
 
 int launch_attention_bwd(const bs_layout* L, const BwdArgs& a, hipStream_t s) {
   if (a.dt == BS_BF16) return run_e<bf16_t>(L, a, s);

@@ -142,6 +142,12 @@ struct BwdArgs {
 };
 int launch_attention_bwd(const bs_layout* L, const BwdArgs& a, hipStream_t s);
 
+// The D buffer of bs_attention_bwd_noalloc: float32 [kBwdScratchRows], a
+// static device array (backward.hip); *out receives its address on the
+// current device (looked up once per device).
+constexpr int64_t kBwdScratchRows = (int64_t)1 << 21;  // 8 MiB
+int bwd_scratch(float** out);
+
 // DSD and DDS with the BS_TRANS_A / BS_TRANS_B flags (dsd.hip): the plain
 // and fast paths where they apply, otherwise the general strided kernel
 // (GenArgs: P the block values, B the dense operand, C the output; N the

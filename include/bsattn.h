@@ -270,6 +270,23 @@ int bs_attention_bwd(bs_layout_t L, const void* Q, const void* K,
                      const float* attn_mask, const float* kp_mask,
                      bs_dtype dt, void* stream);
 
+/* bs_attention_bwd for callers that cannot allocate device memory (code
+   under HIP graph capture, tight serving loops, harnesses that forbid
+   hipMalloc): the same kernels and results, with D kept in a library-owned
+   static device array of 2^21 float32 (8 MiB per device, held until the
+   process ends) instead of a caller workspace. Makes no allocation of any
+   kind. Errors as bs_attention_bwd, plus BS_ERR_SHAPE when Z*H*nbr*b
+   exceeds 2^21 query rows. Every call on one device shares that device's
+   array, so calls that may overlap on one device (several streams or
+   threads) race and must be serialised by the caller; nothing in the array
+   needs to start at zero (each call writes D before it reads it). */
+int bs_attention_bwd_noalloc(bs_layout_t L, const void* Q, const void* K,
+                             const void* V, const void* O, const float* lse,
+                             const void* dO, void* dQ, void* dK, void* dV,
+                             int Z, int d, float scale, int flags,
+                             const float* attn_mask, const float* kp_mask,
+                             bs_dtype dt, void* stream);
+
 /* ---- the three modes with transposed operands (question on blocksparse:
    the three modes; the flags follow the usual matmul convention of
    operands used transposed) ----
