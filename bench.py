@@ -39,7 +39,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "block-sparse attention TFLOP/s on nnz blocks + % of MFMA peak, 1 MI355X"
-PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}   # MI355X dense MFMA
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "fp8": 5033.2}   # MI355X dense MFMA (fp8: twice bf16)
+# fused attention with fp8 score operands: half the flops (Q K^T) at the fp8
+# peak, half (P V) at the bf16 peak
+PEAK_FP8_QK = 1.0 / (0.5 / PEAK_TFLOPS["fp8"] + 0.5 / PEAK_TFLOPS["bf16"])
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "random_b128_bf16"
 
@@ -259,6 +262,21 @@ def run_workload(w, steps, warmup, with_ops=True, with_cpu=True):
                                  n, stream)
             ops["backward_composed"] = {"ms": round(t_bwd, 4), "tflops": round(fb / (t_bwd * 1e-3) / 1e12, 3)}
             del do, ws
+        if w.dtype == "bf16" and w.d == 128:
+            # the same workload with Q and K rounded to fp8 (OCP E4M3): the
+            # score product on the fp8 matrix cores, P.V in bf16
+            f8 = torch.float8_e4m3fn
+            q8, k8 = q.float().to(f8), k.float().to(f8)
+            o8 = torch.empty_like(v)
+            for _ in range(2):
+                bsa.attention(L, q8, k8, v, w.scale, w.causal, out=o8)
+            t8 = _events_time(lambda: bsa.attention(L, q8, k8, v, w.scale, w.causal, out=o8), max(3, steps // 2),
+                              stream)
+            ops["fused_fp8_qk"] = {"ms": round(t8, 4), "tflops": round(flops / (t8 * 1e-3) / 1e12, 3),
+                                   "peak": round(PEAK_FP8_QK, 1),
+                                   "frac": round(flops / (t8 * 1e-3) / 1e12 / PEAK_FP8_QK, 4),
+                                   "operands": "Q, K float8_e4m3fn; V, O bf16"}
+            del q8, k8, o8
         if w.dds_m:
             A, Sd = W.make_dds_operands(w, L.nnz)
             A, Sd = A.to(dev), Sd.to(dev)

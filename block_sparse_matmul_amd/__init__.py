@@ -25,7 +25,8 @@ from typing import Dict, Optional, Sequence, Tuple
 import numpy as np
 
 from . import _lib
-from ._lib import AcsrTerm, BsError, BS_BF16, BS_CAUSAL, BS_F16, BS_F32, BS_TRANS_A, BS_TRANS_B, check, lib
+from ._lib import (AcsrTerm, BsError, BS_BF16, BS_CAUSAL, BS_F16, BS_F32, BS_F8E4M3, BS_TRANS_A, BS_TRANS_B, check,
+                   lib)
 
 __all__ = ["Layout", "sdd", "softmax", "dsd", "dds", "attention", "softmax_backward", "dsd_t",
            "attention_backward", "attention_backward_fused", "attention_autograd", "BsError", "lib"]
@@ -49,7 +50,9 @@ def _dtype_code(t) -> int:
         return BS_BF16
     if t.dtype == torch.float16:
         return BS_F16
-    raise TypeError(f"dense operands must be float32, bfloat16 or float16, got {t.dtype}")
+    if t.dtype == getattr(torch, "float8_e4m3fn", None):
+        return BS_F8E4M3
+    raise TypeError(f"dense operands must be float32, bfloat16, float16 or float8_e4m3fn, got {t.dtype}")
 
 
 def _check_dense(name, t, ndim=4):
@@ -286,18 +289,25 @@ def attention(L: Layout, q, k, v, scale: Optional[float] = None, causal: bool = 
     mask is the layout's, the optional dense additive masks (see softmax)
     and the causal one. With return_lse, also the float32 [Z, H, Nq] row
     log-sum-exp of the masked scaled scores (-inf for empty rows), written
-    by the same kernel: returns (out, lse)."""
+    by the same kernel: returns (out, lse).
+    fp8: q and k of dtype torch.float8_e4m3fn (the score product on the fp8
+    matrix cores), v bfloat16; out is bfloat16 (d = 128, blocks >= 32)."""
+    torch = _torch()
     for n, t in (("q", q), ("k", k), ("v", v)):
         _check_dense(n, t)
     Z, H, Nq, d = q.shape
-    if not (q.dtype == k.dtype == v.dtype):
+    fp8 = q.dtype == getattr(torch, "float8_e4m3fn", None)
+    if fp8:
+        if k.dtype != q.dtype or v.dtype != torch.bfloat16:
+            raise ValueError("fp8 attention takes q, k as float8_e4m3fn and v as bfloat16")
+    elif not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k, v must share a dtype")
     if (H, Nq) != (L.H, L.nbr * L.block) or k.shape != (Z, H, L.nbc * L.block, d) or v.shape != k.shape:
         raise ValueError("q must be [Z, H, nbr*b, d]; k, v [Z, H, nbc*b, d]")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     am, kp = _mask_ptrs(L, Z, q.device, attn_mask, key_padding_mask)
-    out = _out(out, q.shape, q.dtype, q.device)
+    out = _out(out, q.shape, v.dtype, q.device)
     flags = BS_CAUSAL if causal else 0
     if return_lse:
         lse = _out(lse, (Z, H, Nq), _torch().float32, q.device, "lse")

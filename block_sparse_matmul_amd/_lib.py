@@ -22,6 +22,7 @@ BS_ERR_NO_DEVICE = -7
 BS_F32 = 0
 BS_BF16 = 1
 BS_F16 = 2
+BS_F8E4M3 = 3
 BS_CAUSAL = 1
 BS_TRANS_A = 1
 BS_TRANS_B = 2

@@ -86,9 +86,13 @@ int check_masks(const float* attn_mask, const float* kp_mask) {
   return BS_OK;
 }
 
-int check_dtype(bs_dtype dt) {
+int check_dtype(bs_dtype dt, bool fused_attention = false) {
+  if (dt == BS_F8E4M3) {
+    if (!fused_attention) return fail(BS_ERR_UNSUPPORTED, "BS_F8E4M3 is supported by the fused attention only");
+    return BS_OK;
+  }
   if (dt != BS_F32 && dt != BS_BF16 && dt != BS_F16)
-    return fail(BS_ERR_INVALID_ARG, "dtype must be BS_F32, BS_BF16 or BS_F16");
+    return fail(BS_ERR_INVALID_ARG, "dtype must be BS_F32, BS_BF16, BS_F16 or BS_F8E4M3");
   return BS_OK;
 }
 
@@ -520,10 +524,12 @@ int bs_attention_fwd(bs_layout_t L, const void* Q, const void* K, const void* V,
                      void* stream) {
   if (int rc = check_handle(L)) return rc;
   if (int rc = check_masks(attn_mask, kp_mask)) return rc;
-  if (int rc = check_dtype(dt)) return rc;
+  if (int rc = check_dtype(dt, true)) return rc;
   if (flags & ~BS_CAUSAL) return fail(BS_ERR_INVALID_ARG, "unknown flag");
   if (Z < 0) return fail(BS_ERR_INVALID_ARG, "Z must be >= 0");
   if (d != 64 && d != 128) return fail(BS_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (dt == BS_F8E4M3 && (d != 128 || L->block < 32))
+    return fail(BS_ERR_UNSUPPORTED, "BS_F8E4M3 attention needs d = 128 and blocks of 32, 64 or 128");
   const bool causal = flags & BS_CAUSAL;
   if (causal && L->nbr != L->nbc) return fail(BS_ERR_INVALID_ARG, "causal attention needs a square layout");
   const bool work = Z > 0;

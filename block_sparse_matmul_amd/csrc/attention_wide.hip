@@ -38,6 +38,24 @@ constexpr float kLn2B = 0.6931471805599453f;
 constexpr float kTauB = 8.0f;  // lazy-rescale headroom, log2 units
 
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// fp8 operands: tag of the element type in which Q and K are OCP FP8 E4M3
+// (one byte each) and the score product runs on the fp8 matrix cores
+// (v_mfma_f32_16x16x128_f8f6f4, exact products, fp32 accumulation), while V,
+// P and O stay bf16
+struct f8_t {};
+template <typename E>
+struct WideTypes {
+  typedef E PV;  // element type of V, P and O
+  static constexpr bool F8 = false;
+};
+template <>
+struct WideTypes<f8_t> {
+  typedef bf16_t PV;
+  static constexpr bool F8 = true;
+};
 
 template <int D>
 struct Swz;
@@ -50,17 +68,18 @@ struct Swz<64> {  // 128-byte rows, 8 chunks
   static __device__ __forceinline__ int f(int r) { return ((r >> 1) ^ r) & 7; }
 };
 
-template <int BLK, int D>
+template <int BLK, int D, int RBK = 2 * D>
 struct WideCfg {
   static constexpr int NW = BLK / 32;            // waves per key group
-  static constexpr int RB = D * 2;               // bytes per row
-  static constexpr int SB = BLK * RB;            // bytes per staged matrix
+  static constexpr int RB = D * 2;               // bytes per V row
+  static constexpr int SB = BLK * RB;            // bytes per staged V block
+  static constexpr int SBK = BLK * RBK;          // bytes per staged K block (RBK bytes per K row)
   static constexpr int NNT = D / 16;             // 16-column tiles of O
   static constexpr int SLOT = 64 * (2 + 4 * NNT);  // floats per wave and tile for the merge
   // LDS of a workgroup with ns key groups: K stages and V stages; the merge
   // (one query tile at a time) reuses the K stages
-  static constexpr size_t bytes(int ns) { return (size_t)ns * 2 * SB; }
-  static constexpr bool merge_fits(int ns) { return ns == 1 || (size_t)(ns - 1) * NW * SLOT * 4 <= (size_t)ns * SB; }
+  static constexpr size_t bytes(int ns) { return (size_t)ns * (SB + SBK); }
+  static constexpr bool merge_fits(int ns) { return ns == 1 || (size_t)(ns - 1) * NW * SLOT * 4 <= (size_t)ns * SBK; }
 };
 
 // s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in
@@ -82,11 +101,13 @@ __device__ __forceinline__ void wait_vmcnt0() { wait_vmcnt<0>(); }
 template <typename E, int BLK, int D, bool CAUSAL, int NS, bool MASKED>
 __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, const int32_t* __restrict__ row_order,
-    const int32_t* __restrict__ row_order_h, const u16* __restrict__ Q, const u16* __restrict__ K,
+    const int32_t* __restrict__ row_order_h, const void* __restrict__ Qv, const void* __restrict__ Kv,
     const u16* __restrict__ V, u16* __restrict__ O, int Z, int H, int nbr, int nbc, float c, int grouped,
     float* __restrict__ lse, const float* __restrict__ amask, const float* __restrict__ kpmask) {
-  using Cfg = WideCfg<BLK, D>;
-  using HT = H16<E>;
+  constexpr bool F8 = WideTypes<E>::F8;
+  constexpr int RBK = F8 ? D : 2 * D;  // bytes per K row
+  using Cfg = WideCfg<BLK, D, RBK>;
+  using HT = H16<typename WideTypes<E>::PV>;
   using V8 = typename HT::V8;
   using V4 = typename HT::V4;
   using V2 = typename HT::V2;
@@ -94,9 +115,13 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
   constexpr int NQ = D / 32;         // Q fragments per lane and tile
   constexpr int CPR = D / 8;         // 16-byte chunks per row
   constexpr int RB = Cfg::RB;
-  constexpr int RPI = 1024 / RB;     // rows per DMA instruction (64 lanes x 16 bytes)
+  constexpr int RPI = 1024 / RB;     // V rows per DMA instruction (64 lanes x 16 bytes)
+  constexpr int RPIK = 1024 / RBK;   // K rows per DMA instruction
+  constexpr int CPRK = RBK / 16;     // 16-byte chunks per K row
   constexpr int SB = Cfg::SB;
-  constexpr int NI = SB / 1024 / NW;  // DMA instructions per wave and matrix
+  constexpr int SBK = Cfg::SBK;
+  constexpr int NI = SB / 1024 / NW;  // DMA instructions per wave and V block
+  static_assert(!F8 || D == 128, "fp8 score product: one 16x16x128 product per tile needs d = 128");
   constexpr int KS = BLK < 64 ? BLK : 64;  // keys per sub-step
   constexpr int NSUB = BLK / KS;
   constexpr int NJT = KS / 16;
@@ -107,7 +132,7 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
 
   // K and V stages in separate arrays, so that the compiler can tell the
   // K reads from the V transfers in flight (and the other way round)
-  __shared__ __attribute__((aligned(16))) unsigned char Ks[NS * SB];
+  __shared__ __attribute__((aligned(16))) unsigned char Ks[NS * SBK];
   __shared__ __attribute__((aligned(16))) unsigned char Vs[NS * SB];
 
   const int tid_all = threadIdx.x;
@@ -116,7 +141,7 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int li = lane & 15, g = lane >> 4;
-  unsigned char* const Kg = Ks + sg * SB;
+  unsigned char* const Kg = Ks + sg * SBK;
   unsigned char* const Vg = Vs + sg * SB;
   // Which block row: with rows of similar length, XCD-aware and grouped by
   // (batch, head), the head's rows longest first (K and V of a head stay in
@@ -137,25 +162,36 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
   const int64_t zh = (int64_t)z * H + h;
   const int64_t Nq = (int64_t)nbr * BLK, Nk = (int64_t)nbc * BLK;
   const int q_lo = r * BLK + wave * 32;  // first query row of this wave
-  const u16* Kz = K + zh * Nk * D;
+  const unsigned char* Kz = static_cast<const unsigned char*>(Kv) + zh * Nk * RBK;
   const u16* Vz = V + zh * Nk * D;
 
   // ---- Q of both tiles as B fragments (8 values of one row per lane);
   // only the sign of scale*log2(e) is folded in (exact in 16 bits)
   V8 qf[2][NQ];
+  i32x8 qf8[2];  // fp8: 32 bytes of one row per lane (d 32 g .. 32 g + 31)
   const float sgn = c > 0.f ? 1.f : (c < 0.f ? -1.f : 0.f);
   const float cs_in = (c == 0.f) ? 1.f : fabsf(c);
   // with dense masks the scores become s * |c| + log2(e) * mask (log2 units)
   const float cs = MASKED ? 1.f : cs_in;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const u16* pq = Q + (zh * Nq + q_lo + 16 * t + li) * D + g * 8;
+    if constexpr (F8) {
+      const unsigned char* pq = static_cast<const unsigned char*>(Qv) + (zh * Nq + q_lo + 16 * t + li) * D + 32 * g;
+      const i32x4 a = *reinterpret_cast<const i32x4*>(pq), b = *reinterpret_cast<const i32x4*>(pq + 16);
+      qf8[t] = i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+      if (sgn != 1.f) {  // the sign bit of every byte, or zero (both exact)
 #pragma unroll
-    for (int u = 0; u < NQ; ++u) {
-      qf[t][u] = *reinterpret_cast<const V8*>(pq + u * 32);
-      if (sgn != 1.f) {
+        for (int e = 0; e < 8; ++e) qf8[t][e] = (sgn < 0.f) ? (qf8[t][e] ^ (int)0x80808080u) : 0;
+      }
+    } else {
+      const u16* pq = static_cast<const u16*>(Qv) + (zh * Nq + q_lo + 16 * t + li) * D + g * 8;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qf[t][u][e] = HT::cvt((float)qf[t][u][e] * sgn);
+      for (int u = 0; u < NQ; ++u) {
+        qf[t][u] = *reinterpret_cast<const V8*>(pq + u * 32);
+        if (sgn != 1.f) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qf[t][u][e] = HT::cvt((float)qf[t][u][e] * sgn);
+        }
       }
     }
   }
@@ -164,35 +200,51 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
   // of a block; lane l fills slot l % CPR of row l / CPR with the chunk
   // that the swizzle puts there. The swizzle of a row depends only on the
   // parity of the instruction, so two per-lane offsets cover every one.
-  int dofs[2];
+  // Byte offsets; rows of RBK bytes (K) use the swizzle of that row size.
+  int dofs[2], dofk[2];
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     const int ri = lane / CPR, slot = lane % CPR;
-    dofs[p] = ri * D + ((slot ^ Swz<D>::f(p * RPI + ri)) * 8);
+    dofs[p] = ri * RB + ((slot ^ Swz<D>::f(p * RPI + ri)) * 16);
+    const int rk = lane / CPRK, sk = lane % CPRK;
+    dofk[p] = rk * RBK + ((sk ^ Swz<RBK / 2>::f(p * RPIK + rk)) * 16);
   }
   const int d_even = (wave & 1) ? dofs[1] : dofs[0];
   const int d_odd = (wave & 1) ? dofs[0] : dofs[1];
+  const int dk_even = (wave & 1) ? dofk[1] : dofk[0];
+  const int dk_odd = (wave & 1) ? dofk[0] : dofk[1];
   // one part of a matrix: the KS rows of one sub-step (the whole block
-  // with one sub-step); NIP instructions per wave
-  constexpr int NIP = NI / NSUB;
-  auto dma = [&](const u16* gpart, unsigned char* spart) {
+  // with one sub-step); NIV (V) and NIK (K) instructions per wave
+  constexpr int NIV = NI / NSUB;
+  constexpr int NIK = SBK / 1024 / NW / NSUB;
+  static_assert(NIK >= 1 && SBK % (1024 * NW * NSUB) == 0, "whole K DMA instructions per wave");
+  auto dma_n = [&](const unsigned char* gpart, unsigned char* spart, int n, int de, int dodd) {
 #pragma unroll
-    for (int i = 0; i < NIP; ++i) {
-      const int I = wave + NW * i;  // uniform
-      const u16* src = gpart + I * RPI * D + (((NW * i) & 1) ? d_odd : d_even);
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_u8*)(spart + I * 1024), 16, 0, 0);
+    for (int i = 0; i < NIV; ++i) {
+      if (i < n) {
+        const int I = wave + NW * i;  // uniform
+        const unsigned char* src = gpart + I * 1024 + (((NW * i) & 1) ? dodd : de);
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_u8*)(spart + I * 1024), 16, 0, 0);
+      }
     }
   };
-  auto kpart = [&](int e, int x) { return Kz + (int64_t)col_idx[e] * BLK * D + x * KS * D; };
-  auto vpart = [&](int e, int x) { return Vz + (int64_t)col_idx[e] * BLK * D + x * KS * D; };
+  auto dmaK = [&](const unsigned char* gpart, unsigned char* spart) { dma_n(gpart, spart, NIK, dk_even, dk_odd); };
+  auto dmaV = [&](const unsigned char* gpart, unsigned char* spart) { dma_n(gpart, spart, NIV, d_even, d_odd); };
+  auto kpart = [&](int e, int x) { return Kz + ((int64_t)col_idx[e] * BLK + x * KS) * RBK; };
+  auto vpart = [&](int e, int x) {
+    return reinterpret_cast<const unsigned char*>(Vz) + ((int64_t)col_idx[e] * BLK + x * KS) * RB;
+  };
 
   // ---- LDS read offsets (bytes). K: lane (g, li) reads row 16 jt + li,
   // chunk 4u + g; V: lane (g, 4k + m) reads row 4g + k, the 8 bytes at
   // column 16 nt + 4m. Row offsets that are multiples of 16 do not change
   // the swizzle and go into the instruction offsets.
-  int koff[NQ], voff[NNT];
+  int koff[NQ], voff[NNT], koff8[2];
 #pragma unroll
-  for (int u = 0; u < NQ; ++u) koff[u] = li * RB + (((4 * u + g) ^ Swz<D>::f(li)) * 16);
+  for (int u = 0; u < NQ; ++u) koff[u] = li * RBK + (((4 * u + g) ^ Swz<RBK / 2>::f(li)) * 16);
+  // fp8: lane (g, li) reads bytes 32 g .. 32 g + 31 of K row 16 jt + li
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) koff8[hh] = li * RBK + (((2 * g + hh) ^ Swz<RBK / 2>::f(li)) * 16);
   {
     const int k = li >> 2, m = li & 3, vr = 4 * g + k;
 #pragma unroll
@@ -220,13 +272,13 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
   // Every barrier is block-wide (all key groups); transfers complete in
   // issue order, so each wait names how many later ones may stay in flight.
   const int nsteps = (k1 - k0 + NS - 1) / NS;
-  unsigned char* const Kp[2] = {Kg, Kg + KS * RB};
+  unsigned char* const Kp[2] = {Kg, Kg + KS * RBK};
   unsigned char* const Vp[2] = {Vg, Vg + KS * RB};
   if (k0 + sg < k1) {
-    dma(kpart(k0 + sg, 0), Kp[0]);
+    dmaK(kpart(k0 + sg, 0), Kp[0]);
     if constexpr (NSUB == 2) {
-      dma(vpart(k0 + sg, 0), Vp[0]);
-      dma(kpart(k0 + sg, 1), Kp[1]);
+      dmaV(vpart(k0 + sg, 0), Vp[0]);
+      dmaK(kpart(k0 + sg, 1), Kp[1]);
     }
   }
   for (int step = 0; step < nsteps; ++step) {
@@ -237,7 +289,7 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
     if constexpr (NSUB == 1) {
       wait_vmcnt0();
       __syncthreads();  // [A]
-      if (valid) dma(vpart(kk, 0), Vp[0]);
+      if (valid) dmaV(vpart(kk, 0), Vp[0]);
     }
     const bool mask_block = CAUSAL && (cb * BLK + BLK - 1 > q_lo);
     const bool compute = valid && !(CAUSAL && cb * BLK > q_lo + 31);
@@ -249,9 +301,9 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
         // [S sub]: later transfers in flight: V(this, 0) and K(this, 1)
         // before sub-step 0; V(this, 1) and K(next, 0) before sub-step 1
         if (sub == 0) {
-          if (valid) wait_vmcnt<2 * NIP>(); else wait_vmcnt0();
+          if (valid) wait_vmcnt<NIK + NIV>(); else wait_vmcnt0();
         } else {
-          if (has_next) wait_vmcnt<2 * NIP>(); else if (valid) wait_vmcnt<NIP>(); else wait_vmcnt0();
+          if (has_next) wait_vmcnt<NIK + NIV>(); else if (valid) wait_vmcnt<NIV>(); else wait_vmcnt0();
         }
         __syncthreads();
       }
@@ -281,7 +333,29 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
       }
       f32x4 s[2][NJT];
       // ---- S^T = K Q^T for both tiles
-      if (compute) {
+      if constexpr (F8) {
+        if (compute) {
+          // one 16x16x128 fp8 product per key tile and query tile; the K
+          // operand (32 bytes a lane) of tile jt+1 is read while tile jt
+          // is multiplied
+          auto ldk = [&](int jt) {
+            const i32x4 a = *reinterpret_cast<const i32x4*>(Kc + 16 * jt * RBK + koff8[0]);
+            const i32x4 b = *reinterpret_cast<const i32x4*>(Kc + 16 * jt * RBK + koff8[1]);
+            return i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+          };
+          i32x8 ka8[2];
+          ka8[0] = ldk(0);
+#pragma unroll
+          for (int jt = 0; jt < NJT; ++jt) {
+            if (jt + 1 < NJT) ka8[(jt + 1) & 1] = ldk(jt + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+            // format codes 0 (FP8 E4M3) for both operands, no block scales
+            s[0][jt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka8[jt & 1], qf8[0], zero, 0, 0, 0, 0, 0, 0);
+            s[1][jt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka8[jt & 1], qf8[1], zero, 0, 0, 0, 0, 0, 0);
+          }
+        }
+      } else if (compute) {
         // the K operands of tile jt+1 are read while tile jt is multiplied
         V8 ka[2][NQ];
 #pragma unroll
@@ -291,7 +365,7 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
           if (jt + 1 < NJT) {
 #pragma unroll
             for (int u = 0; u < NQ; ++u)
-              ka[(jt + 1) & 1][u] = *reinterpret_cast<const V8*>(Kc + 16 * (jt + 1) * RB + koff[u]);
+              ka[(jt + 1) & 1][u] = *reinterpret_cast<const V8*>(Kc + 16 * (jt + 1) * RBK + koff[u]);
           }
           __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the products
           s[0][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -309,20 +383,20 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
         // otherwise be queued ahead of them (measured 3-5% faster on
         // random_b128_bf16 than issuing it right after the barrier)
         if (sub == 0) {
-          if (valid) dma(vpart(kk, 1), Vp[1]);
+          if (valid) dmaV(vpart(kk, 1), Vp[1]);
         } else {
-          if (has_next) dma(vpart(kk + NS, 0), Vp[0]);
+          if (has_next) dmaV(vpart(kk + NS, 0), Vp[0]);
         }
         // [P sub]: later transfers in flight: K(this, 1) and V(this, 1)
         // before sub-step 0's P.V; K(next, 0) and V(next, 0) before
         // sub-step 1's
         if (sub == 0) {
-          if (valid) wait_vmcnt<2 * NIP>(); else wait_vmcnt0();
+          if (valid) wait_vmcnt<NIK + NIV>(); else wait_vmcnt0();
         } else {
-          if (has_next) wait_vmcnt<2 * NIP>(); else wait_vmcnt0();
+          if (has_next) wait_vmcnt<NIK + NIV>(); else wait_vmcnt0();
         }
         __syncthreads();
-        if (has_next) dma(kpart(kk + NS, sub), Kp[sub]);
+        if (has_next) dmaK(kpart(kk + NS, sub), Kp[sub]);
       }
 
       // ---- softmax of both tiles
@@ -372,7 +446,7 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
       if constexpr (NSUB == 1) {
         wait_vmcnt0();    // this wave's part of V (the only transfer in flight)
         __syncthreads();  // [B]
-        if (has_next) dma(kpart(kk + NS, 0), Kp[0]);
+        if (has_next) dmaK(kpart(kk + NS, 0), Kp[0]);
       }
       if (!compute) continue;
 
@@ -477,7 +551,7 @@ int launch_ns(const bs_layout* L, const AttnArgs& a, float c, hipStream_t s) {
   const bool masked = a.am != nullptr || a.kp != nullptr;
 #define BSA_WIDE_LAUNCH(CA, MA)                                                                                   \
   hipLaunchKernelGGL((k_attn_wide<E, BLK, D, CA, NS, MA>), grid, block, 0, s, L->row_ptr, L->col_idx,            \
-                     L->row_order, L->row_order_h, (const u16*)Q, (const u16*)K, (const u16*)V, (u16*)O, Z, L->H, \
+                     L->row_order, L->row_order_h, Q, K, (const u16*)V, (u16*)O, Z, L->H,                         \
                      L->nbr, L->nbc, c, grouped, a.lse, a.am, a.kp)
   if (a.causal) {
     if (masked) BSA_WIDE_LAUNCH(true, true);
@@ -497,7 +571,7 @@ int launch_ns(const bs_layout* L, const AttnArgs& a, float c, hipStream_t s) {
 template <typename E, int BLK, int D>
 int run(const bs_layout* L, const AttnArgs& a, float c, hipStream_t s) {
   const int Z = a.Z;
-  using Cfg = WideCfg<BLK, D>;
+  using Cfg = WideCfg<BLK, D, WideTypes<E>::F8 ? D : 2 * D>;
   constexpr size_t cap = 160 * 1024;
   // four groups of a 128-block row would be 1024 threads, at most 128
   // VGPRs a lane, which the causal variant exceeded (it spilled)
@@ -536,6 +610,9 @@ int launch_attention_wide(const bs_layout* L, const AttnArgs& a, hipStream_t s) 
   } else if (a.dt == BS_F16) {
     if (a.d == 64) return run_b<f16_t, 64>(L, a, c, s);
     if (a.d == 128) return run_b<f16_t, 128>(L, a, c, s);
+  } else if (a.dt == BS_F8E4M3) {
+    // one 16x16x128 fp8 product per tile covers d = 128
+    if (a.d == 128) return run_b<f8_t, 128>(L, a, c, s);
   }
   return kNotApplicable;
 }

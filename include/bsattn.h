@@ -51,8 +51,15 @@ typedef struct bs_layout* bs_layout_t;
    float32): IEEE binary32, bfloat16 or IEEE binary16. With the 16-bit types
    the products run on the 16-bit matrix cores with float32 accumulation;
    float32 values that feed a product (P, S) are rounded to the operand type
-   (round to nearest even) and results are rounded once at the end. */
-typedef enum { BS_F32 = 0, BS_BF16 = 1, BS_F16 = 2 } bs_dtype;
+   (round to nearest even) and results are rounded once at the end.
+   BS_F8E4M3 (fused attention only: bs_attention, bs_attention_masked,
+   bs_attention_fwd; d = 128 and blocks of 32, 64 or 128): Q and K are OCP
+   FP8 E4M3 bytes, taken as the values they encode (no scale factors), and
+   the score product runs on the fp8 matrix cores (exact products, float32
+   accumulation); V and O are bfloat16 and P is rounded to bfloat16 for the
+   P.V product, as with BS_BF16. Every other call returns
+   BS_ERR_UNSUPPORTED for it. */
+typedef enum { BS_F32 = 0, BS_BF16 = 1, BS_F16 = 2, BS_F8E4M3 = 3 } bs_dtype;
 
 /* flags for bs_softmax / bs_attention */
 enum { BS_CAUSAL = 1 };

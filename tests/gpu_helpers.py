@@ -1,6 +1,8 @@
 """Shared helpers of the GPU parity tests (inputs come from `workloads`,
 expected values only from `oracle`)."""
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -14,6 +16,17 @@ import oracle
 # rounding of an output below 4 adds at most 2^-10 = 9.8e-4. fp16 x fp16
 # products are exact in fp32 and the fp32 accumulation adds ~1e-6.
 TOL = {"f32": 1e-4, "bf16": 2e-2, "f16": 5e-3}
+
+
+# worker threads for the oracle's full-size references (numpy releases the
+# interpreter lock inside its kernels; one BLAS thread per worker)
+WORKERS = max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def pool_map(fn, chunks):
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1), ThreadPoolExecutor(WORKERS) as ex:
+        return list(ex.map(fn, chunks))
 
 
 def announce(*parts):

@@ -39,7 +39,7 @@ def test_header_constants_match_binding():
     """The dtype, flag and error codes the binding passes are the header's."""
     src = open(HEADER).read()
     vals = {m.group(1): int(m.group(2)) for m in re.finditer(r"\b(BS_[A-Z0-9_]+)\s*=\s*(-?\d+)", src)}
-    for name in ("BS_F32", "BS_BF16", "BS_F16", "BS_CAUSAL", "BS_TRANS_A", "BS_TRANS_B", "BS_OK", "BS_ERR_INVALID_ARG", "BS_ERR_UNSUPPORTED",
+    for name in ("BS_F32", "BS_BF16", "BS_F16", "BS_F8E4M3", "BS_CAUSAL", "BS_TRANS_A", "BS_TRANS_B", "BS_OK", "BS_ERR_INVALID_ARG", "BS_ERR_UNSUPPORTED",
                  "BS_ERR_SHAPE", "BS_ERR_HIP", "BS_ERR_OOM", "BS_ERR_NO_DEVICE"):
         assert vals[name] == getattr(_lib, name), name
 

@@ -15,24 +15,18 @@ up. Then:
 The oracle's rows are computed in a thread pool (numpy releases the
 interpreter lock in its kernels), with one BLAS thread per worker.
 """
-import os
-from concurrent.futures import ThreadPoolExecutor
-
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import workloads as W
-from gpu_helpers import (TOL, announce, f64, max_abs, oracle_block_sdd, oracle_row_softmax, sample_rows,
-                         to_dev)
+from gpu_helpers import (TOL, WORKERS, announce, f64, max_abs, oracle_block_sdd, oracle_row_softmax, pool_map,
+                         sample_rows, to_dev)
 
 pytestmark = pytest.mark.gpu
 
 bsa = pytest.importorskip("block_sparse_matmul_amd")
-
-WORKERS = max(1, min(16, len(os.sched_getaffinity(0))))
-
 
 def _setup(w):
     lay = W.make_layout(w)
@@ -46,12 +40,6 @@ def _setup(w):
 
 def _nan_like(t):
     return torch.full_like(t, float("nan"))
-
-
-def _pool_map(fn, chunks):
-    from threadpoolctl import threadpool_limits
-    with threadpool_limits(1), ThreadPoolExecutor(WORKERS) as ex:
-        return list(ex.map(fn, chunks))
 
 
 def oracle_all_rows(w, lay, q, k, v):
@@ -68,7 +56,7 @@ def oracle_all_rows(w, lay, q, k, v):
         def run(chunk):
             return list(oracle.attention_rows(Q, K, V, lay, b, w.scale, w.causal, chunk))
     out = np.zeros(Q.shape[:3] + (V.shape[3],))
-    for chunk, res in zip(chunks, _pool_map(run, chunks)):
+    for chunk, res in zip(chunks, pool_map(run, chunks)):
         for (z, h, r), o in zip(chunk, res):
             out[z, h, r * b:(r + 1) * b] = o
     return out
