@@ -19,6 +19,9 @@ element). Rank 0 prints one JSON line with, besides the contract fields:
   ops           the unfused three-call path (SDD, softmax, DSD), the
                 standalone DDS where the workload has one, and the one-time
                 layout build, each timed on its own after two untimed calls
+  kv_share      on a layout with a K/V sharing plan (slope-1 ACSR): the
+                plan and the kernel time with it (off by default), for
+                comparison
   fused_other_workloads
                 the fused kernel's time, TFLOP/s and roofline fraction on
                 each of the other workloads
@@ -70,6 +73,7 @@ def _source_hash(files):
 
 
 ATTN_SOURCES = ["block_sparse_matmul_amd/csrc/attention.hip", "block_sparse_matmul_amd/csrc/attention_wide.hip",
+                "block_sparse_matmul_amd/csrc/attention_band.hip",
                 "block_sparse_matmul_amd/csrc/rowblock.h", "block_sparse_matmul_amd/csrc/tile.h",
                 "block_sparse_matmul_amd/csrc/internal.h"]
 
@@ -203,12 +207,26 @@ def run_workload(w, steps, warmup, with_ops=True, with_cpu=True):
     achieved = flops / (kern_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     traffic = _traffic(w.name, flops)
+    share = None
+    rows, stride = L.kv_share()
+    if rows > 1:
+        # the fused kernel with the K/V sharing across block rows (off by
+        # default), for comparison
+        L.set_kv_share(True)
+        for _ in range(2):
+            step()
+        t_sh = _events_time(step, max(10, steps // 2), stream)
+        L.set_kv_share(False)
+        share = {"rows": rows, "stride": stride, "kernel_ms": round(kern_ms, 4),
+                 "shared_kernel_ms": round(t_sh, 4), "speedup": round(kern_ms / t_sh, 4)}
     res = {
         "wall_ms": wall_ms, "kernel_ms": kern_ms, "tflops": tflops, "nnz": L.nnz,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic},
         "lut_build_ms": round(lut_ms, 3), "lut_build_first_ms": round(lut_first_ms, 3),
     }
+    if share:
+        res["kv_share"] = share
     if with_ops:
         ops = {}
         if True:
@@ -355,6 +373,8 @@ def main(argv=None):
             others[other.name] = {"dtype": other.dtype, "kernel_ms": round(ro["kernel_ms"], 4),
                                   "tflops": ro["roofline"]["achieved"], "frac": ro["roofline"]["frac"],
                                   "traffic": ro["roofline"]["traffic"], "nnz": ro["nnz"]}
+            if ro.get("kv_share"):
+                others[other.name]["kv_share"] = ro["kv_share"]
     line = {
         "metric": METRIC,
         "value": round(r["tflops"], 3),
@@ -375,6 +395,7 @@ def main(argv=None):
         "mfma_peak_frac": r["roofline"]["frac"],
         "cpu_baseline": r.get("cpu_baseline"),
         "ops": r.get("ops"),
+        "kv_share": r.get("kv_share"),
         "fused_other_workloads": others or None,
         "lut_build_ms": r["lut_build_ms"],
         "lut_build_first_ms": r["lut_build_first_ms"],

@@ -117,6 +117,18 @@ class Layout:
         check(lib().bs_layout_nnz(self._h, C.byref(nnz)))
         self.H, self.nbr, self.nbc, self.block, self.nnz = H.value, nbr.value, nbc.value, b.value, nnz.value
 
+    def kv_share(self) -> Tuple[int, int]:
+        """(rows, stride) of the K/V sharing plan: block rows per workgroup
+        of the fused attention and their distance; (1, 0) without a plan."""
+        rows, stride = C.c_int(), C.c_int()
+        check(lib().bs_layout_kv_share(self.handle, C.byref(rows), C.byref(stride)))
+        return rows.value, stride.value
+
+    def set_kv_share(self, enable: bool) -> None:
+        """Use (True) or skip (False, the default) the sharing plan in the
+        fused attention."""
+        check(lib().bs_layout_set_kv_share(self.handle, 1 if enable else 0))
+
     @property
     def handle(self) -> C.c_void_p:
         if self._h is None:

@@ -42,6 +42,8 @@ SIGNATURES = {
     "bs_layout_build": (_i, [_vp, _i, _i, _i, _i, _vp, C.POINTER(_vp)]),
     "bs_layout_build_acsr": (_i, [C.POINTER(AcsrTerm), _i, _i, _i, _i, _i, _vp, C.POINTER(_vp)]),
     "bs_layout_nnz": (_i, [_vp, _i64p]),
+    "bs_layout_kv_share": (_i, [_vp, _ip, _ip]),
+    "bs_layout_set_kv_share": (_i, [_vp, _i]),
     "bs_layout_info": (_i, [_vp, _ip, _ip, _ip, _ip, _i64p]),
     "bs_layout_export": (_i, [_vp, _i32p, _i32p, _i32p, _i32p, _i32p]),
     "bs_layout_free": (None, [_vp]),

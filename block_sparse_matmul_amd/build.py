@@ -23,7 +23,7 @@ LIB = os.path.join(HERE, "libbsattn.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "lut.hip", "sdd.hip", "softmax.hip", "dsd.hip", "dds.hip", "attention.hip",
-           "attention_wide.hip", "attention_masked.hip",
+           "attention_wide.hip", "attention_masked.hip", "attention_band.hip",
            "backward.hip"]
 
 # Packed fp32 VALU forms are kept off (the compiler would otherwise fuse

@@ -165,6 +165,80 @@ int bs_layout_build(const uint8_t* layout, int H, int nbr, int nbc, int block, v
   return finish_build(L, layout, (hipStream_t)stream, out);
 }
 
+// K/V sharing plan for a slope-1 ACSR layout with offset set d (sorted):
+// the fused attention kernel of attention_band.hip runs G = 2 block rows per
+// workgroup, rows r0, r0 + t, ..., r0 + (G-1) t, and stages the union of
+// their columns once. The row stride t (1..64, with G rows on
+// the grid) is the one whose union U of d, d + t, ..., d + (G-1) t is
+// smallest; the plan is kept when U is at most two thirds of the G |d|
+// blocks the rows hold between them. Groups: for each residue of r0 mod t,
+// runs of G rows of that residue; listed longest first (blocks of U on the
+// grid that a row of the group holds), ties by r0.
+static int plan_share(bs_layout* L, const std::vector<int32_t>& d) {
+  if ((L->block != 32 && L->block != 64) || L->nbr < 2 || d.empty()) return BS_OK;
+  constexpr int G = 2;
+  const int tmax = std::min(64, (L->nbr - 1) / (G - 1));
+  int best_t = 0;
+  std::vector<std::pair<int32_t, int32_t>> best;  // (offset, row mask), ascending
+  for (int t = 1; t <= tmax; ++t) {
+    std::vector<std::pair<int32_t, int32_t>> u;
+    u.reserve(d.size() * G);
+    for (int jj = 0; jj < G; ++jj)
+      for (int32_t o : d) u.emplace_back(o + jj * t, 1 << jj);
+    std::sort(u.begin(), u.end());
+    std::vector<std::pair<int32_t, int32_t>> m;  // merge equal offsets
+    for (const auto& e : u) {
+      if (!m.empty() && m.back().first == e.first) m.back().second |= e.second;
+      else m.push_back(e);
+    }
+    if (best_t == 0 || m.size() < best.size()) {
+      best_t = t;
+      best = std::move(m);
+    }
+  }
+  if (best_t == 0 || 3 * best.size() > 2 * (size_t)G * d.size()) return BS_OK;
+  const int t = best_t;
+  std::vector<std::pair<int64_t, int32_t>> groups;  // (-length, r0)
+  for (int rho = 0; rho < t && rho < L->nbr; ++rho) {
+    for (int r0 = rho; r0 < L->nbr; r0 += G * t) {
+      int vm = 0;
+      for (int jj = 0; jj < G; ++jj)
+        if (r0 + jj * t < L->nbr) vm |= 1 << jj;
+      int64_t len = 0;
+      for (const auto& e : best)
+        if (r0 + e.first >= 0 && r0 + e.first < L->nbc && (e.second & vm)) ++len;
+      groups.emplace_back(-len, r0);
+    }
+  }
+  std::sort(groups.begin(), groups.end());
+  const size_t n = best.size(), ng = groups.size();
+  std::vector<int32_t> host(2 * n + ng);
+  for (size_t i = 0; i < n; ++i) {
+    host[i] = best[i].first;
+    host[n + i] = best[i].second;
+  }
+  for (size_t i = 0; i < ng; ++i) host[2 * n + i] = groups[i].second;
+  int32_t* dev = nullptr;
+  if (bsa::dev_alloc(&dev, host.size() * sizeof(int32_t)) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(BS_ERR_OOM, "device allocation of the K/V sharing plan failed");
+  }
+  hipError_t e = hipMemcpy(dev, host.data(), host.size() * sizeof(int32_t), hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(dev);
+    return bsa::hip_fail(e, "hipMemcpy(K/V sharing plan)");
+  }
+  L->share_mem = dev;
+  L->share_uoff = dev;
+  L->share_umask = dev + n;
+  L->share_grp = dev + 2 * n;
+  L->share_n = (int)n;
+  L->share_ngrp = (int)ng;
+  L->share_stride = t;
+  L->share_rows = G;
+  return BS_OK;
+}
+
 // ACSR terms analysed on the host (SPLAT's just-in-time reading of the
 // format): when every term has slope 1 and covers every row, the columns of
 // row r are r + d for d in one set of relative offsets (the union of the
@@ -200,7 +274,7 @@ static int analyse_band(bs_layout* L, const bs_acsr_term* terms, int n_terms) {
   }
   L->band_off = dev;
   L->band_n = (int)d.size();
-  return BS_OK;
+  return plan_share(L, d);
 }
 
 int bs_layout_build_acsr(const bs_acsr_term* terms, int n_terms, int H, int nbr, int nbc, int block, void* stream,
@@ -260,6 +334,21 @@ int bs_layout_nnz(bs_layout_t L, int64_t* nnz) {
   return BS_OK;
 }
 
+int bs_layout_kv_share(bs_layout_t L, int* rows, int* stride) {
+  if (int rc = check_handle(L)) return rc;
+  if (!rows || !stride) return fail(BS_ERR_INVALID_ARG, "rows or stride pointer is NULL");
+  *rows = L->share_n > 0 ? L->share_rows : 1;
+  *stride = L->share_n > 0 ? L->share_stride : 0;
+  return BS_OK;
+}
+
+int bs_layout_set_kv_share(bs_layout_t L, int enable) {
+  if (int rc = check_handle(L)) return rc;
+  if (enable != 0 && enable != 1) return fail(BS_ERR_INVALID_ARG, "enable must be 0 or 1");
+  L->share_on = enable == 1;
+  return BS_OK;
+}
+
 int bs_layout_info(bs_layout_t L, int* H, int* nbr, int* nbc, int* block, int64_t* nnz) {
   if (int rc = check_handle(L)) return rc;
   if (H) *H = L->H;
@@ -294,6 +383,7 @@ void bs_layout_free(bs_layout_t L) {
   if (L->col_idx) (void)hipFree(L->col_idx);  // start of the nnz allocation
   if (L->mem) (void)hipFree(L->mem);
   if (L->band_off) (void)hipFree(L->band_off);
+  if (L->share_mem) (void)hipFree(L->share_mem);
   delete L;
 }
 

@@ -14,6 +14,8 @@ int launch_attention(const bs_layout* L, const AttnArgs& at, hipStream_t s) {
     if (at.dt == BS_F8E4M3) return fail(BS_ERR_UNSUPPORTED, "BS_F8E4M3 attention: no kernel for this shape");
   }
   if (at.am != nullptr || at.kp != nullptr) return launch_attention_masked(L, at, s);
+  const int rc = launch_attention_band(L, at, s);
+  if (rc != kNotApplicable) return rc;
   Args a{at.Q, at.K, at.V, at.O, nullptr, at.Z, at.scale * kLog2e, at.causal};
   a.use_band = L->band_off != nullptr;
   a.lse = at.lse;

@@ -36,6 +36,18 @@ struct bs_layout {
   // grid (own allocation; null otherwise)
   int32_t* band_off = nullptr;
   int band_n = 0;
+  // K/V sharing across block rows on such a layout (attention_band.hip):
+  // groups of share_rows rows r0, r0 + share_stride, ...; the group's
+  // columns are r0 + share_uoff[i] (ascending), held by the rows whose bits
+  // are set in share_umask[i]; share_grp lists every group's r0, longest
+  // group first. One allocation (share_mem); share_n = 0 when there is no
+  // plan. share_on: whether the fused attention uses it.
+  int32_t* share_mem = nullptr;
+  const int32_t* share_uoff = nullptr;
+  const int32_t* share_umask = nullptr;
+  const int32_t* share_grp = nullptr;
+  int share_n = 0, share_ngrp = 0, share_stride = 0, share_rows = 1;
+  bool share_on = false;
   // non-empty block rows grouped by softmax length class (see
   // softmax_class), class 0 first, (head, row) order inside a class;
   // class c is row_cls[cls_begin[c] .. cls_begin[c+1])
@@ -184,6 +196,10 @@ int launch_dsd_rowblock(const bs_layout* L, const float* P, const void* B,
 // (blocks of 32, 64, 128, with or without dense masks); returns
 // kNotApplicable for other blocks, head sizes or types.
 int launch_attention_wide(const bs_layout* L, const AttnArgs& a, hipStream_t s);
+// The fused attention with K/V shared across block rows (float32, a layout
+// with a sharing plan, blocks of 32 with d in {64, 128} or 64 with d = 64,
+// no dense masks); kNotApplicable otherwise or when sharing is off.
+int launch_attention_band(const bs_layout* L, const AttnArgs& a, hipStream_t s);
 
 bool log_enabled();
 

@@ -114,6 +114,34 @@ int bs_layout_build_acsr(const bs_acsr_term* terms, int n_terms, int H,
    BS_ERR_INVALID_ARG for a NULL handle or output pointer. */
 int bs_layout_nnz(bs_layout_t L, int64_t* nnz);
 
+/* K/V sharing across block rows (SPLAT abstract: the regular geometry of
+   an ACSR pattern, analysed when the handle is built). On a handle from
+   bs_layout_build_acsr whose terms all have slope 1 and cover every row,
+   row r holds the columns r + o for o in one offset set, so rows r and
+   r + t share the columns that the set and its shift by t have in common.
+   The handle keeps a plan when two rows r and r + stride hold at least 1.5
+   times as many blocks as the union of their columns, for the stride (1 to
+   64) with the smallest union. With sharing on (bs_layout_set_kv_share),
+   the fused attention with float32 operands, no dense masks, and blocks of
+   32 (head_dim 64 or 128) or 64 (head_dim 64) then runs `rows` = 2 block
+   rows r0, r0 + stride per workgroup and stages each K/V block of their
+   union once. Each row still adds up its own blocks in ascending column
+   order with the same arithmetic as the one-row kernel, so the output has
+   the same bits as with sharing off whenever the one-row kernel runs one
+   key group per row. bs_layout_kv_share reports the plan: *rows = 1 and
+   *stride = 0 when the handle has none. Errors: BS_ERR_INVALID_ARG for a
+   NULL handle or output pointer. */
+int bs_layout_kv_share(bs_layout_t L, int* rows, int* stride);
+
+/* enable = 1: the fused attention uses the handle's sharing plan where one
+   applies; 0 (the default): one block row per workgroup (on the float32
+   strided workload the two measured the same, 389 and 391 us, the kernel
+   being bound by the matrix cores rather than by staging). Read when a call
+   is issued (calls already on a stream keep their kernel); not synchronised
+   with calls on the same handle from other host threads. Errors:
+   BS_ERR_INVALID_ARG for a NULL handle or enable other than 0 or 1. */
+int bs_layout_set_kv_share(bs_layout_t L, int enable);
+
 /* Sizes of a handle (any output pointer may be NULL). */
 int bs_layout_info(bs_layout_t L, int* H, int* nbr, int* nbc, int* block,
                    int64_t* nnz);

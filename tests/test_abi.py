@@ -23,7 +23,8 @@ def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("bs_layout_build", "bs_layout_build_acsr", "bs_layout_nnz", "bs_sdd", "bs_softmax", "bs_dsd", "bs_dds",
               "bs_attention", "bs_last_error", "bs_layout_free", "bs_layout_export",
-              "bs_softmax_backward", "bs_dsd_t", "bs_attention_backward"):
+              "bs_softmax_backward", "bs_dsd_t", "bs_attention_backward", "bs_layout_kv_share",
+              "bs_layout_set_kv_share"):
         assert n in names
 
 
@@ -93,6 +94,10 @@ def test_compute_calls_reject_null_handle():
     n = C.c_int64(-1)
     assert L.bs_layout_nnz(None, C.byref(n)) == _lib.BS_ERR_INVALID_ARG and n.value == -1
     assert L.bs_layout_export(None, None, None, None, None, None) == _lib.BS_ERR_INVALID_ARG
+    rows, stride = C.c_int(-1), C.c_int(-1)
+    assert L.bs_layout_kv_share(None, C.byref(rows), C.byref(stride)) == _lib.BS_ERR_INVALID_ARG
+    assert rows.value == -1 and stride.value == -1
+    assert L.bs_layout_set_kv_share(None, 1) == _lib.BS_ERR_INVALID_ARG
     L.bs_layout_free(None)  # ignored
 
 

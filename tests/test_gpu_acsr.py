@@ -4,7 +4,9 @@ fused kernel computes each row's columns from one sorted set of relative
 offsets instead of reading the column table; the order of the blocks is the
 same ascending order, so the output must equal, bit for bit, the output for
 the same pattern built from a dense layout. Other ACSR layouts keep the
-tables. Parity against the oracle as for every layout.
+tables. Parity against the oracle as for every layout. These tests keep the K/V
+sharing across rows off (its kernel has tests of its own) except where
+named.
 """
 import numpy as np
 import pytest
@@ -45,6 +47,7 @@ def test_slope1_acsr_attention_equals_dense_layout_and_oracle(case, b, causal):
     announce("acsr attention", case, b, causal)
     q, k, v = _qkv(Z, H, nb * b, d, 30 + case)
     La = bsa.Layout.acsr(terms, H, nb, nb, b)
+    La.set_kv_share(False)
     Ld = bsa.Layout(torch.from_numpy(lay), b)
     Oa = bsa.attention(La, to_dev(q), to_dev(k), to_dev(v), 0.125, causal)
     Od = bsa.attention(Ld, to_dev(q), to_dev(k), to_dev(v), 0.125, causal)
@@ -67,15 +70,23 @@ def test_non_slope1_acsr_keeps_the_tables():
 
 def test_strided_workload_acsr_path_bit_equal_to_table_path():
     """The strided workload at full size: the fused kernel from 76 column
-    offsets gives the same bits as from its 180,736-entry column table."""
+    offsets gives the same bits as from its 180,736-entry column table; so
+    does the kernel that shares K/V across rows (one key group per row, as
+    the table path runs this workload: the same blocks in the same order
+    with the same arithmetic)."""
     w = W.workload("strided_acsr_b32")
     announce("acsr strided full size")
     q, k, v = (to_dev(t) for t in W.make_qkv(w))
     La = bsa.Layout.acsr(W.make_acsr(w), w.H, w.nb, w.nb, w.block)
     Ld = bsa.Layout(torch.from_numpy(W.make_layout(w)), w.block)
+    assert La.kv_share() == (2, 4)
+    La.set_kv_share(True)
+    Os = bsa.attention(La, q, k, v, w.scale, w.causal)
+    La.set_kv_share(False)
     Oa = bsa.attention(La, q, k, v, w.scale, w.causal)
     Od = bsa.attention(Ld, q, k, v, w.scale, w.causal)
     assert torch.equal(Oa, Od)
+    assert torch.equal(Os, Od)
 
 
 @pytest.mark.parametrize("b", [16, 64])
@@ -94,6 +105,7 @@ def test_slope1_acsr_with_masks_lse_and_fused_backward(b):
     kp[1, N // 2:] = -float("inf")
     do = torch.randn((Z, H, N, d), generator=g)
     La = bsa.Layout.acsr(terms, H, nb, nb, b)
+    La.set_kv_share(False)
     Ld = bsa.Layout(torch.from_numpy(lay), b)
     qd, kd, vd, kpd = to_dev(q), to_dev(k), to_dev(v), to_dev(kp)
     Oa, la = bsa.attention(La, qd, kd, vd, 0.125, True, key_padding_mask=kpd, return_lse=True)
