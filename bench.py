@@ -72,13 +72,16 @@ def _source_hash(files):
     return h.hexdigest()[:16]
 
 
-ATTN_SOURCES = ["block_sparse_matmul_amd/csrc/attention.hip", "block_sparse_matmul_amd/csrc/attention_wide.hip",
-                "block_sparse_matmul_amd/csrc/attention_band.hip",
-                "block_sparse_matmul_amd/csrc/rowblock.h", "block_sparse_matmul_amd/csrc/tile.h",
-                "block_sparse_matmul_amd/csrc/internal.h"]
+# the sources each dtype's fused kernel is built from (dispatch included): a
+# committed traffic figure counts only while they are unchanged
+_C = "block_sparse_matmul_amd/csrc/"
+ATTN_SOURCES = {
+    "f32": [_C + "attention.hip", _C + "rowblock.h", _C + "tile.h", _C + "internal.h"],
+    "bf16": [_C + "attention.hip", _C + "attention_wide.hip", _C + "tile.h", _C + "internal.h"],
+}
 
 
-def _traffic(workload, launches_flops):
+def _traffic(workload, dtype):
     """HBM bytes per launch of the fused kernel from committed counters."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
     if not os.path.exists(path):
@@ -88,7 +91,7 @@ def _traffic(workload, launches_flops):
         if "=" in line and not line.lstrip().startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_hash") != _source_hash(ATTN_SOURCES):
+    if kv.get("source_hash") != _source_hash(ATTN_SOURCES[dtype]):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -206,7 +209,7 @@ def run_workload(w, steps, warmup, with_ops=True, with_cpu=True):
     tflops = flops / (wall_ms * 1e-3) / 1e12
     achieved = flops / (kern_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    traffic = _traffic(w.name, flops)
+    traffic = _traffic(w.name, w.dtype)
     share = None
     rows, stride = L.kv_share()
     if rows > 1:
