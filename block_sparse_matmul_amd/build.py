@@ -24,7 +24,7 @@ ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "lut.hip", "sdd.hip", "softmax.hip", "dsd.hip", "dds.hip", "attention.hip",
            "attention_wide.hip", "attention_masked.hip", "attention_band.hip",
-           "backward.hip"]
+           "backward.hip", "backward_wide.hip"]
 
 # Packed fp32 VALU forms are kept off (the compiler would otherwise fuse
 # pairs of fp32 ops into v_pk_* instructions). MFMA results are kept in

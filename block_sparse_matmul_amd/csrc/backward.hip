@@ -496,6 +496,8 @@ int bwd_scratch(float** out) {
 }
 
 int launch_attention_bwd(const bs_layout* L, const BwdArgs& a, hipStream_t s) {
+  const int rc = launch_attention_bwd_wide(L, a, s);
+  if (rc != kNotApplicable) return rc;
   if (a.dt == BS_BF16) return run_e<bf16_t>(L, a, s);
   if (a.dt == BS_F16) return run_e<f16_t>(L, a, s);
   return run_e<float>(L, a, s);

@@ -153,6 +153,9 @@ struct BwdArgs {
   const float* kp = nullptr;
 };
 int launch_attention_bwd(const bs_layout* L, const BwdArgs& a, hipStream_t s);
+// The fused backward with 32 rows per wave and LDS DMA staging (16-bit
+// operands, blocks of 64 or 128, no dense masks); kNotApplicable otherwise.
+int launch_attention_bwd_wide(const bs_layout* L, const BwdArgs& a, hipStream_t s);
 
 // The D buffer of bs_attention_bwd_noalloc: float32 [kBwdScratchRows], a
 // static device array (backward.hip); *out receives its address on the
