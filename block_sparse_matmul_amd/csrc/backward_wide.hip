@@ -18,7 +18,11 @@
 //    transposing reads (ds_read_b64_tr_b16) are both free of bank conflicts;
 //  * each block moves in two halves; a half is fetched as soon as every
 //    wave is done with the half it replaces, and lands while the other
-//    half is computed (one barrier per half).
+//    half is computed (one barrier per half). The fetch is issued after the
+//    first chunk's row products, so that its LDS writes do not queue ahead
+//    of their reads, and every operand of a product is requested before
+//    its first MFMA (scheduling barriers): together 2% faster on
+//    random_b128_bf16 (forward plus backward 4.94 against 5.03 ms).
 // Kernels (modes of one template):
 //  * dQ: one workgroup per (batch, head, block row); per 32-key chunk of a
 //    column block: S^T = K Q^T and dP^T = V dO^T (K, V rows from LDS, Q and
@@ -219,6 +223,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_bwd_wide(
       V8 a[NQ];
 #pragma unroll
       for (int q = 0; q < NQ; ++q) a[q] = *reinterpret_cast<const V8*>(xb + 16 * jt * RB + roff[q]);
+      __builtin_amdgcn_sched_barrier(0);
       out[0][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
       out[1][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -238,11 +243,16 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_bwd_wide(
     for (int t = 0; t < 2; ++t)
       pb[t] = V8{HT::cvt(w[t][0][0]), HT::cvt(w[t][0][1]), HT::cvt(w[t][0][2]), HT::cvt(w[t][0][3]),
                  HT::cvt(w[t][1][0]), HT::cvt(w[t][1][1]), HT::cvt(w[t][1][2]), HT::cvt(w[t][1][3])};
+    V4 a0[NNT], a1[NNT];
 #pragma unroll
     for (int nt = 0; nt < NNT; ++nt) {
-      const V4 a0 = lds_read_tr16_as<V4>(reinterpret_cast<const u16*>(xb + toff[nt]));
-      const V4 a1 = lds_read_tr16_as<V4>(reinterpret_cast<const u16*>(xb + 16 * RB + toff[nt]));
-      const V8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      a0[nt] = lds_read_tr16_as<V4>(reinterpret_cast<const u16*>(xb + toff[nt]));
+      a1[nt] = lds_read_tr16_as<V4>(reinterpret_cast<const u16*>(xb + 16 * RB + toff[nt]));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int nt = 0; nt < NNT; ++nt) {
+      const V8 a = {a0[nt][0], a0[nt][1], a0[nt][2], a0[nt][3], a1[nt][0], a1[nt][1], a1[nt][2], a1[nt][3]};
       acc[0][nt] = HT::mfma16(a, pb[0], acc[0][nt]);
       acc[1][nt] = HT::mfma16(a, pb[1], acc[1][nt]);
     }
@@ -268,9 +278,14 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_bwd_wide(
       // is done with the half about to be refetched
       __builtin_amdgcn_s_waitcnt(kVmcntZero);
       __syncthreads();
-      if (x == 0) dma_half(o, 1, 0);
-      else if (kk + 1 < k1) dma_half(idx[kk + 1], 0, (kk + 1 - k0) & 1);
-      if (!compute) continue;
+      auto issue = [&]() {
+        if (x == 0) dma_half(o, 1, 0);
+        else if (kk + 1 < k1) dma_half(idx[kk + 1], 0, (kk + 1 - k0) & 1);
+      };
+      if (!compute) {
+        issue();
+        continue;
+      }
 #pragma unroll
       for (int ch = 0; ch < NCH; ++ch) {
         const int rofs = x * HALF + 32 * ch;  // first row of the chunk within the block
@@ -279,6 +294,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_bwd_wide(
         f32x4 s[2][2], dp[2][2];
         rprod(s, x1, f1);
         if constexpr (HASDP) rprod(dp, x2, f2);
+        if (ch == 0) issue();
         // element (own row 16 t + li, other row rofs + 16 jt + 4 g + rr)
         f32x4 l4[2], d4[2];
         if constexpr (DKDV) {
