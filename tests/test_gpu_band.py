@@ -118,3 +118,24 @@ def test_band_switch():
     L.set_kv_share(True)
     L.set_kv_share(False)
     assert L.kv_share() == (2, 4)  # the plan stays; only its use is off
+
+
+@pytest.mark.parametrize("b", [32, 64])
+def test_band_attention_non_square(b):
+    """More key blocks than query blocks (the terms reach past the last
+    row's diagonal): the plan clips columns at the key grid."""
+    terms = [(0, 20, 1, -3, 1, 12), (0, 20, 1, -20, 4, 12)]
+    nbr, nbc, H, Z, d = 20, 28, 2, 2, 64
+    announce("band attention non-square", b)
+    lay = oracle.acsr_expand(terms, H, nbr, nbc)
+    g = torch.Generator("cpu").manual_seed(760 + b)
+    q = torch.randn((Z, H, nbr * b, d), generator=g)
+    k, v = (torch.randn((Z, H, nbc * b, d), generator=g) for _ in range(2))
+    L = bsa.Layout.acsr(terms, H, nbr, nbc, b)
+    assert L.kv_share()[0] == 2
+    L.set_kv_share(True)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    O = bsa.attention(L, qd, kd, vd, 0.125, out=torch.full_like(qd, float("nan")))
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(O).all())
+    assert max_abs(f64(O), oracle.attention_dense(q, k, v, lay, b, 0.125)) <= TOL["f32"]

@@ -200,5 +200,8 @@ def test_unknown_dtype_code_rejected():
     a = torch.zeros((1, 1, 32, 64), device="cuda", dtype=torch.float16)
     s = torch.zeros((1, 4, 16, 16), device="cuda")
     ptr = lambda t: C.c_void_p(t.data_ptr())
-    rc = _lib.lib().bs_sdd(L.handle, ptr(a), ptr(a), ptr(s), 1, 64, 3, None)
+    rc = _lib.lib().bs_sdd(L.handle, ptr(a), ptr(a), ptr(s), 1, 64, 4, None)
     assert rc == _lib.BS_ERR_INVALID_ARG
+    # code 3 is BS_F8E4M3, defined but taken by the fused attention only
+    rc = _lib.lib().bs_sdd(L.handle, ptr(a), ptr(a), ptr(s), 1, 64, _lib.BS_F8E4M3, None)
+    assert rc == _lib.BS_ERR_UNSUPPORTED
