@@ -349,8 +349,8 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build runs the block-sparse attention kernel on a "
-              "single MI355X (multi-GPU sharding is a design note, not implemented); use --gpus 1",
+        print("bench.py measures one GPU only: the library runs the block-sparse attention kernels on a "
+              "single MI355X (sharding across GPUs is not implemented); use --gpus 1",
               file=sys.stderr)
         return 2
     if args.calibrate_copy:

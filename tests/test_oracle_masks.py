@@ -1,7 +1,7 @@
 """Pins for the oracle's dense additive masks (question on blocksparse: dense
-masks can be passed alongside the layout; the format is this build's
-reading: attn_mask [Nq, Nk] shared by batch and heads, kp_mask [Z, Nk] per
-batch element, both added to scale * S).
+masks can be passed alongside the layout; the page gives no format, and
+the one taken here is: attn_mask [Nq, Nk] shared by batch and heads,
+kp_mask [Z, Nk] per batch element, both added to scale * S).
 
 Independent routes: torch's scaled_dot_product_attention math path in
 float64 with a float (additive) attn_mask, forward and autograd; attention
