@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_helpers import TOL, announce, f64, max_abs, to_dev
+from gpu_helpers import TOL, announce, f64, max_abs, pool_map, to_dev
 
 import block_sparse_matmul_amd as bsa
 
@@ -143,13 +143,14 @@ def test_fused_backward_masked(b, dt, causal):
         assert max_abs(f64(got), ref) <= _grad_tol(dt, ref), name
 
 
-@pytest.mark.parametrize("idx", [1, 2, 4])
-def test_fused_backward_full_size_sampled_heads(idx):
-    """causal_b64 and bigbird_b64 (fp32) at full size, the dense oracle
-    gradient of two (batch, head) pairs; random_b128_bf16 at full size (the
-    head-grouped order of the 16-bit kernels), its last head (about 10 s of
-    float64 oracle). The gradients are written over NaN, and every element
-    must come back finite (nothing left unwritten)."""
+@pytest.mark.parametrize("idx", [1, 2, 3, 4])
+def test_fused_backward_full_size(idx):
+    """causal_b64, bigbird_b64, strided_acsr_b32 (fp32) and
+    random_b128_bf16 (the 16-bit kernels, head-grouped order) at full size
+    against the dense oracle gradient of every (batch, head) pair. The dense
+    route of a random_b128_bf16 head holds about 12 GB of float64 matrices,
+    so those heads run four at a time. The gradients are written over NaN,
+    and every element must come back finite (nothing left unwritten)."""
     w = W.WORKLOADS[idx]
     lay = W.make_layout(w)
     q, k, v = W.make_qkv(w)
@@ -165,13 +166,27 @@ def test_fused_backward_full_size_sampled_heads(idx):
     for name, g in (("dq", dq), ("dk", dk), ("dv", dv)):
         assert bool(torch.isfinite(g).all()), ("unwritten gradient", name)
     dt = "f32" if q.dtype == torch.float32 else "bf16"
-    pairs = ((0, 0), (w.Z - 1, w.H - 1)) if w.dtype == "f32" else ((w.Z - 1, w.H - 1),)
-    for z, h in pairs:
+    pairs = [(z, h) for z in range(w.Z) for h in range(w.H)]
+    got = {name: f64(t) for name, t in (("dq", dq), ("dk", dk), ("dv", dv))}
+
+    def check(pair):
+        z, h = pair
         sl = (slice(z, z + 1), slice(h, h + 1))
         refs = oracle.attention_backward_dense(q[sl], k[sl], v[sl], do[sl], lay[h:h + 1], w.block, w.scale,
                                                w.causal)
-        for name, got, ref in (("dq", dq, refs[0]), ("dk", dk, refs[1]), ("dv", dv, refs[2])):
-            assert max_abs(f64(got[sl]), ref) <= _grad_tol(dt, ref), (name, z, h)
+        return [(name, max_abs(got[name][sl], ref), _grad_tol(dt, ref)) for name, ref in zip(("dq", "dk", "dv"), refs)]
+
+    if w.dtype == "f32":
+        results = pool_map(check, pairs)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(4), ThreadPoolExecutor(4) as ex:
+            results = list(ex.map(check, pairs))
+    for pair, res in zip(pairs, results):
+        for name, err, tol in res:
+            assert err <= tol, (name, pair, err)
 
 
 def test_fused_backward_empty_layout_and_empty_batch():
