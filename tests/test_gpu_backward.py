@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_helpers import TOL, announce, f64, max_abs, to_dev
+from gpu_helpers import TOL, announce, f64, max_abs, pool_map, to_dev
 
 import block_sparse_matmul_amd as bsa
 
@@ -153,9 +153,9 @@ def test_autograd_wrapper_matches_backward_entry_point_and_oracle():
         assert max_abs(f64(got), ref) <= TOL["f32"]
 
 
-def test_attention_backward_full_size_causal_b64_sampled_heads():
+def test_attention_backward_full_size_causal_b64():
     """causal_b64 at full size (the launch configuration of the forward
-    bench); the dense oracle gradient of two (batch, head) pairs."""
+    bench), every (batch, head) pair against the dense oracle gradient."""
     w = W.WORKLOADS[1]
     lay = W.make_layout(w)
     q, k, v = W.make_qkv(w)
@@ -164,8 +164,15 @@ def test_attention_backward_full_size_causal_b64_sampled_heads():
     announce("attention_backward full size", w.name)
     L = bsa.Layout(torch.from_numpy(lay), w.block)
     dq, dk, dv = bsa.attention_backward(L, to_dev(q), to_dev(k), to_dev(v), to_dev(do), w.scale, w.causal)
-    for z, h in ((0, 0), (w.Z - 1, w.H - 1)):
+    got = {"dq": f64(dq), "dk": f64(dk), "dv": f64(dv)}
+
+    def check(pair):
+        z, h = pair
         sl = (slice(z, z + 1), slice(h, h + 1))
         refs = oracle.attention_backward_dense(q[sl], k[sl], v[sl], do[sl], lay[h:h + 1], w.block, w.scale, w.causal)
-        for name, got, ref in (("dq", dq, refs[0]), ("dk", dk, refs[1]), ("dv", dv, refs[2])):
-            assert max_abs(f64(got[sl]), ref) <= TOL["f32"], (name, z, h)
+        return [(name, max_abs(got[name][sl], ref)) for name, ref in zip(("dq", "dk", "dv"), refs)]
+
+    pairs = [(z, h) for z in range(w.Z) for h in range(w.H)]
+    for pair, res in zip(pairs, pool_map(check, pairs)):
+        for name, err in res:
+            assert err <= TOL["f32"], (name, pair, err)
