@@ -20,8 +20,8 @@ element). Rank 0 prints one JSON line with, besides the contract fields:
                 standalone DDS where the workload has one, and the one-time
                 layout build, each timed on its own after two untimed calls
   kv_share      on a layout with a K/V sharing plan (slope-1 ACSR): the
-                plan and the kernel time with and without it (off by
-                default), timed in alternating rounds
+                plan and the kernel time with and without it, timed in
+                alternating rounds (the headline uses the library's default)
   fused_other_workloads
                 the fused kernel's time, TFLOP/s and roofline fraction on
                 each of the other workloads
@@ -213,16 +213,16 @@ def run_workload(w, steps, warmup, with_ops=True, with_cpu=True):
     share = None
     rows, stride = L.kv_share()
     if rows > 1:
-        # the fused kernel with and without the K/V sharing across block rows
-        # (off by default), timed in alternating rounds of 10 calls (a run
-        # timed after another starts at a different clock), medians
+        # the fused kernel with and without the K/V sharing across block rows,
+        # timed in alternating rounds of 10 calls (a run timed after another
+        # starts at a different clock), medians
         t_one, t_sh = [], []
         for r in range(7):
             for on, dst in ((False, t_one), (True, t_sh)):
                 L.set_kv_share(on)
                 step()
                 dst.append(_events_time(step, 10, stream))
-        L.set_kv_share(False)
+        L.set_kv_share(None)
         t_one, t_sh = sorted(t_one)[3], sorted(t_sh)[3]
         share = {"rows": rows, "stride": stride, "one_row_kernel_ms": round(t_one, 4),
                  "shared_kernel_ms": round(t_sh, 4), "speedup": round(t_one / t_sh, 4),

@@ -124,10 +124,12 @@ class Layout:
         check(lib().bs_layout_kv_share(self.handle, C.byref(rows), C.byref(stride)))
         return rows.value, stride.value
 
-    def set_kv_share(self, enable: bool) -> None:
-        """Use (True) or skip (False, the default) the sharing plan in the
-        fused attention."""
-        check(lib().bs_layout_set_kv_share(self.handle, 1 if enable else 0))
+    def set_kv_share(self, enable: Optional[bool]) -> None:
+        """Use (True) or skip (False) the sharing plan in the fused
+        attention; None (the default) uses it where it measured faster
+        (16-bit operands, blocks of 64)."""
+        mode = -1 if enable is None else (1 if enable else 0)
+        check(lib().bs_layout_set_kv_share(self.handle, mode))
 
     @property
     def handle(self) -> C.c_void_p:

@@ -166,8 +166,10 @@ int bs_layout_build(const uint8_t* layout, int H, int nbr, int nbc, int block, v
 }
 
 // K/V sharing plan for a slope-1 ACSR layout with offset set d (sorted):
-// the fused attention kernel of attention_band.hip runs G = 2 block rows per
-// workgroup, rows r0, r0 + t, ..., r0 + (G-1) t, and stages the union of
+// the fused attention kernels that share K/V (attention_band.hip for
+// float32, blocks of 32 and 64; the BAND mode of attention_wide.hip for
+// 16-bit operands, blocks of 32 to 128) run G = 2 block rows per
+// workgroup, rows r0, r0 + t, ..., r0 + (G-1) t, and stage the union of
 // their columns once. The row stride t (1..64, with G rows on
 // the grid) is the one whose union U of d, d + t, ..., d + (G-1) t is
 // smallest; the plan is kept when U is at most two thirds of the G |d|
@@ -175,7 +177,7 @@ int bs_layout_build(const uint8_t* layout, int H, int nbr, int nbc, int block, v
 // runs of G rows of that residue; listed longest first (blocks of U on the
 // grid that a row of the group holds), ties by r0.
 static int plan_share(bs_layout* L, const std::vector<int32_t>& d) {
-  if ((L->block != 32 && L->block != 64) || L->nbr < 2 || d.empty()) return BS_OK;
+  if (L->block < 32 || L->nbr < 2 || d.empty()) return BS_OK;
   constexpr int G = 2;
   const int tmax = std::min(64, (L->nbr - 1) / (G - 1));
   int best_t = 0;
@@ -342,10 +344,10 @@ int bs_layout_kv_share(bs_layout_t L, int* rows, int* stride) {
   return BS_OK;
 }
 
-int bs_layout_set_kv_share(bs_layout_t L, int enable) {
+int bs_layout_set_kv_share(bs_layout_t L, int mode) {
   if (int rc = check_handle(L)) return rc;
-  if (enable != 0 && enable != 1) return fail(BS_ERR_INVALID_ARG, "enable must be 0 or 1");
-  L->share_on = enable == 1;
+  if (mode < -1 || mode > 1) return fail(BS_ERR_INVALID_ARG, "mode must be -1, 0 or 1");
+  L->share_mode = mode;
   return BS_OK;
 }
 

@@ -261,7 +261,10 @@ int launch_bd(const bs_layout* L, const AttnArgs& a, hipStream_t s) {
 }  // namespace
 
 int launch_attention_band(const bs_layout* L, const AttnArgs& a, hipStream_t s) {
-  if (!L->share_on || L->share_n == 0 || a.dt != BS_F32 || a.am != nullptr || a.kp != nullptr) return kNotApplicable;
+  // float32: only on request (it measured the same time as the one-row
+  // kernel on strided_acsr_b32)
+  if (L->share_mode != 1 || L->share_n == 0 || a.dt != BS_F32 || a.am != nullptr || a.kp != nullptr)
+    return kNotApplicable;
   if (L->share_rows != 2) return kNotApplicable;
   if (L->block == 32) return a.d == 64 ? launch_bd<32, 64>(L, a, s) : launch_bd<32, 128>(L, a, s);
   if (L->block == 64 && a.d == 64) return launch_bd<64, 64>(L, a, s);

@@ -98,12 +98,24 @@ __device__ __forceinline__ void wait_vmcnt0() { wait_vmcnt<0>(); }
 // operations in flight; the mask reads join that count, which can only
 // make a wait wait for more (every operation completes in order), never
 // for less.
-template <typename E, int BLK, int D, bool CAUSAL, int NS, bool MASKED>
+//
+// BAND: K/V shared across block rows on a slope-1 ACSR layout (the sharing
+// plan of the layout; see attention_band.hip for the plan): the NS = 2
+// groups of the workgroup take block rows r0 and r0 + stride instead of
+// dealing one row's blocks; they walk the union of the two rows' columns
+// (r0 + uoff[i]) together, through one K and V stage that group 0 fills,
+// and the waves of a row compute on the blocks whose mask bit is theirs.
+// Each row adds up its own blocks in ascending order with the same
+// per-block code, so no merge is needed.
+template <typename E, int BLK, int D, bool CAUSAL, int NS, bool MASKED, bool BAND = false>
 __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, const int32_t* __restrict__ row_order,
     const int32_t* __restrict__ row_order_h, const void* __restrict__ Qv, const void* __restrict__ Kv,
     const u16* __restrict__ V, u16* __restrict__ O, int Z, int H, int nbr, int nbc, float c, int grouped,
-    float* __restrict__ lse, const float* __restrict__ amask, const float* __restrict__ kpmask) {
+    float* __restrict__ lse, const float* __restrict__ amask, const float* __restrict__ kpmask,
+    const int32_t* __restrict__ uoff = nullptr, const int32_t* __restrict__ umask = nullptr,
+    const int32_t* __restrict__ grp = nullptr, int nu = 0, int stride = 0) {
+  static_assert(!BAND || (NS == 2 && !MASKED), "K/V sharing: two rows a workgroup, no dense masks");
   constexpr bool F8 = WideTypes<E>::F8;
   constexpr int RBK = F8 ? D : 2 * D;  // bytes per K row
   using Cfg = WideCfg<BLK, D, RBK>;
@@ -132,8 +144,10 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
 
   // K and V stages in separate arrays, so that the compiler can tell the
   // K reads from the V transfers in flight (and the other way round)
-  __shared__ __attribute__((aligned(16))) unsigned char Ks[NS * SBK];
-  __shared__ __attribute__((aligned(16))) unsigned char Vs[NS * SB];
+  constexpr int NSTG = BAND ? 1 : NS;  // K / V stages (one shared stage with BAND)
+  constexpr int KSTEP = BAND ? 1 : NS;  // positions of the column walk per step
+  __shared__ __attribute__((aligned(16))) unsigned char Ks[NSTG * SBK];
+  __shared__ __attribute__((aligned(16))) unsigned char Vs[NSTG * SB];
 
   const int tid_all = threadIdx.x;
   const int sg = __builtin_amdgcn_readfirstlane(tid_all / NT);  // key group
@@ -141,14 +155,23 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int li = lane & 15, g = lane >> 4;
-  unsigned char* const Kg = Ks + sg * SBK;
-  unsigned char* const Vg = Vs + sg * SB;
+  unsigned char* const Kg = Ks + (BAND ? 0 : sg * SBK);
+  unsigned char* const Vg = Vs + (BAND ? 0 : sg * SB);
   // Which block row: with rows of similar length, XCD-aware and grouped by
   // (batch, head), the head's rows longest first (K and V of a head stay in
   // the XCD's L2 while its rows are in flight); otherwise longest first
   // across the whole job, batch index fastest (the long rows start first).
   int z, hr;
-  if (grouped) {
+  int r0 = 0;          // BAND: the group's first row
+  bool row_ok = true;  // BAND: this key group's row is on the grid
+  if constexpr (BAND) {
+    const int zhn = Z * H;
+    r0 = grp[blockIdx.x / zhn];
+    z = (blockIdx.x % zhn) % Z;
+    const int rr = r0 + sg * stride;
+    row_ok = rr < nbr;
+    hr = ((blockIdx.x % zhn) / Z) * nbr + (row_ok ? rr : r0);
+  } else if (grouped) {
     const int unit = xcd_unit(blockIdx.x, gridDim.x);
     const int zhu = unit / nbr;
     z = zhu / H;
@@ -158,7 +181,25 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
     hr = row_order[blockIdx.x / Z];
   }
   const int h = hr / nbr, r = hr % nbr;
-  const int k0 = row_ptr[hr], k1 = row_ptr[hr + 1];
+  int k0, k1;
+  if constexpr (BAND) {
+    // the union entries whose columns are on the grid
+    auto first_at_least = [&](int v) {
+      int lo = 0, hi = nu;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (uoff[mid] < v) lo = mid + 1;
+        else hi = mid;
+      }
+      return lo;
+    };
+    k0 = first_at_least(-r0);
+    k1 = first_at_least(nbc - r0);
+  } else {
+    k0 = row_ptr[hr];
+    k1 = row_ptr[hr + 1];
+  }
+  auto col_of = [&](int e) { return BAND ? r0 + uoff[e] : col_idx[e]; };
   const int64_t zh = (int64_t)z * H + h;
   const int64_t Nq = (int64_t)nbr * BLK, Nk = (int64_t)nbc * BLK;
   const int q_lo = r * BLK + wave * 32;  // first query row of this wave
@@ -218,7 +259,13 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
   constexpr int NIV = NI / NSUB;
   constexpr int NIK = SBK / 1024 / NW / NSUB;
   static_assert(NIK >= 1 && SBK % (1024 * NW * NSUB) == 0, "whole K DMA instructions per wave");
+
   auto dma_n = [&](const unsigned char* gpart, unsigned char* spart, int n, int de, int dodd) {
+    if constexpr (BAND) {
+      // group 0 fills the shared stage (splitting the transfers between
+      // the groups measured no faster)
+      if (sg != 0) return;
+    }
 #pragma unroll
     for (int i = 0; i < NIV; ++i) {
       if (i < n) {
@@ -230,9 +277,9 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
   };
   auto dmaK = [&](const unsigned char* gpart, unsigned char* spart) { dma_n(gpart, spart, NIK, dk_even, dk_odd); };
   auto dmaV = [&](const unsigned char* gpart, unsigned char* spart) { dma_n(gpart, spart, NIV, d_even, d_odd); };
-  auto kpart = [&](int e, int x) { return Kz + ((int64_t)col_idx[e] * BLK + x * KS) * RBK; };
+  auto kpart = [&](int e, int x) { return Kz + ((int64_t)col_of(e) * BLK + x * KS) * RBK; };
   auto vpart = [&](int e, int x) {
-    return reinterpret_cast<const unsigned char*>(Vz) + ((int64_t)col_idx[e] * BLK + x * KS) * RB;
+    return reinterpret_cast<const unsigned char*>(Vz) + ((int64_t)col_of(e) * BLK + x * KS) * RB;
   };
 
   // ---- LDS read offsets (bytes). K: lane (g, li) reads row 16 jt + li,
@@ -271,28 +318,31 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
   //         block; softmax; P.V on V half x.
   // Every barrier is block-wide (all key groups); transfers complete in
   // issue order, so each wait names how many later ones may stay in flight.
-  const int nsteps = (k1 - k0 + NS - 1) / NS;
+  const int nsteps = (k1 - k0 + KSTEP - 1) / KSTEP;
+  const int gofs = BAND ? 0 : sg;  // this group's first position of the walk
   unsigned char* const Kp[2] = {Kg, Kg + KS * RBK};
   unsigned char* const Vp[2] = {Vg, Vg + KS * RB};
-  if (k0 + sg < k1) {
-    dmaK(kpart(k0 + sg, 0), Kp[0]);
+  if (k0 + gofs < k1) {
+    dmaK(kpart(k0 + gofs, 0), Kp[0]);
     if constexpr (NSUB == 2) {
-      dmaV(vpart(k0 + sg, 0), Vp[0]);
-      dmaK(kpart(k0 + sg, 1), Kp[1]);
+      dmaV(vpart(k0 + gofs, 0), Vp[0]);
+      dmaK(kpart(k0 + gofs, 1), Kp[1]);
     }
   }
   for (int step = 0; step < nsteps; ++step) {
-    const int kk = k0 + step * NS + sg;
+    const int kk = k0 + step * KSTEP + gofs;
     const bool valid = kk < k1;
-    const bool has_next = kk + NS < k1;
-    const int cb = valid ? col_idx[kk] : 0;
+    const bool has_next = kk + KSTEP < k1;
+    const int cb = valid ? col_of(kk) : 0;
     if constexpr (NSUB == 1) {
       wait_vmcnt0();
       __syncthreads();  // [A]
       if (valid) dmaV(vpart(kk, 0), Vp[0]);
     }
     const bool mask_block = CAUSAL && (cb * BLK + BLK - 1 > q_lo);
-    const bool compute = valid && !(CAUSAL && cb * BLK > q_lo + 31);
+    // BAND: only the blocks this group's row holds
+    const bool mine = !BAND || (row_ok && valid && ((umask[kk] >> sg) & 1));
+    const bool compute = valid && mine && !(CAUSAL && cb * BLK > q_lo + 31);
 
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub) {
@@ -385,7 +435,7 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
         if (sub == 0) {
           if (valid) dmaV(vpart(kk, 1), Vp[1]);
         } else {
-          if (has_next) dmaV(vpart(kk + NS, 0), Vp[0]);
+          if (has_next) dmaV(vpart(kk + KSTEP, 0), Vp[0]);
         }
         // [P sub]: later transfers in flight: K(this, 1) and V(this, 1)
         // before sub-step 0's P.V; K(next, 0) and V(next, 0) before
@@ -396,7 +446,7 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
           if (has_next) wait_vmcnt<NIK + NIV>(); else wait_vmcnt0();
         }
         __syncthreads();
-        if (has_next) dmaK(kpart(kk + NS, sub), Kp[sub]);
+        if (has_next) dmaK(kpart(kk + KSTEP, sub), Kp[sub]);
       }
 
       // ---- softmax of both tiles
@@ -446,7 +496,7 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
       if constexpr (NSUB == 1) {
         wait_vmcnt0();    // this wave's part of V (the only transfer in flight)
         __syncthreads();  // [B]
-        if (has_next) dmaK(kpart(kk + NS, 0), Kp[0]);
+        if (has_next) dmaK(kpart(kk + KSTEP, 0), Kp[0]);
       }
       if (!compute) continue;
 
@@ -486,7 +536,9 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
 
   // ---- merge the key groups into group 0 through the K stages, one query
   // tile at a time: each side's (l, O) is rescaled by exp2(m_side - m_max)
-  if constexpr (NS > 1) {
+  if constexpr (BAND) {
+    if (!row_ok) return;
+  } else if constexpr (NS > 1) {
     float* red = reinterpret_cast<float*>(Ks);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -565,12 +617,39 @@ int launch_ns(const bs_layout* L, const AttnArgs& a, float c, hipStream_t s) {
   return BS_OK;
 }
 
+// K/V shared across two block rows of a slope-1 ACSR layout (its sharing
+// plan, when the handle has one and sharing is on; no dense masks)
+template <typename E, int BLK, int D>
+int launch_band(const bs_layout* L, const AttnArgs& a, float c, hipStream_t s) {
+  const dim3 grid((unsigned)((int64_t)L->share_ngrp * a.Z * L->H)), block(BLK * 2 * 2);
+#define BSA_WIDE_BAND(CA)                                                                                         \
+  hipLaunchKernelGGL((k_attn_wide<E, BLK, D, CA, 2, false, true>), grid, block, 0, s, L->row_ptr, L->col_idx,     \
+                     L->row_order, L->row_order_h, a.Q, a.K, (const u16*)a.V, (u16*)a.O, a.Z, L->H, L->nbr,       \
+                     L->nbc, c, 0, a.lse, nullptr, nullptr, L->share_uoff, L->share_umask, L->share_grp,          \
+                     L->share_n, L->share_stride)
+  if (a.causal) BSA_WIDE_BAND(true);
+  else BSA_WIDE_BAND(false);
+#undef BSA_WIDE_BAND
+  BSA_HIP(hipGetLastError());
+  return BS_OK;
+}
+
 // Key groups per workgroup: split a row's blocks over NS groups once the
 // longest row alone (about two workgroups share a CU) outlasts a CU's share
 // of the job.
 template <typename E, int BLK, int D>
 int run(const bs_layout* L, const AttnArgs& a, float c, hipStream_t s) {
   const int Z = a.Z;
+  // K/V sharing on request, and by default at blocks of 64, where it
+  // measured faster on band layouts (strided, 16384 tokens, 16 heads,
+  // bf16: d = 128 3%, d = 64 6-7%); at 128-blocks the eight-wave
+  // workgroup, one per CU, measured 12-16% slower, at 32-blocks 0-3%
+  // faster
+  if constexpr (!WideTypes<E>::F8) {
+    const bool share = L->share_mode == 1 || (L->share_mode == -1 && BLK == 64);
+    if (share && L->share_n > 0 && L->share_rows == 2 && a.am == nullptr && a.kp == nullptr)
+      return launch_band<E, BLK, D>(L, a, c, s);
+  }
   using Cfg = WideCfg<BLK, D, WideTypes<E>::F8 ? D : 2 * D>;
   constexpr size_t cap = 160 * 1024;
   // four groups of a 128-block row would be 1024 threads, at most 128

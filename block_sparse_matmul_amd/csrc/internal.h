@@ -41,13 +41,14 @@ struct bs_layout {
   // columns are r0 + share_uoff[i] (ascending), held by the rows whose bits
   // are set in share_umask[i]; share_grp lists every group's r0, longest
   // group first. One allocation (share_mem); share_n = 0 when there is no
-  // plan. share_on: whether the fused attention uses it.
+  // plan. share_mode: whether the fused attention uses it: 1 yes, 0 no, -1
+  // where it measured faster (16-bit operands, blocks of 64).
   int32_t* share_mem = nullptr;
   const int32_t* share_uoff = nullptr;
   const int32_t* share_umask = nullptr;
   const int32_t* share_grp = nullptr;
   int share_n = 0, share_ngrp = 0, share_stride = 0, share_rows = 1;
-  bool share_on = false;
+  int share_mode = -1;
   // non-empty block rows grouped by softmax length class (see
   // softmax_class), class 0 first, (head, row) order inside a class;
   // class c is row_cls[cls_begin[c] .. cls_begin[c+1])

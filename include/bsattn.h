@@ -121,26 +121,30 @@ int bs_layout_nnz(bs_layout_t L, int64_t* nnz);
    r + t share the columns that the set and its shift by t have in common.
    The handle keeps a plan when two rows r and r + stride hold at least 1.5
    times as many blocks as the union of their columns, for the stride (1 to
-   64) with the smallest union. With sharing on (bs_layout_set_kv_share),
-   the fused attention with float32 operands, no dense masks, and blocks of
-   32 (head_dim 64 or 128) or 64 (head_dim 64) then runs `rows` = 2 block
-   rows r0, r0 + stride per workgroup and stages each K/V block of their
-   union once. Each row still adds up its own blocks in ascending column
-   order with the same arithmetic as the one-row kernel, so the output has
-   the same bits as with sharing off whenever the one-row kernel runs one
-   key group per row. bs_layout_kv_share reports the plan: *rows = 1 and
-   *stride = 0 when the handle has none. Errors: BS_ERR_INVALID_ARG for a
-   NULL handle or output pointer. */
+   64) with the smallest union (blocks of 32 or more). When the plan is used
+   (bs_layout_set_kv_share), the fused attention without dense masks runs
+   `rows` = 2 block rows r0, r0 + stride per workgroup and stages each K/V
+   block of their union once: float32 with blocks of 32 (head_dim 64 or
+   128) or 64 (head_dim 64), and bf16 / fp16 with blocks of 32 to 128. Each
+   row still adds up its own blocks in ascending column order with the same
+   arithmetic as the one-row kernel, so the output has the same bits as
+   without sharing whenever the one-row kernel runs one key group per row.
+   bs_layout_kv_share reports the plan: *rows = 1 and *stride = 0 when the
+   handle has none. Errors: BS_ERR_INVALID_ARG for a NULL handle or output
+   pointer. */
 int bs_layout_kv_share(bs_layout_t L, int* rows, int* stride);
 
-/* enable = 1: the fused attention uses the handle's sharing plan where one
-   applies; 0 (the default): one block row per workgroup (on the float32
-   strided workload the two measured the same, 389 and 391 us, the kernel
-   being bound by the matrix cores rather than by staging). Read when a call
-   is issued (calls already on a stream keep their kernel); not synchronised
-   with calls on the same handle from other host threads. Errors:
-   BS_ERR_INVALID_ARG for a NULL handle or enable other than 0 or 1. */
-int bs_layout_set_kv_share(bs_layout_t L, int enable);
+/* Use of the sharing plan by the fused attention: mode 1 wherever it
+   applies, 0 never (one block row per workgroup), -1 (the default) where
+   it measured faster: bf16 / fp16 with blocks of 64 (strided band, 16384
+   tokens: 3% at head_dim 128, 6-7% at 64). Float32 measured the same time
+   either way (389 and 391 us on strided_acsr_b32, a kernel bound by the
+   matrix cores rather than by staging); bf16 with blocks of 128 measured
+   12-16% slower with it. Read when a call is issued (calls already on a
+   stream keep their kernel); not synchronised with calls on the same handle
+   from other host threads. Errors: BS_ERR_INVALID_ARG for a NULL handle or
+   a mode other than -1, 0 or 1. */
+int bs_layout_set_kv_share(bs_layout_t L, int mode);
 
 /* Sizes of a handle (any output pointer may be NULL). */
 int bs_layout_info(bs_layout_t L, int* H, int* nbr, int* nbc, int* block,

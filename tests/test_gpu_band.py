@@ -1,6 +1,7 @@
 """The fused attention that shares K/V across block rows (slope-1 ACSR
-layouts, float32): groups of rows r0, r0 + t, ... walk the union of their
-columns and stage each block once. Parity against the oracle's dense route
+layouts; float32 kernel and the 16-bit kernel's sharing mode): groups of
+rows r0, r0 + t, ... walk the union of their columns and stage each block
+once. Parity against the oracle's dense route
 on small layouts whose groups are ragged (rows past the grid, columns held by
 one row only, rows with no block at all), causal and not, blocks of 32 and
 64, head_dim 64 and 128; the row log-sum-exp; agreement with the one-row
@@ -35,7 +36,7 @@ def _offsets(terms, nbr, nbc):
 def _expected_plan(terms, nb, block):
     G = 2
     d = _offsets(terms, nb, nb)
-    if block not in (32, 64) or nb < 2 or not d:
+    if block < 32 or nb < 2 or not d:
         return (1, 0)
     best = None
     for t in range(1, min(64, (nb - 1) // (G - 1)) + 1):
@@ -98,8 +99,8 @@ def test_band_attention_matches_oracle(case, shape, causal):
 
 def test_band_plans_of_the_cases():
     """The plans the handles report: the rule above for every case at
-    every block (none at blocks of 16 or 128), the strided workload's shape
-    on stride 4, and no plan where no shift overlaps enough (offsets -10, 0,
+    every block (none at blocks of 16), the strided workload's shape on
+    stride 4, and no plan where no shift overlaps enough (offsets -10, 0,
     7: any shift keeps at most one of the three)."""
     announce("band plans")
     sparse = ([(0, 12, 1, -10, 10, 2), (0, 12, 1, 7, 1, 1)], 12)
@@ -114,10 +115,31 @@ def test_band_switch():
     announce("band switch")
     terms, nb = CASES[0]
     L = bsa.Layout.acsr(terms, 1, nb, nb, 32)
-    assert bsa._lib.lib().bs_layout_set_kv_share(L.handle, 2) == bsa._lib.BS_ERR_INVALID_ARG
+    for bad in (2, -2):
+        assert bsa._lib.lib().bs_layout_set_kv_share(L.handle, bad) == bsa._lib.BS_ERR_INVALID_ARG
     L.set_kv_share(True)
     L.set_kv_share(False)
     assert L.kv_share() == (2, 4)  # the plan stays; only its use is off
+    L.set_kv_share(None)
+
+
+@pytest.mark.parametrize("b,dt,shares", [(32, "f32", False), (64, "bf16", True), (128, "bf16", False)])
+def test_band_default_mode(b, dt, shares):
+    """The default (-1): the sharing kernel for 16-bit operands with blocks
+    of 64, the one-row kernel otherwise; each gives the same bits as the
+    kernel forced on or off (the small cases here run one key group per row
+    where sharing is off, so both give the same bits anyway for float32)."""
+    terms, nb = CASES[0]
+    H, Z, d = 2, 1, 64
+    announce("band default mode", b, dt)
+    g = torch.Generator("cpu").manual_seed(790 + b)
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    q, k, v = (to_dev(torch.randn((Z, H, nb * b, d), generator=g).to(tdt)) for _ in range(3))
+    L = bsa.Layout.acsr(terms, H, nb, nb, b)
+    O_def = bsa.attention(L, q, k, v, 0.125)
+    L.set_kv_share(shares)
+    O_forced = bsa.attention(L, q, k, v, 0.125)
+    assert torch.equal(O_def, O_forced)
 
 
 @pytest.mark.parametrize("b", [32, 64])
@@ -139,3 +161,43 @@ def test_band_attention_non_square(b):
     torch.cuda.synchronize()
     assert bool(torch.isfinite(O).all())
     assert max_abs(f64(O), oracle.attention_dense(q, k, v, lay, b, 0.125)) <= TOL["f32"]
+
+
+WIDE_SHAPES = [(32, 64), (32, 128), (64, 128), (128, 64), (128, 128)]
+DT16 = {"bf16": torch.bfloat16, "f16": torch.float16}
+LSE_TOL16 = {"bf16": 4e-3, "f16": 1e-3}
+
+
+@pytest.mark.parametrize("case", [0, 1, 3, 4])
+@pytest.mark.parametrize("shape", WIDE_SHAPES, ids=[f"b{b}d{d}" for b, d in WIDE_SHAPES])
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_band_attention_16bit_matches_oracle(case, shape, dt, causal):
+    """The 16-bit kernel with K/V shared across two rows: the oracle on the
+    rounded inputs at the 16-bit bars, the row log-sum-exp, and the same
+    kernel without sharing on the same handle."""
+    terms, nb = CASES[case]
+    b, d = shape
+    H, Z = 2, 2
+    announce("band attention 16-bit", case, b, d, dt, causal)
+    lay = oracle.acsr_expand(terms, H, nb, nb)
+    g = torch.Generator("cpu").manual_seed(780 + case)
+    q, k, v = (torch.randn((Z, H, nb * b, d), generator=g).to(DT16[dt]) for _ in range(3))
+    L = bsa.Layout.acsr(terms, H, nb, nb, b)
+    assert L.kv_share()[0] == 2
+    L.set_kv_share(True)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    O, lse = bsa.attention(L, qd, kd, vd, 0.125, causal, return_lse=True, out=torch.full_like(qd, float("nan")))
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(O).all()), "unwritten output"
+    ref = oracle.attention_dense(q, k, v, lay, b, 0.125, causal)
+    assert max_abs(f64(O), ref) <= TOL[dt]
+    ref_lse = oracle.attention_lse(q, k, lay, b, 0.125, causal)
+    got = f64(lse)
+    inf = np.isneginf(ref_lse)
+    assert np.array_equal(np.isneginf(got), inf)
+    if (~inf).any():
+        assert float(np.abs(got[~inf] - ref_lse[~inf]).max()) <= LSE_TOL16[dt]
+    L.set_kv_share(False)
+    O1 = bsa.attention(L, qd, kd, vd, 0.125, causal)
+    assert max_abs(f64(O), f64(O1)) <= TOL[dt]
