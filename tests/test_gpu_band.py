@@ -142,17 +142,18 @@ def test_band_default_mode(b, dt, shares):
     assert torch.equal(O_def, O_forced)
 
 
-@pytest.mark.parametrize("b", [32, 64])
-def test_band_attention_non_square(b):
+@pytest.mark.parametrize("b,dt", [(32, "f32"), (64, "f32"), (32, "bf16"), (64, "bf16"), (128, "bf16")])
+def test_band_attention_non_square(b, dt):
     """More key blocks than query blocks (the terms reach past the last
     row's diagonal): the plan clips columns at the key grid."""
     terms = [(0, 20, 1, -3, 1, 12), (0, 20, 1, -20, 4, 12)]
     nbr, nbc, H, Z, d = 20, 28, 2, 2, 64
-    announce("band attention non-square", b)
+    announce("band attention non-square", b, dt)
     lay = oracle.acsr_expand(terms, H, nbr, nbc)
     g = torch.Generator("cpu").manual_seed(760 + b)
-    q = torch.randn((Z, H, nbr * b, d), generator=g)
-    k, v = (torch.randn((Z, H, nbc * b, d), generator=g) for _ in range(2))
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    q = torch.randn((Z, H, nbr * b, d), generator=g).to(tdt)
+    k, v = (torch.randn((Z, H, nbc * b, d), generator=g).to(tdt) for _ in range(2))
     L = bsa.Layout.acsr(terms, H, nbr, nbc, b)
     assert L.kv_share()[0] == 2
     L.set_kv_share(True)
@@ -160,7 +161,7 @@ def test_band_attention_non_square(b):
     O = bsa.attention(L, qd, kd, vd, 0.125, out=torch.full_like(qd, float("nan")))
     torch.cuda.synchronize()
     assert bool(torch.isfinite(O).all())
-    assert max_abs(f64(O), oracle.attention_dense(q, k, v, lay, b, 0.125)) <= TOL["f32"]
+    assert max_abs(f64(O), oracle.attention_dense(q, k, v, lay, b, 0.125)) <= TOL[dt]
 
 
 WIDE_SHAPES = [(32, 64), (32, 128), (64, 128), (128, 64), (128, 128)]
