@@ -26,8 +26,9 @@
  *  - Every call returns BS_OK (0) or a negative bs_status. Arguments are
  *    validated before any HIP call is made; bs_last_error() gives the
  *    message of the last failure on the calling thread.
- *  - A layout handle is immutable after it is built and may be used from
- *    several streams and threads at once.
+ *  - A layout handle's tables are immutable after it is built, and the
+ *    handle may be used from several streams and threads at once; its one
+ *    setting, bs_layout_set_kv_share, is read when a call is issued.
  *
  * Shapes (b = block, nnz = number of stored blocks over all heads)
  *  - layout                 uint8 [H][nbr][nbc], values 0 or 1, one layout
