@@ -76,7 +76,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_bwd_wide(
   using HT = H16<E>;
   using V8 = typename HT::V8;
   using V4 = typename HT::V4;
-  constexpr int NW = BLK / 32, NT = 64 * NW;
+  constexpr int NW = BLK / 32;              // waves (32 own rows each)
   constexpr int NQ = D / 32;         // 8-element fragments per row and lane
   constexpr int NNT = D / 16;        // 16-column tiles of a gradient
   constexpr int RB = 2 * D;          // bytes per row
@@ -88,7 +88,6 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_bwd_wide(
   constexpr int NCH = HALF / 32;     // 32-row chunks per half
   static_assert(NIP >= 1 && PB % (1024 * NW) == 0, "whole DMA instructions per wave");
   static_assert(NCH >= 1, "blocks of 64 or 128");
-  (void)NT;
 
   __shared__ __attribute__((aligned(16))) unsigned char X1s[BLK * RB];  // K (dQ) or Q (dK dV)
   __shared__ __attribute__((aligned(16))) unsigned char X2s[BLK * RB];  // V (dQ) or dO (dK dV)
