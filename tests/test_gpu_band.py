@@ -202,3 +202,23 @@ def test_band_attention_16bit_matches_oracle(case, shape, dt, causal):
     L.set_kv_share(False)
     O1 = bsa.attention(L, qd, kd, vd, 0.125, causal)
     assert max_abs(f64(O), f64(O1)) <= TOL[dt]
+
+
+def test_band_layout_with_masks_takes_the_masked_kernel():
+    """A sharing plan does not apply with dense masks: the masked kernel
+    runs (sharing forced on or not) and matches the oracle."""
+    terms, nb = CASES[0]
+    b, d, H, Z = 64, 64, 2, 2
+    N = nb * b
+    announce("band layout with masks")
+    lay = oracle.acsr_expand(terms, H, nb, nb)
+    g = torch.Generator("cpu").manual_seed(800)
+    q, k, v = (torch.randn((Z, H, N, d), generator=g).to(torch.bfloat16) for _ in range(3))
+    kp = torch.randn((Z, N), generator=g)
+    kp[1, N // 3:] = -float("inf")
+    L = bsa.Layout.acsr(terms, H, nb, nb, b)
+    ref = oracle.attention_dense(q, k, v, lay, b, 0.125, False, kp_mask=kp)
+    for mode in (None, True, False):
+        L.set_kv_share(mode)
+        O = bsa.attention(L, to_dev(q), to_dev(k), to_dev(v), 0.125, key_padding_mask=to_dev(kp))
+        assert max_abs(f64(O), ref) <= TOL["bf16"], mode
