@@ -135,7 +135,8 @@ __global__ __launch_bounds__(BLK * 4) void k_bwd(
     z = blockIdx.x % Z;
   }
   const int h = hu / n_own, u = hu % n_own;
-  const int k0 = ptr[hu], k1 = ptr[hu + 1];
+  int k0 = ptr[hu], k1 = ptr[hu + 1];
+  if constexpr (CAUSAL) trim_causal<DKDV>(idx, u, k0, k1);
   const int64_t zh = (int64_t)z * H + h;
   const int64_t Nown = (int64_t)n_own * BLK, Noth = (int64_t)n_oth * BLK;
   const int64_t Nq = DKDV ? Noth : Nown, Nk = DKDV ? Nown : Noth;
@@ -321,19 +322,9 @@ __global__ __launch_bounds__(BLK * 4) void k_bwd(
     store_next();
     __syncthreads();
     if (kk + 1 < k1) load_next(idx[kk + 1]);
-    // causal: skip a block whose every key is after every query of the
-    // wave; mask element-wise where the block reaches across the diagonal
-    bool compute = true, mask_block = false;
-    if constexpr (CAUSAL) {
-      if constexpr (DKDV) {
-        compute = o * BLK + BLK - 1 >= own_lo;     // some query at or after the wave's first key
-        mask_block = own_lo + 15 > o * BLK;        // some key after some query
-      } else {
-        compute = o * BLK <= own_lo + 15;
-        mask_block = o * BLK + BLK - 1 > own_lo;
-      }
-    }
-    if (!compute) continue;
+    // causal: mask element-wise on the diagonal block (the walk holds no
+    // block wholly above the diagonal)
+    const bool mask_block = CAUSAL && o == u;
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub) {
       const int kofs = sub * KS;

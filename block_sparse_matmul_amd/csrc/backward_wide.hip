@@ -110,7 +110,8 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_bwd_wide(
     z = blockIdx.x % Z;
   }
   const int h = hu / n_own, u = hu % n_own;
-  const int k0 = ptr[hu], k1 = ptr[hu + 1];
+  int k0 = ptr[hu], k1 = ptr[hu + 1];
+  if constexpr (CAUSAL) trim_causal<DKDV>(idx, u, k0, k1);
   const int64_t zh = (int64_t)z * H + h;
   const int64_t Nown = (int64_t)n_own * BLK, Noth = (int64_t)n_oth * BLK;
   const int64_t Nq = DKDV ? Noth : Nown;
@@ -260,17 +261,10 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_bwd_wide(
   if (k0 < k1) dma_half(idx[k0], 0, 0);
   for (int kk = k0; kk < k1; ++kk) {
     const int o = idx[kk];  // the other side's block
-    // causal: skip a block with every key after every query of the wave
-    bool compute = true, mask_block = false;
-    if constexpr (CAUSAL) {
-      if constexpr (DKDV) {
-        compute = o * BLK + BLK - 1 >= own_lo;  // some query at or after the wave's first key
-        mask_block = own_lo + 31 > o * BLK;     // some key after some query
-      } else {
-        compute = o * BLK <= own_lo + 31;
-        mask_block = o * BLK + BLK - 1 > own_lo;
-      }
-    }
+    // causal: the diagonal block holds keys after queries (every wave of
+    // the workgroup computes on it: each has some pair on or below the
+    // diagonal)
+    const bool mask_block = CAUSAL && o == u;
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
       // this half has landed (the only transfer in flight), and every wave
@@ -281,10 +275,6 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_bwd_wide(
         if (x == 0) dma_half(o, 1, 0);
         else if (kk + 1 < k1) dma_half(idx[kk + 1], 0, (kk + 1 - k0) & 1);
       };
-      if (!compute) {
-        issue();
-        continue;
-      }
 #pragma unroll
       for (int ch = 0; ch < NCH; ++ch) {
         const int rofs = x * HALF + 32 * ch;  // first row of the chunk within the block

@@ -75,6 +75,37 @@ __device__ __forceinline__ int xcd_unit(int b, int G) {
   return x * q + (x < rem ? x : rem) + j;
 }
 
+// Causal backward walk of block row (DKDV = false) or block column (true) u
+// over entries [k0, k1) of an ascending index list: blocks wholly above the
+// diagonal (a key block after the row, or a query block before the column)
+// have P = 0 and add nothing, and are dropped from the walk. They form a
+// tail (rows) or a head (columns) of the list, found by binary search; the
+// diagonal block u itself stays.
+template <bool DKDV>
+__device__ __forceinline__ void trim_causal(const int32_t* __restrict__ idx, int u, int& k0, int& k1) {
+  if constexpr (DKDV) {
+    if (k0 < k1 && idx[k0] < u) {
+      int lo = k0 + 1, hi = k1;  // first entry >= u
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (idx[mid] < u) lo = mid + 1;
+        else hi = mid;
+      }
+      k0 = lo;
+    }
+  } else {
+    if (k0 < k1 && idx[k1 - 1] > u) {
+      int lo = k0, hi = k1 - 1;  // first entry > u
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (idx[mid] > u) hi = mid;
+        else lo = mid + 1;
+      }
+      k1 = lo;
+    }
+  }
+}
+
 namespace bsa {
 
 // error reporting (thread-local message, see bs_last_error)

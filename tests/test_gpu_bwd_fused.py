@@ -97,13 +97,16 @@ def test_fused_backward(b, d, dt, causal):
         assert max_abs(f64(got), ref) <= _grad_tol(dt, ref), name
 
 
-@pytest.mark.parametrize("b", [16, 64])
+@pytest.mark.parametrize("b", [16, 64, 128])
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-def test_fused_backward_nonsquare(b, dt):
-    H, nbr, nbc, Z, d = 2, 3, 5, 2, 64
-    lay = W.small_random_layout(H, nbr, nbc, 0.5, 420 + b)
+@pytest.mark.parametrize("nbr,nbc", [(3, 5), (5, 3)])
+def test_fused_backward_nonsquare(b, dt, nbr, nbc):
+    """More key blocks than query blocks and the other way round (causal
+    needs a square layout and is rejected here)."""
+    H, Z, d = 2, 2, 64
+    lay = W.small_random_layout(H, nbr, nbc, 0.5, 420 + b + nbr)
     lay[:, :, 0] = 1
-    announce("fused backward non-square", b, dt)
+    announce("fused backward non-square", b, dt, nbr, nbc)
     g = torch.Generator("cpu").manual_seed(421)
     q, do = (torch.randn((Z, H, nbr * b, d), generator=g).to(DT[dt]) for _ in range(2))
     k, v = (torch.randn((Z, H, nbc * b, d), generator=g).to(DT[dt]) for _ in range(2))
@@ -113,7 +116,44 @@ def test_fused_backward_nonsquare(b, dt):
     grads = bsa.attention_backward_fused(L, qd, kd, vd, o, lse, dod, 0.125)
     refs = oracle.attention_backward_dense(q, k, v, do, lay, b, 0.125, False)
     for name, got, ref in zip(("dq", "dk", "dv"), grads, refs):
+        assert not torch.isnan(got).any(), name
         assert max_abs(f64(got), ref) <= _grad_tol(dt, ref), name
+    with pytest.raises(bsa.BsError):
+        bsa.attention_backward_fused(L, qd, kd, vd, o, lse, dod, 0.125, True)
+
+
+@pytest.mark.parametrize("b", [32, 64, 128])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("masked", [False, True])
+def test_causal_backward_ignores_blocks_above_the_diagonal(b, dt, masked):
+    """Causal, a stored block wholly above the diagonal has P = 0: the
+    backward walks drop such blocks, so the gradients equal, bit for bit,
+    those of the same layout without them (same forward outputs), and the
+    oracle's."""
+    H, nb, Z, d = 2, 5, 2, 128
+    N = nb * b
+    lay = W.small_random_layout(H, nb, nb, 0.6, 440 + b, force_diagonal=True)
+    lay[:, 0, :] = 1  # the first block row holds every column (all but one above the diagonal)
+    tri = lay * np.tril(np.ones((nb, nb), np.uint8))[None]
+    assert (lay != tri).any()
+    announce("causal backward above-diagonal blocks", b, dt, masked)
+    q, k, v, do = _t([(Z, H, N, d)] * 4, 441, dt)
+    kw = {}
+    if masked:
+        g = torch.Generator("cpu").manual_seed(442)
+        kw = {"attn_mask": to_dev(torch.randn((N, N), generator=g)),
+              "key_padding_mask": to_dev(torch.randn((Z, N), generator=g) * 0.5)}
+    qd, kd, vd, dod = (to_dev(t) for t in (q, k, v, do))
+    L, T = bsa.Layout(torch.from_numpy(lay), b), bsa.Layout(torch.from_numpy(tri), b)
+    o, lse = bsa.attention(L, qd, kd, vd, 0.125, True, return_lse=True, **kw)
+    got = bsa.attention_backward_fused(L, qd, kd, vd, o, lse, dod, 0.125, True, **kw)
+    ref_t = bsa.attention_backward_fused(T, qd, kd, vd, o, lse, dod, 0.125, True, **kw)
+    am = kw["attn_mask"].cpu() if masked else None
+    kp = kw["key_padding_mask"].cpu() if masked else None
+    refs = oracle.attention_backward_dense(q, k, v, do, lay, b, 0.125, True, am, kp)
+    for name, a, c, ref in zip(("dq", "dk", "dv"), got, ref_t, refs):
+        assert torch.equal(a, c), name
+        assert max_abs(f64(a), ref) <= _grad_tol(dt, ref), name
 
 
 @pytest.mark.parametrize("b", [16, 64, 128])
