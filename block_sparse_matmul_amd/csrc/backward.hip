@@ -69,7 +69,9 @@ struct GLds {
   static constexpr bool F32 = std::is_same<E, float>::value;
   static constexpr int RSTR = D + 32 / (int)sizeof(St);  // row reads
   static constexpr int NT_COPIES = DKDV ? 2 : 1;         // matrices read transposed
-  static constexpr size_t STATS = DKDV ? 2 * BLK * sizeof(float) : 0;
+  // lse and D of the block's queries (dK dV); two slots by block parity
+  // with 128-blocks, whose next block is staged in halves
+  static constexpr size_t STATS = DKDV ? (BLK == 128 ? 4 : 2) * BLK * sizeof(float) : 0;
   static constexpr size_t DUP_BYTES = (size_t)(2 * BLK * RSTR + NT_COPIES * BLK * (D + 4)) * sizeof(St) + STATS;
   static constexpr bool DUP = F32 && DUP_BYTES <= 160 * 1024;  // separate transposed-read copies
   static constexpr int TSTR = DUP ? D + 4 : RSTR;               // transposed reads
@@ -107,6 +109,14 @@ __global__ __launch_bounds__(BLK * 4) void k_bwd(
   constexpr int CPR = D / VEC;
   constexpr int KCH = BLK * CPR / NT;
   static_assert(KCH >= 1 && BLK * CPR % NT == 0, "staging");
+  // With two sub-steps (128-blocks) the next block is staged in halves (the
+  // rows of one sub-step): a half moves into registers while the current
+  // block's other half is computed and into LDS once every wave is done
+  // with the half it replaces. HK chunks per thread are held; one half is
+  // chunks [x HK, (x + 1) HK) of the block (whole rows: NT / CPR rows per
+  // chunk index divide 64).
+  constexpr int HK = NSUB == 2 ? KCH / 2 : KCH;
+  static_assert(NSUB == 1 || (KCH % 2 == 0 && 64 % (NT / CPR) == 0), "halves of whole rows");
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[Lay::BYTES];
   St* const X1r = reinterpret_cast<St*>(smem);             // K (dQ) or Q (dK dV), row reads
@@ -114,7 +124,7 @@ __global__ __launch_bounds__(BLK * 4) void k_bwd(
   St* const X1t = Lay::DUP ? X2r + Lay::MAT : X1r;         // transposed-read copies
   St* const X2t = Lay::DUP ? X1t + Lay::TMAT : X2r;
   float* const st_lse = reinterpret_cast<float*>(smem + (size_t)Lay::ELEMS * sizeof(St));  // DKDV only
-  float* const st_d = st_lse + BLK;
+  float* const st_d = st_lse + BLK;  // slot 1 (two sub-steps): st_lse + 2 BLK, st_d + 2 BLK
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -197,7 +207,7 @@ __global__ __launch_bounds__(BLK * 4) void k_bwd(
   // ---- staging (the other side's block: rows o*BLK.. of X1 and X2)
   const St* const X1g = (DKDV ? Q : K) + zh * Noth * D;
   const St* const X2g = (DKDV ? dO : V) + zh * Noth * D;
-  Vec s1[KCH], s2[KCH];
+  Vec s1[HK], s2[HK];
   float s_lse = 0.f, s_d = 0.f;  // DKDV: one query's statistics per thread (tid < BLK)
   int goff[KCH], roff[KCH], toff[KCH];
 #pragma unroll
@@ -207,36 +217,40 @@ __global__ __launch_bounds__(BLK * 4) void k_bwd(
     roff[i] = (ch / CPR) * RSTR + (ch % CPR) * VEC;
     toff[i] = (ch / CPR) * TSTR + (ch % CPR) * VEC;
   }
-  auto load_next = [&](int o) {
+  // chunks [x HK, x HK + HK) of the other side's block o into registers;
+  // with the first of them (x = 0) the block's query statistics (dK dV)
+  auto load_part = [&](int o, int x) {
     const St* a = X1g + (int64_t)o * BLK * D;
     const St* b = X2g + (int64_t)o * BLK * D;
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      s1[i] = *reinterpret_cast<const Vec*>(a + goff[i]);
-      s2[i] = *reinterpret_cast<const Vec*>(b + goff[i]);
+    for (int i = 0; i < HK; ++i) {
+      s1[i] = *reinterpret_cast<const Vec*>(a + goff[x * HK + i]);
+      s2[i] = *reinterpret_cast<const Vec*>(b + goff[x * HK + i]);
     }
     if constexpr (DKDV) {
-      if (tid < BLK) {
+      if (x == 0 && tid < BLK) {
         const float l = lse[zh * Nq + (int64_t)o * BLK + tid];
         s_lse = (l == -INFINITY) ? INFINITY : l * kLog2eG;
         s_d = Dv[zh * Nq + (int64_t)o * BLK + tid];
       }
     }
   };
-  auto store_next = [&]() {
+  // the registers of part x into LDS; the statistics into slot `slot`
+  auto store_part = [&](int x, int slot) {
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      *reinterpret_cast<Vec*>(&X1r[roff[i]]) = s1[i];
-      *reinterpret_cast<Vec*>(&X2r[roff[i]]) = s2[i];
+    for (int i = 0; i < HK; ++i) {
+      const int j = x * HK + i;
+      *reinterpret_cast<Vec*>(&X1r[roff[j]]) = s1[i];
+      *reinterpret_cast<Vec*>(&X2r[roff[j]]) = s2[i];
       if constexpr (Lay::DUP) {
-        *reinterpret_cast<Vec*>(&X1t[toff[i]]) = s1[i];
-        if constexpr (DKDV) *reinterpret_cast<Vec*>(&X2t[toff[i]]) = s2[i];
+        *reinterpret_cast<Vec*>(&X1t[toff[j]]) = s1[i];
+        if constexpr (DKDV) *reinterpret_cast<Vec*>(&X2t[toff[j]]) = s2[i];
       }
     }
     if constexpr (DKDV) {
-      if (tid < BLK) {
-        st_lse[tid] = s_lse;
-        st_d[tid] = s_d;
+      if (x == 0 && tid < BLK) {
+        st_lse[2 * BLK * slot + tid] = s_lse;
+        st_d[2 * BLK * slot + tid] = s_d;
       }
     }
   };
@@ -315,19 +329,43 @@ __global__ __launch_bounds__(BLK * 4) void k_bwd(
     }
   };
 
-  if (k0 < k1) load_next(idx[k0]);
+  if (k0 < k1) {
+    load_part(idx[k0], 0);
+    if constexpr (NSUB == 2) {
+      store_part(0, 0);
+      load_part(idx[k0], 1);
+    }
+  }
   for (int kk = k0; kk < k1; ++kk) {
     const int o = idx[kk];  // the other side's block index
-    __syncthreads();        // every wave is done with the previous block
-    store_next();
-    __syncthreads();
-    if (kk + 1 < k1) load_next(idx[kk + 1]);
+    const int slot = NSUB == 2 ? (kk - k0) & 1 : 0;
+    __syncthreads();  // every wave is done with the previous block
+    if constexpr (NSUB == 2) {
+      // the second half of this block (its first half and statistics are
+      // in LDS); then the first half of the next one into registers
+      store_part(1, slot);
+      if (kk + 1 < k1) load_part(idx[kk + 1], 0);
+    } else {
+      store_part(0, 0);
+      __syncthreads();
+      if (kk + 1 < k1) load_part(idx[kk + 1], 0);
+    }
     // causal: mask element-wise on the diagonal block (the walk holds no
     // block wholly above the diagonal)
     const bool mask_block = CAUSAL && o == u;
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub) {
       const int kofs = sub * KS;
+      if (sub == 1) {
+        // every wave is done with the first half, and the second is in LDS:
+        // the next block's first half replaces this one's, and its second
+        // half moves into registers
+        __syncthreads();
+        if (kk + 1 < k1) {
+          store_part(0, slot ^ 1);
+          load_part(idx[kk + 1], 1);
+        }
+      }
       f32x4 s[NJT], dp[NJT];
       rprod(s, X1r, kofs, f1);
       rprod(dp, X2r, kofs, f2);
@@ -352,8 +390,8 @@ __global__ __launch_bounds__(BLK * 4) void k_bwd(
         }
         f32x4 l2, dd;
         if constexpr (DKDV) {
-          l2 = *reinterpret_cast<const f32x4*>(&st_lse[kofs + 16 * jt + 4 * g]);
-          dd = *reinterpret_cast<const f32x4*>(&st_d[kofs + 16 * jt + 4 * g]);
+          l2 = *reinterpret_cast<const f32x4*>(&st_lse[2 * BLK * slot + kofs + 16 * jt + 4 * g]);
+          dd = *reinterpret_cast<const f32x4*>(&st_d[2 * BLK * slot + kofs + 16 * jt + 4 * g]);
         } else {
           l2 = f32x4{lse2_own, lse2_own, lse2_own, lse2_own};
           dd = f32x4{d_own, d_own, d_own, d_own};
