@@ -198,6 +198,9 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
   } else {
     k0 = row_ptr[hr];
     k1 = row_ptr[hr + 1];
+    // causal: key blocks after the row (wholly above the diagonal) are
+    // neither staged nor computed
+    if constexpr (CAUSAL) trim_causal<false>(col_idx, r, k0, k1);
   }
   auto col_of = [&](int e) { return BAND ? r0 + uoff[e] : col_idx[e]; };
   const int64_t zh = (int64_t)z * H + h;

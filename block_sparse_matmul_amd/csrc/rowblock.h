@@ -206,10 +206,15 @@ __global__ __launch_bounds__(BLK * 4 * NS) void k_rowblock(
     };
     boff = first_at_least(-(hr % nbr));
     k0 = 0;
-    k1 = first_at_least(nbc - (hr % nbr)) - boff;
+    // causal attention: no column after the row either (offsets up to 0)
+    const int end = nbc - (hr % nbr);
+    k1 = first_at_least((ATTN && CAUSAL && end > 1) ? 1 : end) - boff;
   } else {
     k0 = row_ptr[hr];
     k1 = row_ptr[hr + 1];
+    // causal attention: key blocks after the row (wholly above the
+    // diagonal) are neither staged nor computed
+    if constexpr (ATTN && CAUSAL) trim_causal<false>(col_idx, hr % nbr, k0, k1);
   }
   auto col_of = [&](int kk) { return band != nullptr ? hr % nbr + band[boff + kk] : col_idx[kk]; };
   const int64_t zh = (int64_t)z * H + h;

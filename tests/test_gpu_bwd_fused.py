@@ -125,6 +125,34 @@ def test_fused_backward_nonsquare(b, dt, nbr, nbc):
 @pytest.mark.parametrize("b", [32, 64, 128])
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("masked", [False, True])
+def test_causal_forward_ignores_blocks_above_the_diagonal(b, dt, masked):
+    """Causal, the forward walks drop stored blocks wholly above the
+    diagonal: output and row log-sum-exp equal, bit for bit, those of the
+    same layout without them, and the oracle's."""
+    H, nb, Z, d = 2, 5, 2, 64
+    N = nb * b
+    lay = W.small_random_layout(H, nb, nb, 0.6, 450 + b, force_diagonal=True)
+    lay[:, 0, :] = 1
+    tri = lay * np.tril(np.ones((nb, nb), np.uint8))[None]
+    announce("causal forward above-diagonal blocks", b, dt, masked)
+    q, k, v = _t([(Z, H, N, d)] * 3, 451, dt)
+    kw, am, kp = {}, None, None
+    if masked:
+        g = torch.Generator("cpu").manual_seed(452)
+        am, kp = torch.randn((N, N), generator=g), torch.randn((Z, N), generator=g) * 0.5
+        kw = {"attn_mask": to_dev(am), "key_padding_mask": to_dev(kp)}
+    qd, kd, vd = (to_dev(t) for t in (q, k, v))
+    L, T = bsa.Layout(torch.from_numpy(lay), b), bsa.Layout(torch.from_numpy(tri), b)
+    o, lse = bsa.attention(L, qd, kd, vd, 0.125, True, return_lse=True, **kw)
+    o_t, lse_t = bsa.attention(T, qd, kd, vd, 0.125, True, return_lse=True, **kw)
+    assert torch.equal(o, o_t) and torch.equal(lse, lse_t)
+    ref = oracle.attention_dense(q, k, v, lay, b, 0.125, True, am, kp)
+    assert max_abs(f64(o), ref) <= TOL[dt]
+
+
+@pytest.mark.parametrize("b", [32, 64, 128])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("masked", [False, True])
 def test_causal_backward_ignores_blocks_above_the_diagonal(b, dt, masked):
     """Causal, a stored block wholly above the diagonal has P = 0: the
     backward walks drop such blocks, so the gradients equal, bit for bit,
