@@ -8,9 +8,12 @@
 //  * each wave owns 32 query rows (two 16-row tiles), so every K or V
 //    operand read from LDS feeds two MFMAs: half the LDS read traffic per
 //    flop, which is what bounds the 16-row layout with 16-bit operands;
-//  * blocks are staged with LDS DMA (global_load_lds_dwordx4: every lane
-//    moves 16 bytes from its own global address into consecutive LDS
-//    slots), so staging needs no registers and no LDS store instructions.
+//  * blocks are staged with LDS DMA (buffer_load_dwordx4 ... lds: every
+//    lane moves 16 bytes from its own offset in the (batch, head)'s K or V
+//    into consecutive LDS slots), so staging needs no registers and no LDS
+//    store instructions. The buffer form takes a scalar base and offset and
+//    a 32-bit per-lane offset; the global form needed a 64-bit address add
+//    per lane and transfer (1.5-2% slower on random_b128_bf16).
 //    Rows are stored unpadded with their 16-byte chunks XOR-swizzled by row
 //    (d = 128: slot = chunk ^ ((2 row) & 14); d = 64: slot = chunk ^
 //    (((row >> 1) ^ row) & 7)), which keeps the K reads (16 bytes per lane)
@@ -36,6 +39,9 @@ namespace {
 constexpr float kLog2eB = 1.4426950408889634f;
 constexpr float kLn2B = 0.6931471805599453f;
 constexpr float kTauB = 8.0f;  // lazy-rescale headroom, log2 units
+// fourth word of a raw buffer resource on gfx9 (32-bit data format, no
+// swizzle, no index stride)
+constexpr int kRsrcWord3 = 0x00020000;
 
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -208,6 +214,14 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
   const int q_lo = r * BLK + wave * 32;  // first query row of this wave
   const unsigned char* Kz = static_cast<const unsigned char*>(Kv) + zh * Nk * RBK;
   const u16* Vz = V + zh * Nk * D;
+  // K and V of the (batch, head) as raw buffer resources (the launch checks
+  // that each fits in 32-bit offsets): a transfer then takes a scalar base
+  // and offset and a 32-bit per-lane offset, with no per-lane 64-bit address
+  // arithmetic; reads past the extent would return zeros
+  const __amdgpu_buffer_rsrc_t kres =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(Kz), 0, (int)(unsigned)(Nk * RBK), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t vres =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(Vz), 0, (int)(unsigned)(Nk * RB), kRsrcWord3);
 
   // ---- Q of both tiles as B fragments (8 values of one row per lane);
   // only the sign of scale*log2(e) is folded in (exact in 16 bits)
@@ -263,7 +277,7 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
   constexpr int NIK = SBK / 1024 / NW / NSUB;
   static_assert(NIK >= 1 && SBK % (1024 * NW * NSUB) == 0, "whole K DMA instructions per wave");
 
-  auto dma_n = [&](const unsigned char* gpart, unsigned char* spart, int n, int de, int dodd) {
+  auto dma_n = [&](__amdgpu_buffer_rsrc_t res, unsigned gofs, unsigned char* spart, int n, int de, int dodd) {
     if constexpr (BAND) {
       // group 0 fills the shared stage (splitting the transfers between
       // the groups measured no faster)
@@ -273,17 +287,16 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
     for (int i = 0; i < NIV; ++i) {
       if (i < n) {
         const int I = wave + NW * i;  // uniform
-        const unsigned char* src = gpart + I * 1024 + (((NW * i) & 1) ? dodd : de);
-        __builtin_amdgcn_global_load_lds((const void*)src, (lds_u8*)(spart + I * 1024), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(res, (lds_u8*)(spart + I * 1024), 16,
+                                                 (unsigned)(((NW * i) & 1) ? dodd : de), gofs + I * 1024, 0, 0);
       }
     }
   };
-  auto dmaK = [&](const unsigned char* gpart, unsigned char* spart) { dma_n(gpart, spart, NIK, dk_even, dk_odd); };
-  auto dmaV = [&](const unsigned char* gpart, unsigned char* spart) { dma_n(gpart, spart, NIV, d_even, d_odd); };
-  auto kpart = [&](int e, int x) { return Kz + ((int64_t)col_of(e) * BLK + x * KS) * RBK; };
-  auto vpart = [&](int e, int x) {
-    return reinterpret_cast<const unsigned char*>(Vz) + ((int64_t)col_of(e) * BLK + x * KS) * RB;
-  };
+  auto dmaK = [&](unsigned gofs, unsigned char* spart) { dma_n(kres, gofs, spart, NIK, dk_even, dk_odd); };
+  auto dmaV = [&](unsigned gofs, unsigned char* spart) { dma_n(vres, gofs, spart, NIV, d_even, d_odd); };
+  // byte offsets of the KS rows of sub-step x of the block at walk position e
+  auto kpart = [&](int e, int x) { return (unsigned)(col_of(e) * BLK + x * KS) * (unsigned)RBK; };
+  auto vpart = [&](int e, int x) { return (unsigned)(col_of(e) * BLK + x * KS) * (unsigned)RB; };
 
   // ---- LDS read offsets (bytes). K: lane (g, li) reads row 16 jt + li,
   // chunk 4u + g; V: lane (g, 4k + m) reads row 4g + k, the 8 bytes at
@@ -648,6 +661,8 @@ int run(const bs_layout* L, const AttnArgs& a, float c, hipStream_t s) {
   // bf16: d = 128 3%, d = 64 6-7%); at 128-blocks the eight-wave
   // workgroup, one per CU, measured 12-16% slower, at 32-blocks 0-3%
   // faster
+  // the transfers address a (batch, head)'s K and V with 32-bit offsets
+  if ((int64_t)L->nbc * BLK * 2 * D > 0xFFFFFFFFll) return kNotApplicable;
   if constexpr (!WideTypes<E>::F8) {
     const bool share = L->share_mode == 1 || (L->share_mode == -1 && BLK == 64);
     if (share && L->share_n > 0 && L->share_rows == 2 && a.am == nullptr && a.kp == nullptr)

@@ -12,8 +12,8 @@
 //  * each wave owns 32 rows of its side (two 16-row tiles), so every
 //    operand read from LDS feeds two MFMAs (the 16-row kernels read the
 //    whole staged block per 16 rows and were bound by LDS reads);
-//  * the other side's block is staged by LDS DMA (global_load_lds_dwordx4)
-//    into unpadded rows whose 16-byte chunks are XOR-swizzled by row, the
+//  * the other side's block is staged by LDS DMA (buffer_load_dwordx4 ...
+//    lds, a scalar base and a 32-bit per-lane offset) into unpadded rows whose 16-byte chunks are XOR-swizzled by row, the
 //    layout of the 16-bit forward: row reads (16 bytes a lane) and
 //    transposing reads (ds_read_b64_tr_b16) are both free of bank conflicts;
 //  * each block moves in two halves; a half is fetched as soon as every
@@ -53,6 +53,9 @@ namespace {
 constexpr float kLog2eW = 1.4426950408889634f;
 
 typedef __attribute__((address_space(3))) unsigned char lds_u8w;
+// fourth word of a raw buffer resource on gfx9 (32-bit data format, no
+// swizzle, no index stride)
+constexpr int kRsrcWord3W = 0x00020000;
 
 // 16-byte chunk slot of a row's chunk: d = 128 (256-byte rows): chunk ^
 // ((2 row) & 14); d = 64 (128-byte rows): chunk ^ (((row >> 1) ^ row) & 7).
@@ -170,29 +173,42 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_bwd_wide(
   }
   const int d_even = (wave & 1) ? dofs[1] : dofs[0];
   const int d_odd = (wave & 1) ? dofs[0] : dofs[1];
-  const unsigned char* const X1g = reinterpret_cast<const unsigned char*>((DKDV ? Q : K) + zh * Noth * D);
-  const unsigned char* const X2g = reinterpret_cast<const unsigned char*>((DKDV ? dO : V) + zh * Noth * D);
+  // the other side's matrices and (dK dV) its row statistics for this
+  // (batch, head) as raw buffer resources (the launch checks that they fit
+  // in 32-bit offsets): each transfer takes a scalar base and offset and a
+  // 32-bit per-lane offset
+  const __amdgpu_buffer_rsrc_t x1res = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u16*>((DKDV ? Q : K) + zh * Noth * D), 0, (int)(unsigned)(Noth * RB), kRsrcWord3W);
+  const __amdgpu_buffer_rsrc_t x2res = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u16*>((DKDV ? dO : V) + zh * Noth * D), 0, (int)(unsigned)(Noth * RB), kRsrcWord3W);
+  const __amdgpu_buffer_rsrc_t lres =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(lse + zh * Nq), 0, (int)(unsigned)(Nq * 4), kRsrcWord3W);
+  const __amdgpu_buffer_rsrc_t dres =
+      __builtin_amdgcn_make_buffer_rsrc(Dv + zh * Nq, 0, (int)(unsigned)(Nq * 4), kRsrcWord3W);
   auto dma_half = [&](int o, int x, int par) {
-    const int64_t base = ((int64_t)o * BLK + x * HALF) * RB;
+    const unsigned base = (unsigned)(o * BLK + x * HALF) * (unsigned)RB;
     if constexpr (DKDV) {
       if (x == 0 && wave == 0) {
         // lanes 0 .. BLK/4 - 1: 16-byte chunks of lse; the next BLK/4: of D;
         // lanes past those (blocks of 64) repeat D's last chunk into the
         // unused tail of the buffer
         const int ch = lane < BLK / 2 ? lane : BLK / 2 - 1;
-        const float* src = ch < BLK / 4 ? lse + zh * Nq + (int64_t)o * BLK + 4 * ch
-                                        : Dv + zh * Nq + (int64_t)o * BLK + 4 * (ch - BLK / 4);
-        __builtin_amdgcn_global_load_lds((const void*)src, (lds_u8w*)(&Ss[par][0]), 16, 0, 0);
+        const unsigned qofs = (unsigned)(o * BLK) * 4u;
+        if (ch < BLK / 4)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(lres, (lds_u8w*)(&Ss[par][0]), 16, 16u * ch, qofs, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(dres, (lds_u8w*)(&Ss[par][0]), 16, 16u * (ch - BLK / 4), qofs, 0,
+                                                   0);
       }
     }
 #pragma unroll
     for (int i = 0; i < NIP; ++i) {
       const int I = wave + NW * i;  // uniform
-      const int off = I * 1024 + (((NW * i) & 1) ? d_odd : d_even);
-      __builtin_amdgcn_global_load_lds((const void*)(X1g + base + off), (lds_u8w*)(X1s + x * PB + I * 1024), 16, 0,
-                                       0);
-      __builtin_amdgcn_global_load_lds((const void*)(X2g + base + off), (lds_u8w*)(X2s + x * PB + I * 1024), 16, 0,
-                                       0);
+      const unsigned off = (unsigned)(((NW * i) & 1) ? d_odd : d_even);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(x1res, (lds_u8w*)(X1s + x * PB + I * 1024), 16, off,
+                                               base + I * 1024, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(x2res, (lds_u8w*)(X2s + x * PB + I * 1024), 16, off,
+                                               base + I * 1024, 0, 0);
     }
   };
 
@@ -380,6 +396,9 @@ int run_we(const bs_layout* L, const BwdArgs& a, hipStream_t s) {
 int launch_attention_bwd_wide(const bs_layout* L, const BwdArgs& a, hipStream_t s) {
   if ((a.dt != BS_BF16 && a.dt != BS_F16) || a.am != nullptr || a.kp != nullptr) return kNotApplicable;
   if ((L->block != 64 && L->block != 128) || (a.d != 64 && a.d != 128)) return kNotApplicable;
+  // the transfers address a (batch, head)'s matrices with 32-bit offsets
+  const int64_t rows = (int64_t)(L->nbr > L->nbc ? L->nbr : L->nbc) * L->block;
+  if (rows * 2 * a.d > 0xFFFFFFFFll) return kNotApplicable;
   return a.dt == BS_BF16 ? run_we<bf16_t>(L, a, s) : run_we<f16_t>(L, a, s);
 }
 
