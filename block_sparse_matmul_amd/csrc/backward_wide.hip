@@ -67,13 +67,16 @@ __device__ __forceinline__ int swz(int r) {
 
 enum { MODE_DQ = 0, MODE_DK = 1, MODE_DV = 2 };
 
-template <typename E, int BLK, int D, bool CAUSAL, int MODE>
+// KP: a key-padding mask kpmask [Z][keys] (additive, natural-log units)
+// joins the scores as x = s |c| + log2(e) kp, the forward's form; a dense
+// attention mask takes the 16-row kernels (read once more per pass here).
+template <typename E, int BLK, int D, bool CAUSAL, int MODE, bool KP = false>
 __global__ __launch_bounds__(BLK * 2, 2) void k_bwd_wide(
     const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx, const int32_t* __restrict__ order,
     const int32_t* __restrict__ order_h, int grouped, const u16* __restrict__ Q, const u16* __restrict__ K,
     const u16* __restrict__ V, const u16* __restrict__ O, const u16* __restrict__ dO, u16* __restrict__ G,
     const float* __restrict__ lse, float* __restrict__ Dv, int Z, int H, int n_own, int n_oth, float c,
-    float scale) {
+    float scale, const float* __restrict__ kpmask = nullptr) {
   constexpr bool DKDV = MODE != MODE_DQ;  // own rows are keys (block columns walked)
   constexpr bool HASDP = MODE != MODE_DV;  // dP (and D) needed
   using HT = H16<E>;
@@ -138,6 +141,12 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_bwd_wide(
         for (int e = 0; e < 8; ++e) f1[t][q][e] = HT::cvt((float)f1[t][q][e] * sgn);
       }
     }
+  }
+  // dK dV with a key-padding mask: the value of each tile's key (own row)
+  float kp_own[2] = {0.f, 0.f};
+  if constexpr (KP && DKDV) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) kp_own[t] = kpmask[(int64_t)z * Nown + own_lo + 16 * t + li];
   }
   // dQ: the tiles' row statistics: lse2 = lse in log2 units (+inf for a row
   // that saw nothing, so that P = 0 there), D = dO . O, written out
@@ -297,6 +306,14 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_bwd_wide(
         const unsigned char* x1 = X1s + rofs * RB;
         const unsigned char* x2 = X2s + rofs * RB;
         f32x4 s[2][2], dp[2][2];
+        // dQ with a key-padding mask: the values of the chunk's keys (read
+        // while the row products run)
+        f32x4 kpv[KP && !DKDV ? 2 : 1];
+        if constexpr (KP && !DKDV) {
+#pragma unroll
+          for (int jt = 0; jt < 2; ++jt)
+            kpv[jt] = *reinterpret_cast<const f32x4*>(kpmask + (int64_t)z * Noth + o * BLK + rofs + 16 * jt + 4 * g);
+        }
         rprod(s, x1, f1);
         if constexpr (HASDP) rprod(dp, x2, f2);
         if (ch == 0) issue();
@@ -317,6 +334,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_bwd_wide(
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
               float xv = s[t][jt][rr] * cs;
+              if constexpr (KP) xv = fmaf(DKDV ? kp_own[t] : kpv[jt][rr], kLog2eW, xv);
               float l2, dd = 0.f;
               if constexpr (DKDV) {
                 const float l = l4[jt][rr];
@@ -353,6 +371,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_bwd_wide(
 
 template <typename E, int BLK, int D, int MODE>
 int launch_w(const bs_layout* L, const BwdArgs& a, hipStream_t s) {
+  const bool kp = a.kp != nullptr;
   constexpr bool DKDV = MODE != MODE_DQ;
   const int n_own = DKDV ? L->nbc : L->nbr, n_oth = DKDV ? L->nbr : L->nbc;
   const dim3 grid(L->H * n_own * a.Z), block(BLK * 2);
@@ -367,12 +386,17 @@ int launch_w(const bs_layout* L, const BwdArgs& a, hipStream_t s) {
   const int grouped = (4.0 * max_len <= per_slot) ? 1 : 0;
   const float c = a.scale * kLog2eW;
   u16* g = (u16*)(MODE == MODE_DQ ? a.dQ : (MODE == MODE_DK ? a.dK : a.dV));
-#define BSA_BWDW_LAUNCH(CA)                                                                                      \
-  hipLaunchKernelGGL((k_bwd_wide<E, BLK, D, CA, MODE>), grid, block, 0, s, ptr, idx, order, order_h, grouped,    \
-                     (const u16*)a.Q, (const u16*)a.K, (const u16*)a.V, (const u16*)a.O, (const u16*)a.dO, g,      \
-                     a.lse, a.Dws, a.Z, L->H, n_own, n_oth, c, a.scale)
-  if (a.causal) BSA_BWDW_LAUNCH(true);
-  else BSA_BWDW_LAUNCH(false);
+#define BSA_BWDW_LAUNCH(CA, KPM)                                                                                 \
+  hipLaunchKernelGGL((k_bwd_wide<E, BLK, D, CA, MODE, KPM>), grid, block, 0, s, ptr, idx, order, order_h,        \
+                     grouped, (const u16*)a.Q, (const u16*)a.K, (const u16*)a.V, (const u16*)a.O, (const u16*)a.dO, \
+                     g, a.lse, a.Dws, a.Z, L->H, n_own, n_oth, c, a.scale, a.kp)
+  if (a.causal) {
+    if (kp) BSA_BWDW_LAUNCH(true, true);
+    else BSA_BWDW_LAUNCH(true, false);
+  } else {
+    if (kp) BSA_BWDW_LAUNCH(false, true);
+    else BSA_BWDW_LAUNCH(false, false);
+  }
 #undef BSA_BWDW_LAUNCH
   BSA_HIP(hipGetLastError());
   return BS_OK;
@@ -394,7 +418,10 @@ int run_we(const bs_layout* L, const BwdArgs& a, hipStream_t s) {
 }  // namespace
 
 int launch_attention_bwd_wide(const bs_layout* L, const BwdArgs& a, hipStream_t s) {
-  if ((a.dt != BS_BF16 && a.dt != BS_F16) || a.am != nullptr || a.kp != nullptr) return kNotApplicable;
+  // a key-padding mask is read here; a dense attention mask, read at every
+  // stored block by each of the three passes, takes the 16-row kernels
+  // (two passes)
+  if ((a.dt != BS_BF16 && a.dt != BS_F16) || a.am != nullptr) return kNotApplicable;
   if ((L->block != 64 && L->block != 128) || (a.d != 64 && a.d != 128)) return kNotApplicable;
   // the transfers address a (batch, head)'s matrices with 32-bit offsets
   const int64_t rows = (int64_t)(L->nbr > L->nbc ? L->nbr : L->nbc) * L->block;

@@ -122,6 +122,37 @@ def test_fused_backward_nonsquare(b, dt, nbr, nbc):
         bsa.attention_backward_fused(L, qd, kd, vd, o, lse, dod, 0.125, True)
 
 
+KP_CASES = [(b, 64, dt, causal) for b in (32, 64, 128) for dt in ("bf16", "f16") for causal in (False, True)] + \
+    [(128, 128, "bf16", False), (128, 128, "bf16", True), (64, 128, "f16", False)]
+
+
+@pytest.mark.parametrize("b,d,dt,causal", KP_CASES)
+def test_fused_backward_key_padding(b, d, dt, causal):
+    """A key-padding mask alone (the 32-row 16-bit kernels read it at 64-
+    and 128-blocks): random values, a padded tail of keys, and a batch entry
+    whose every key is masked (no gradient at all there)."""
+    H, nb, Z = 2, 4, 3
+    N = nb * b
+    lay = W.small_random_layout(H, nb, nb, 0.5, 460 + b, force_diagonal=True)
+    lay[1, 2, :] = 0
+    announce("fused backward key padding", b, d, dt, causal)
+    q, k, v, do = _t([(Z, H, N, d)] * 4, 461 + b, dt)
+    g = torch.Generator("cpu").manual_seed(462)
+    kp = torch.randn((Z, N), generator=g) * 0.5
+    kp[0, N - N // 3:] = -float("inf")
+    kp[1, :] = -float("inf")
+    L = bsa.Layout(torch.from_numpy(lay), b)
+    qd, kd, vd, dod, kpd = (to_dev(t) for t in (q, k, v, do, kp))
+    scale = 1.0 / np.sqrt(d)
+    o, lse = bsa.attention(L, qd, kd, vd, scale, causal, key_padding_mask=kpd, return_lse=True)
+    grads = bsa.attention_backward_fused(L, qd, kd, vd, o, lse, dod, scale, causal, key_padding_mask=kpd)
+    refs = oracle.attention_backward_dense(q, k, v, do, lay, b, scale, causal, None, kp)
+    for name, got, ref in zip(("dq", "dk", "dv"), grads, refs):
+        assert not torch.isnan(got).any(), name
+        assert max_abs(f64(got), ref) <= _grad_tol(dt, ref), name
+        assert not got[1].any(), name  # every key of batch entry 1 masked
+
+
 @pytest.mark.parametrize("b", [32, 64, 128])
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("masked", [False, True])
