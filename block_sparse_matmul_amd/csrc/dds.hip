@@ -126,28 +126,31 @@ __global__ __launch_bounds__(256 * NS) void k_dds(const int32_t* __restrict__ co
   f32x4 sreg[KCH];  // the next slab of S
   R4 anext[NKT];    // the next step's A fragments
   R4 acur[NKT];
-  // step T covers contraction rows T*KS .. T*KS + KS - 1
+  // step T covers contraction rows T*KS .. T*KS + KS - 1. Every load is
+  // issued on every call (rows past the column's end read its last block
+  // instead, and are neither stored nor multiplied), so that the compiler
+  // counts the same loads on every path and its waits leave later loads in
+  // flight (a conditional load made each wait cover every load).
   auto load_step = [&](int T) {
     const int q0 = T * KS;
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       // first row of this wave's chunks (uniform), then the lane's own row
-      const int qw = q0 + __builtin_amdgcn_readfirstlane(srow[i]);
-      if (qw < total_rows) {
-        const int q = q0 + srow[i];
-        const int64_t k = blk_id[e0 + qw / BLK];
-        // S is read once: a streaming load keeps it from displacing A
-        sreg[i] = __builtin_nontemporal_load(
-            reinterpret_cast<const f32x4*>(Sz + k * (BLK * BLK) + (q % BLK) * BLK + scol[i]));
+      int qw = q0 + __builtin_amdgcn_readfirstlane(srow[i]);
+      int q = q0 + srow[i];
+      if (qw >= total_rows) {
+        qw = total_rows - BLK;
+        q = qw + (srow[i] % BLK);
       }
+      const int64_t k = blk_id[e0 + qw / BLK];
+      // S is read once: a streaming load keeps it from displacing A
+      sreg[i] = __builtin_nontemporal_load(
+          reinterpret_cast<const f32x4*>(Sz + k * (BLK * BLK) + (q % BLK) * BLK + scol[i]));
     }
-    if (active) {
 #pragma unroll
-      for (int kt = 0; kt < NKT; ++kt) {
-        const int q = q0 + 16 * kt;
-        if (q < total_rows)
-          anext[kt] = *reinterpret_cast<const R4*>(a_lane + (int64_t)row_idx[e0 + q / BLK] * BLK + q % BLK);
-      }
+    for (int kt = 0; kt < NKT; ++kt) {
+      const int q = min(q0 + 16 * kt, total_rows - 16);
+      anext[kt] = *reinterpret_cast<const R4*>(a_lane + (int64_t)row_idx[e0 + q / BLK] * BLK + q % BLK);
     }
   };
   auto store_slab = [&](int T) {
@@ -171,7 +174,7 @@ __global__ __launch_bounds__(256 * NS) void k_dds(const int32_t* __restrict__ co
 
   const int total = (total_rows + KS - 1) / KS;  // steps of the column
   const int nsteps = (total + NS - 1) / NS;
-  if (sg < total) load_step(sg);
+  if (total > 0) load_step(sg < total ? sg : total - 1);
   for (int step = 0; step < nsteps; ++step) {
     const int t = step * NS + sg;
     const bool valid = t < total;
@@ -180,7 +183,8 @@ __global__ __launch_bounds__(256 * NS) void k_dds(const int32_t* __restrict__ co
     __syncthreads();
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt) acur[kt] = anext[kt];
-    if (t + NS < total) load_step(t + NS);
+    __builtin_amdgcn_sched_barrier(0);  // the copies before the next loads
+    load_step(t + NS < total ? t + NS : total - 1);
     if (!valid || !active) continue;
     // 16-row tiles of this step inside the contraction (the last step of a
     // column can be partial)
