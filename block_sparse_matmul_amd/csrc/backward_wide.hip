@@ -13,9 +13,10 @@
 //    operand read from LDS feeds two MFMAs (the 16-row kernels read the
 //    whole staged block per 16 rows and were bound by LDS reads);
 //  * the other side's block is staged by LDS DMA (buffer_load_dwordx4 ...
-//    lds, a scalar base and a 32-bit per-lane offset) into unpadded rows whose 16-byte chunks are XOR-swizzled by row, the
-//    layout of the 16-bit forward: row reads (16 bytes a lane) and
-//    transposing reads (ds_read_b64_tr_b16) are both free of bank conflicts;
+//    lds, a scalar base and a 32-bit per-lane offset) into unpadded rows
+//    whose 16-byte chunks are XOR-swizzled by row, the layout of the 16-bit
+//    forward: row reads (16 bytes a lane) and transposing reads
+//    (ds_read_b64_tr_b16) are both free of bank conflicts;
 //  * each block moves in two halves; a half is fetched as soon as every
 //    wave is done with the half it replaces, and lands while the other
 //    half is computed (one barrier per half). The fetch is issued after the
@@ -23,21 +24,24 @@
 //    of their reads, and every operand of a product is requested before
 //    its first MFMA (scheduling barriers): together 2% faster on
 //    random_b128_bf16 (forward plus backward 4.94 against 5.03 ms).
-// Kernels (modes of one template):
+// Work of the waves (modes of one template):
 //  * dQ: one workgroup per (batch, head, block row); per 32-key chunk of a
 //    column block: S^T = K Q^T and dP^T = V dO^T (K, V rows from LDS, Q and
 //    dO rows of the wave in registers), P and dS in registers, then
 //    dQ^T += K^T dS^T (K read transposed). It also forms D and writes it.
-//  * dK: one workgroup per (batch, head, block column); per 32-query chunk
-//    of a row block: S = Q K^T and dP = dO V^T (Q, dO rows from LDS, K and V
-//    rows of the wave in registers), dS with the chunk's lse and D, then
-//    dK^T += Q^T dS (Q read transposed).
+//  * dK: per block column; per 32-query chunk of a row block: S = Q K^T and
+//    dP = dO V^T (Q, dO rows from LDS, K and V rows of the wave in
+//    registers), dS with the chunk's lse and D, then dK^T += Q^T dS (Q read
+//    transposed).
 //  * dV: the same walk; S = Q K^T, P with the chunk's lse, then
 //    dV^T += dO^T P (dO read transposed).
-// dK and dV are separate kernels (S formed in both) because one kernel
-// holding both accumulators (32 rows x d x 2 floats a wave) needs more than
-// the 256 registers of two waves per SIMD; at one wave per SIMD it ran 8%
-// slower than the 16-row kernel.
+// Two kernels: dQ, and dK with dV in one workgroup of twice the waves
+// (MODE_DKV), half of them doing the dK work and half the dV work on the
+// same staged blocks of Q and dO. A wave holding both accumulators (32 rows
+// x d x 2 floats) would need more than the 256 registers of two waves per
+// SIMD (at one wave per SIMD it ran 8% slower than the 16-row kernel), so
+// S is formed by both halves; against separate dK and dV kernels the shared
+// staging measured 3-5% faster on the whole backward, bit-identical.
 // P and dS are rounded to the operand type for the products; gradients are
 // rounded once from float32 accumulators.
 #include <math.h>
@@ -65,24 +69,31 @@ __device__ __forceinline__ int swz(int r) {
   else return ((r >> 1) ^ r) & 7;
 }
 
-enum { MODE_DQ = 0, MODE_DK = 1, MODE_DV = 2 };
+enum { MODE_DQ = 0, MODE_DK = 1, MODE_DV = 2, MODE_DKV = 3 };
 
 // KP: a key-padding mask kpmask [Z][keys] (additive, natural-log units)
 // joins the scores as x = s |c| + log2(e) kp, the forward's form; a dense
 // attention mask takes the 16-row kernels (read once more per pass here).
+//
+// MODE_DKV: dK and dV in one workgroup of twice the waves, the first half
+// accumulating dK (the dK mode's work), the second dV (the dV mode's); the
+// two share each staged block of Q and dO, so the column's blocks are
+// staged once instead of twice.
 template <typename E, int BLK, int D, bool CAUSAL, int MODE, bool KP = false>
-__global__ __launch_bounds__(BLK * 2, 2) void k_bwd_wide(
+__global__ __launch_bounds__(BLK * 2 * (MODE == MODE_DKV ? 2 : 1), MODE == MODE_DKV ? 1 : 2) void k_bwd_wide(
     const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx, const int32_t* __restrict__ order,
     const int32_t* __restrict__ order_h, int grouped, const u16* __restrict__ Q, const u16* __restrict__ K,
     const u16* __restrict__ V, const u16* __restrict__ O, const u16* __restrict__ dO, u16* __restrict__ G,
     const float* __restrict__ lse, float* __restrict__ Dv, int Z, int H, int n_own, int n_oth, float c,
-    float scale, const float* __restrict__ kpmask = nullptr) {
+    float scale, const float* __restrict__ kpmask = nullptr, u16* __restrict__ G2 = nullptr) {
   constexpr bool DKDV = MODE != MODE_DQ;  // own rows are keys (block columns walked)
-  constexpr bool HASDP = MODE != MODE_DV;  // dP (and D) needed
+  constexpr bool DUAL = MODE == MODE_DKV;
+  constexpr bool HASDP = MODE != MODE_DV;  // dP (and D) needed by some wave
   using HT = H16<E>;
   using V8 = typename HT::V8;
   using V4 = typename HT::V4;
-  constexpr int NW = BLK / 32;              // waves (32 own rows each)
+  constexpr int NWR = BLK / 32;             // waves per role (32 own rows each)
+  constexpr int NW = DUAL ? 2 * NWR : NWR;  // waves of the workgroup
   constexpr int NQ = D / 32;         // 8-element fragments per row and lane
   constexpr int NNT = D / 16;        // 16-column tiles of a gradient
   constexpr int RB = 2 * D;          // bytes per row
@@ -121,7 +132,9 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_bwd_wide(
   const int64_t zh = (int64_t)z * H + h;
   const int64_t Nown = (int64_t)n_own * BLK, Noth = (int64_t)n_oth * BLK;
   const int64_t Nq = DKDV ? Noth : Nown;
-  const int own_lo = u * BLK + wave * 32;  // first own row of this wave
+  // DUAL: role 0 (the first NWR waves) accumulates dK, role 1 dV
+  const int role = DUAL ? wave / NWR : (MODE == MODE_DV ? 1 : 0);
+  const int own_lo = u * BLK + (wave % NWR) * 32;  // first own row of this wave
 
   // ---- the wave's own rows (two tiles) as B fragments: F1 = Q (dQ) or K
   // (dK dV) with the sign of scale*log2(e) folded in (exact), F2 = dO or V
@@ -135,7 +148,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_bwd_wide(
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       f1[t][q] = *reinterpret_cast<const V8*>(p1 + 32 * q);
-      if constexpr (HASDP) f2[t][q] = *reinterpret_cast<const V8*>(p2 + 32 * q);
+      if (HASDP && role == 0) f2[t][q] = *reinterpret_cast<const V8*>(p2 + 32 * q);
       if (sgn != 1.f) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) f1[t][q][e] = HT::cvt((float)f1[t][q][e] * sgn);
@@ -284,6 +297,9 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_bwd_wide(
   };
 
   if (k0 < k1) dma_half(idx[k0], 0, 0);
+  auto walk = [&](auto mode_c) {
+    constexpr int M = decltype(mode_c)::value;
+    constexpr bool HDP = M != MODE_DV;
   for (int kk = k0; kk < k1; ++kk) {
     const int o = idx[kk];  // the other side's block
     // causal: the diagonal block holds keys after queries (every wave of
@@ -315,7 +331,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_bwd_wide(
             kpv[jt] = *reinterpret_cast<const f32x4*>(kpmask + (int64_t)z * Noth + o * BLK + rofs + 16 * jt + 4 * g);
         }
         rprod(s, x1, f1);
-        if constexpr (HASDP) rprod(dp, x2, f2);
+        if constexpr (HDP) rprod(dp, x2, f2);
         if (ch == 0) issue();
         // element (own row 16 t + li, other row rofs + 16 jt + 4 g + rr)
         f32x4 l4[2], d4[2];
@@ -324,7 +340,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_bwd_wide(
 #pragma unroll
           for (int jt = 0; jt < 2; ++jt) {
             l4[jt] = *reinterpret_cast<const f32x4*>(st + rofs + 16 * jt + 4 * g);
-            if constexpr (HASDP) d4[jt] = *reinterpret_cast<const f32x4*>(st + BLK + rofs + 16 * jt + 4 * g);
+            if constexpr (HDP) d4[jt] = *reinterpret_cast<const f32x4*>(st + BLK + rofs + 16 * jt + 4 * g);
           }
         }
 #pragma unroll
@@ -339,7 +355,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_bwd_wide(
               if constexpr (DKDV) {
                 const float l = l4[jt][rr];
                 l2 = (l == -INFINITY) ? INFINITY : l * kLog2eW;
-                if constexpr (HASDP) dd = d4[jt][rr];
+                if constexpr (HDP) dd = d4[jt][rr];
               } else {
                 l2 = lse2_own[t];
                 dd = d_own[t];
@@ -350,18 +366,27 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_bwd_wide(
               }
               const float p = __builtin_amdgcn_exp2f(xv - l2);
               s[t][jt][rr] = p;
-              if constexpr (HASDP) dp[t][jt][rr] = scale * p * (dp[t][jt][rr] - dd);
+              if constexpr (HDP) dp[t][jt][rr] = scale * p * (dp[t][jt][rr] - dd);
             }
-        if constexpr (MODE == MODE_DV) tprod(acc, x2, s);  // dV^T += dO^T P
+        if constexpr (M == MODE_DV) tprod(acc, x2, s);  // dV^T += dO^T P
         else tprod(acc, x1, dp);  // dQ^T += K^T dS^T, dK^T += Q^T dS
       }
     }
+  }
+  };
+  // the whole walk for a wave of mode M: the kernel's mode, or with DUAL
+  // the wave's role (both roles meet at the same barriers)
+  if constexpr (DUAL) {
+    if (role == 0) walk(std::integral_constant<int, MODE_DK>{});
+    else walk(std::integral_constant<int, MODE_DV>{});
+  } else {
+    walk(std::integral_constant<int, MODE>{});
   }
 
   // ---- results: lane (g, li) holds columns 16 nt + 4 g .. of own row 16 t + li
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    u16* pg = G + (zh * Nown + own_lo + 16 * t + li) * D + 4 * g;
+    u16* pg = (DUAL && role == 1 ? G2 : G) + (zh * Nown + own_lo + 16 * t + li) * D + 4 * g;
 #pragma unroll
     for (int nt = 0; nt < NNT; ++nt)
       *reinterpret_cast<V4*>(pg + nt * 16) =
@@ -374,7 +399,7 @@ int launch_w(const bs_layout* L, const BwdArgs& a, hipStream_t s) {
   const bool kp = a.kp != nullptr;
   constexpr bool DKDV = MODE != MODE_DQ;
   const int n_own = DKDV ? L->nbc : L->nbr, n_oth = DKDV ? L->nbr : L->nbc;
-  const dim3 grid(L->H * n_own * a.Z), block(BLK * 2);
+  const dim3 grid(L->H * n_own * a.Z), block(BLK * 2 * (MODE == MODE_DKV ? 2 : 1));
   const int32_t* ptr = DKDV ? L->col_ptr : L->row_ptr;
   const int32_t* idx = DKDV ? L->row_idx : L->col_idx;
   const int32_t* order = DKDV ? L->col_order : L->row_order;
@@ -385,11 +410,11 @@ int launch_w(const bs_layout* L, const BwdArgs& a, hipStream_t s) {
   const int max_len = DKDV ? L->max_col_len : L->max_row_len;
   const int grouped = (4.0 * max_len <= per_slot) ? 1 : 0;
   const float c = a.scale * kLog2eW;
-  u16* g = (u16*)(MODE == MODE_DQ ? a.dQ : (MODE == MODE_DK ? a.dK : a.dV));
+  u16* g = (u16*)(MODE == MODE_DQ ? a.dQ : (MODE == MODE_DV ? a.dV : a.dK));
 #define BSA_BWDW_LAUNCH(CA, KPM)                                                                                 \
   hipLaunchKernelGGL((k_bwd_wide<E, BLK, D, CA, MODE, KPM>), grid, block, 0, s, ptr, idx, order, order_h,        \
                      grouped, (const u16*)a.Q, (const u16*)a.K, (const u16*)a.V, (const u16*)a.O, (const u16*)a.dO, \
-                     g, a.lse, a.Dws, a.Z, L->H, n_own, n_oth, c, a.scale, a.kp)
+                     g, a.lse, a.Dws, a.Z, L->H, n_own, n_oth, c, a.scale, a.kp, (u16*)a.dV)
   if (a.causal) {
     if (kp) BSA_BWDW_LAUNCH(true, true);
     else BSA_BWDW_LAUNCH(true, false);
@@ -405,8 +430,7 @@ int launch_w(const bs_layout* L, const BwdArgs& a, hipStream_t s) {
 template <typename E, int BLK, int D>
 int run_w(const bs_layout* L, const BwdArgs& a, hipStream_t s) {
   if (int rc = launch_w<E, BLK, D, MODE_DQ>(L, a, s)) return rc;  // dQ and D
-  if (int rc = launch_w<E, BLK, D, MODE_DK>(L, a, s)) return rc;  // dK (reads D)
-  return launch_w<E, BLK, D, MODE_DV>(L, a, s);                    // dV
+  return launch_w<E, BLK, D, MODE_DKV>(L, a, s);                  // dK and dV (reads D)
 }
 
 template <typename E>
