@@ -96,6 +96,15 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 __device__ __forceinline__ void wait_vmcnt0() { wait_vmcnt<0>(); }
+// workgroup barrier after this wave's LDS operations, without the memory
+// fence of __syncthreads (which also waits for every LDS DMA transfer in
+// flight): the transfers are paced by the explicit vmcnt waits
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 // MASKED: the dense additive masks (amask [nbr*b][nbc*b], kpmask [Z][nbc*b],
 // either may be null) are read at the start of each sub-step, one 16-byte
@@ -371,7 +380,7 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
         } else {
           if (has_next) wait_vmcnt<NIK + NIV>(); else if (valid) wait_vmcnt<NIV>(); else wait_vmcnt0();
         }
-        __syncthreads();
+        lds_barrier();
       }
       const unsigned char* const Kc = Kp[sub];
       // dense masks of this sub-step, both query tiles (in flight during
@@ -461,7 +470,7 @@ __global__ __launch_bounds__(BLK * 2 * NS) void k_attn_wide(
         } else {
           if (has_next) wait_vmcnt<NIK + NIV>(); else wait_vmcnt0();
         }
-        __syncthreads();
+        lds_barrier();
         if (has_next) dmaK(kpart(kk + KSTEP, sub), Kp[sub]);
       }
 
