@@ -42,8 +42,9 @@
 // SIMD (at one wave per SIMD it ran 8% slower than the 16-row kernel), so
 // S is formed by both halves; against separate dK and dV kernels the shared
 // staging measured 3-5% faster on the whole backward, bit-identical.
-// P and dS are rounded to the operand type for the products; gradients are
-// rounded once from float32 accumulators.
+// P and dS / scale are rounded to the operand type for the products (the
+// scale multiplies dQ and dK once, at the end); gradients are rounded once
+// from float32 accumulators.
 #include <math.h>
 
 #include <type_traits>
@@ -353,8 +354,11 @@ __global__ __launch_bounds__(BLK * 2 * (MODE == MODE_DKV ? 2 : 1), MODE == MODE_
               if constexpr (KP) xv = fmaf(DKDV ? kp_own[t] : kpv[jt][rr], kLog2eW, xv);
               float l2, dd = 0.f;
               if constexpr (DKDV) {
+                // a row with nothing visible (lse = -inf: P = 0 there) needs
+                // a key-padding mask: without one every query row of a
+                // visited block sees keys of it (causal: its diagonal key)
                 const float l = l4[jt][rr];
-                l2 = (l == -INFINITY) ? INFINITY : l * kLog2eW;
+                l2 = (KP && l == -INFINITY) ? INFINITY : l * kLog2eW;
                 if constexpr (HDP) dd = d4[jt][rr];
               } else {
                 l2 = lse2_own[t];
@@ -366,7 +370,7 @@ __global__ __launch_bounds__(BLK * 2 * (MODE == MODE_DKV ? 2 : 1), MODE == MODE_
               }
               const float p = __builtin_amdgcn_exp2f(xv - l2);
               s[t][jt][rr] = p;
-              if constexpr (HDP) dp[t][jt][rr] = scale * p * (dp[t][jt][rr] - dd);
+              if constexpr (HDP) dp[t][jt][rr] = p * (dp[t][jt][rr] - dd);  // dS / scale
             }
         if constexpr (M == MODE_DV) tprod(acc, x2, s);  // dV^T += dO^T P
         else tprod(acc, x1, dp);  // dQ^T += K^T dS^T, dK^T += Q^T dS
@@ -383,14 +387,16 @@ __global__ __launch_bounds__(BLK * 2 * (MODE == MODE_DKV ? 2 : 1), MODE == MODE_
     walk(std::integral_constant<int, MODE>{});
   }
 
-  // ---- results: lane (g, li) holds columns 16 nt + 4 g .. of own row 16 t + li
+  // ---- results: lane (g, li) holds columns 16 nt + 4 g .. of own row 16 t + li;
+  // dQ and dK take the scale of dS here, once per element
+  const float osc = (DUAL ? role == 0 : MODE != MODE_DV) ? scale : 1.f;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     u16* pg = (DUAL && role == 1 ? G2 : G) + (zh * Nown + own_lo + 16 * t + li) * D + 4 * g;
 #pragma unroll
     for (int nt = 0; nt < NNT; ++nt)
-      *reinterpret_cast<V4*>(pg + nt * 16) =
-          V4{HT::cvt(acc[t][nt][0]), HT::cvt(acc[t][nt][1]), HT::cvt(acc[t][nt][2]), HT::cvt(acc[t][nt][3])};
+      *reinterpret_cast<V4*>(pg + nt * 16) = V4{HT::cvt(acc[t][nt][0] * osc), HT::cvt(acc[t][nt][1] * osc),
+                                                HT::cvt(acc[t][nt][2] * osc), HT::cvt(acc[t][nt][3] * osc)};
   }
 }
 
