@@ -163,7 +163,8 @@ __global__ __launch_bounds__(BLK * 2 * (MODE == MODE_DKV ? 2 : 1), MODE == MODE_
     for (int t = 0; t < 2; ++t) kp_own[t] = kpmask[(int64_t)z * Nown + own_lo + 16 * t + li];
   }
   // dQ: the tiles' row statistics: lse2 = lse in log2 units (+inf for a row
-  // that saw nothing, so that P = 0 there), D = dO . O, written out
+  // that saw nothing, so that P = 0 there), D = dO . O, written out as -D
+  // (the dK pass starts its dP accumulators from it)
   float lse2_own[2] = {0.f, 0.f}, d_own[2] = {0.f, 0.f};
   if constexpr (!DKDV) {
 #pragma unroll
@@ -180,7 +181,7 @@ __global__ __launch_bounds__(BLK * 2 * (MODE == MODE_DKV ? 2 : 1), MODE == MODE_
         for (int e = 0; e < 8; ++e) acc = fmaf((float)f2[t][q][e], (float)ov[e], acc);
       }
       d_own[t] = rows4_sum(acc);
-      if (g == 0) Dv[row] = d_own[t];
+      if (g == 0) Dv[row] = -d_own[t];
     }
   }
 
@@ -254,17 +255,17 @@ __global__ __launch_bounds__(BLK * 2 * (MODE == MODE_DKV ? 2 : 1), MODE == MODE_
 #pragma unroll
     for (int nt = 0; nt < NNT; ++nt) acc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // out[t][jt] = X rows (16 jt + li of the chunk) . F[t] rows, both tiles
-  // from one read of each X operand
-  auto rprod = [&](f32x4 (&out)[2][2], const unsigned char* xb, const auto& f) {
+  // out[t][jt] = init[t][jt] + X rows (16 jt + li of the chunk) . F[t]
+  // rows, both tiles from one read of each X operand
+  auto rprod = [&](f32x4 (&out)[2][2], const unsigned char* xb, const auto& f, const f32x4 (&init)[2][2]) {
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt) {
       V8 a[NQ];
 #pragma unroll
       for (int q = 0; q < NQ; ++q) a[q] = *reinterpret_cast<const V8*>(xb + 16 * jt * RB + roff[q]);
       __builtin_amdgcn_sched_barrier(0);
-      out[0][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      out[1][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      out[0][jt] = init[0][jt];
+      out[1][jt] = init[1][jt];
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
         out[0][jt] = HT::mfma16(a[q], f[0][q], out[0][jt]);
@@ -331,10 +332,8 @@ __global__ __launch_bounds__(BLK * 2 * (MODE == MODE_DKV ? 2 : 1), MODE == MODE_
           for (int jt = 0; jt < 2; ++jt)
             kpv[jt] = *reinterpret_cast<const f32x4*>(kpmask + (int64_t)z * Noth + o * BLK + rofs + 16 * jt + 4 * g);
         }
-        rprod(s, x1, f1);
-        if constexpr (HDP) rprod(dp, x2, f2);
-        if (ch == 0) issue();
-        // element (own row 16 t + li, other row rofs + 16 jt + 4 g + rr)
+        // element (own row 16 t + li, other row rofs + 16 jt + 4 g + rr);
+        // dK dV: the chunk's lse and -D (read while the row products run)
         f32x4 l4[2], d4[2];
         if constexpr (DKDV) {
           const float* st = &Ss[(kk - k0) & 1][0];
@@ -344,6 +343,19 @@ __global__ __launch_bounds__(BLK * 2 * (MODE == MODE_DKV ? 2 : 1), MODE == MODE_
             if constexpr (HDP) d4[jt] = *reinterpret_cast<const f32x4*>(st + BLK + rofs + 16 * jt + 4 * g);
           }
         }
+        // S starts from 0, dP from -D: the product then holds dP - D
+        const f32x4 zero[2][2] = {};
+        f32x4 nd[2][2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int jt = 0; jt < 2; ++jt) {
+            if constexpr (DKDV) nd[t][jt] = d4[jt];
+            else nd[t][jt] = f32x4{-d_own[t], -d_own[t], -d_own[t], -d_own[t]};
+          }
+        rprod(s, x1, f1, zero);
+        if constexpr (HDP) rprod(dp, x2, f2, nd);
+        if (ch == 0) issue();
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -352,17 +364,15 @@ __global__ __launch_bounds__(BLK * 2 * (MODE == MODE_DKV ? 2 : 1), MODE == MODE_
             for (int rr = 0; rr < 4; ++rr) {
               float xv = s[t][jt][rr] * cs;
               if constexpr (KP) xv = fmaf(DKDV ? kp_own[t] : kpv[jt][rr], kLog2eW, xv);
-              float l2, dd = 0.f;
+              float l2;
               if constexpr (DKDV) {
                 // a row with nothing visible (lse = -inf: P = 0 there) needs
                 // a key-padding mask: without one every query row of a
                 // visited block sees keys of it (causal: its diagonal key)
                 const float l = l4[jt][rr];
                 l2 = (KP && l == -INFINITY) ? INFINITY : l * kLog2eW;
-                if constexpr (HDP) dd = d4[jt][rr];
               } else {
                 l2 = lse2_own[t];
-                dd = d_own[t];
               }
               if (CAUSAL && mask_block) {
                 const int own_r = own_lo + 16 * t + li, oth = o * BLK + rofs + 16 * jt + 4 * g + rr;
@@ -370,7 +380,7 @@ __global__ __launch_bounds__(BLK * 2 * (MODE == MODE_DKV ? 2 : 1), MODE == MODE_
               }
               const float p = __builtin_amdgcn_exp2f(xv - l2);
               s[t][jt][rr] = p;
-              if constexpr (HDP) dp[t][jt][rr] = p * (dp[t][jt][rr] - dd);  // dS / scale
+              if constexpr (HDP) dp[t][jt][rr] *= p;  // (dP - D) P = dS / scale
             }
         if constexpr (M == MODE_DV) tprod(acc, x2, s);  // dV^T += dO^T P
         else tprod(acc, x1, dp);  // dQ^T += K^T dS^T, dK^T += Q^T dS
