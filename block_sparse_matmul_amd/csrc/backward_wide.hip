@@ -17,31 +17,27 @@
 //    whose 16-byte chunks are XOR-swizzled by row, the layout of the 16-bit
 //    forward: row reads (16 bytes a lane) and transposing reads
 //    (ds_read_b64_tr_b16) are both free of bank conflicts;
-//  * each block moves in two halves; a half is fetched as soon as every
-//    wave is done with the half it replaces, and lands while the other
-//    half is computed (one barrier per half). The fetch is issued after the
-//    first chunk's row products, so that its LDS writes do not queue ahead
-//    of their reads, and every operand of a product is requested before
-//    its first MFMA (scheduling barriers): together 2% faster on
-//    random_b128_bf16 (forward plus backward 4.94 against 5.03 ms).
-// Work of the waves (modes of one template):
-//  * dQ: one workgroup per (batch, head, block row); per 32-key chunk of a
-//    column block: S^T = K Q^T and dP^T = V dO^T (K, V rows from LDS, Q and
-//    dO rows of the wave in registers), P and dS in registers, then
-//    dQ^T += K^T dS^T (K read transposed). It also forms D and writes it.
-//  * dK: per block column; per 32-query chunk of a row block: S = Q K^T and
-//    dP = dO V^T (Q, dO rows from LDS, K and V rows of the wave in
-//    registers), dS with the chunk's lse and D, then dK^T += Q^T dS (Q read
-//    transposed).
-//  * dV: the same walk; S = Q K^T, P with the chunk's lse, then
-//    dV^T += dO^T P (dO read transposed).
-// Two kernels: dQ, and dK with dV in one workgroup of twice the waves
-// (MODE_DKV), half of them doing the dK work and half the dV work on the
-// same staged blocks of Q and dO. A wave holding both accumulators (32 rows
-// x d x 2 floats) would need more than the 256 registers of two waves per
-// SIMD (at one wave per SIMD it ran 8% slower than the 16-row kernel), so
-// S is formed by both halves; against separate dK and dV kernels the shared
-// staging measured 3-5% faster on the whole backward, bit-identical.
+//  * each block moves in two halves with one barrier per half; a half is
+//    fetched as soon as every wave is done with the slot it refills, after
+//    the first chunk's row products (so that its LDS writes do not queue
+//    ahead of their reads), and every operand of a product is requested
+//    before its first MFMA (scheduling barriers).
+// Two kernels:
+//  * dQ (k_bwd_wide): one workgroup per (batch, head, block row); per
+//    32-key chunk of a column block: S^T = K Q^T and dP^T - D = V dO^T - D
+//    (K, V rows from LDS, Q and dO rows of the wave in registers), P and
+//    dS in registers, then dQ^T += K^T dS^T (K read transposed). It also
+//    forms D and writes -D to the workspace.
+//  * dK and dV (k_bwd_dkv_pipe): one workgroup per (batch, head, block
+//    column) with two groups of waves on the same 32-key tiles. The dV
+//    waves form S and P once per 32-query chunk, hand P to the dK waves
+//    through LDS and accumulate dV^T += dO^T P; the dK waves run one
+//    staged half behind: dP - D, dS, dK^T += Q^T dS. S is formed once per
+//    block (14 b^2 d executed over both kernels instead of 16): a wave
+//    holding both accumulators would need more than the 256 registers of
+//    two waves per SIMD, and handing P over with a barrier per chunk
+//    measured no faster; running the dK waves a half behind lets the one
+//    barrier per half order the hand-over.
 // P and dS / scale are rounded to the operand type for the products (the
 // scale multiplies dQ and dK once, at the end); gradients are rounded once
 // from float32 accumulators.
@@ -70,31 +66,23 @@ __device__ __forceinline__ int swz(int r) {
   else return ((r >> 1) ^ r) & 7;
 }
 
-enum { MODE_DQ = 0, MODE_DK = 1, MODE_DV = 2, MODE_DKV = 3 };
-
 // KP: a key-padding mask kpmask [Z][keys] (additive, natural-log units)
 // joins the scores as x = s |c| + log2(e) kp, the forward's form; a dense
 // attention mask takes the 16-row kernels (read once more per pass here).
-//
-// MODE_DKV: dK and dV in one workgroup of twice the waves, the first half
-// accumulating dK (the dK mode's work), the second dV (the dV mode's); the
-// two share each staged block of Q and dO, so the column's blocks are
-// staged once instead of twice.
-template <typename E, int BLK, int D, bool CAUSAL, int MODE, bool KP = false>
-__global__ __launch_bounds__(BLK * 2 * (MODE == MODE_DKV ? 2 : 1), MODE == MODE_DKV ? 1 : 2) void k_bwd_wide(
+
+// ---- dQ: own rows are the wave's 32 queries, the walk goes over the
+// block row's key blocks (K and V staged)
+template <typename E, int BLK, int D, bool CAUSAL, bool KP>
+__global__ __launch_bounds__(BLK * 2, 2) void k_bwd_wide(
     const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx, const int32_t* __restrict__ order,
     const int32_t* __restrict__ order_h, int grouped, const u16* __restrict__ Q, const u16* __restrict__ K,
     const u16* __restrict__ V, const u16* __restrict__ O, const u16* __restrict__ dO, u16* __restrict__ G,
     const float* __restrict__ lse, float* __restrict__ Dv, int Z, int H, int n_own, int n_oth, float c,
-    float scale, const float* __restrict__ kpmask = nullptr, u16* __restrict__ G2 = nullptr) {
-  constexpr bool DKDV = MODE != MODE_DQ;  // own rows are keys (block columns walked)
-  constexpr bool DUAL = MODE == MODE_DKV;
-  constexpr bool HASDP = MODE != MODE_DV;  // dP (and D) needed by some wave
+    float scale, const float* __restrict__ kpmask) {
   using HT = H16<E>;
   using V8 = typename HT::V8;
   using V4 = typename HT::V4;
-  constexpr int NWR = BLK / 32;             // waves per role (32 own rows each)
-  constexpr int NW = DUAL ? 2 * NWR : NWR;  // waves of the workgroup
+  constexpr int NW = BLK / 32;       // waves (32 own rows each)
   constexpr int NQ = D / 32;         // 8-element fragments per row and lane
   constexpr int NNT = D / 16;        // 16-column tiles of a gradient
   constexpr int RB = 2 * D;          // bytes per row
@@ -107,11 +95,8 @@ __global__ __launch_bounds__(BLK * 2 * (MODE == MODE_DKV ? 2 : 1), MODE == MODE_
   static_assert(NIP >= 1 && PB % (1024 * NW) == 0, "whole DMA instructions per wave");
   static_assert(NCH >= 1, "blocks of 64 or 128");
 
-  __shared__ __attribute__((aligned(16))) unsigned char X1s[BLK * RB];  // K (dQ) or Q (dK dV)
-  __shared__ __attribute__((aligned(16))) unsigned char X2s[BLK * RB];  // V (dQ) or dO (dK dV)
-  // dK dV: lse and D of the row block's queries, fetched with its first
-  // half (one DMA instruction of wave 0), two blocks' worth by parity
-  __shared__ __attribute__((aligned(16))) float Ss[DKDV ? 2 : 1][DKDV ? 256 : 4];
+  __shared__ __attribute__((aligned(16))) unsigned char X1s[BLK * RB];  // K
+  __shared__ __attribute__((aligned(16))) unsigned char X2s[BLK * RB];  // V
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -129,60 +114,49 @@ __global__ __launch_bounds__(BLK * 2 * (MODE == MODE_DKV ? 2 : 1), MODE == MODE_
   }
   const int h = hu / n_own, u = hu % n_own;
   int k0 = ptr[hu], k1 = ptr[hu + 1];
-  if constexpr (CAUSAL) trim_causal<DKDV>(idx, u, k0, k1);
+  if constexpr (CAUSAL) trim_causal<false>(idx, u, k0, k1);
   const int64_t zh = (int64_t)z * H + h;
   const int64_t Nown = (int64_t)n_own * BLK, Noth = (int64_t)n_oth * BLK;
-  const int64_t Nq = DKDV ? Noth : Nown;
-  // DUAL: role 0 (the first NWR waves) accumulates dK, role 1 dV
-  const int role = DUAL ? wave / NWR : (MODE == MODE_DV ? 1 : 0);
-  const int own_lo = u * BLK + (wave % NWR) * 32;  // first own row of this wave
+  const int own_lo = u * BLK + wave * 32;  // first own row of this wave
 
-  // ---- the wave's own rows (two tiles) as B fragments: F1 = Q (dQ) or K
-  // (dK dV) with the sign of scale*log2(e) folded in (exact), F2 = dO or V
+  // ---- the wave's own rows (two tiles) as B fragments: F1 = Q with the
+  // sign of scale*log2(e) folded in (exact), F2 = dO
   const float sgn = c > 0.f ? 1.f : (c < 0.f ? -1.f : 0.f);
   const float cs = (c == 0.f) ? 1.f : fabsf(c);
-  V8 f1[2][NQ], f2[2][HASDP ? NQ : 1];
+  V8 f1[2][NQ], f2[2][NQ];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const u16* p1 = (DKDV ? K : Q) + (zh * Nown + own_lo + 16 * t + li) * D + 8 * g;
-    const u16* p2 = (DKDV ? V : dO) + (zh * Nown + own_lo + 16 * t + li) * D + 8 * g;
+    const u16* p1 = Q + (zh * Nown + own_lo + 16 * t + li) * D + 8 * g;
+    const u16* p2 = dO + (zh * Nown + own_lo + 16 * t + li) * D + 8 * g;
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       f1[t][q] = *reinterpret_cast<const V8*>(p1 + 32 * q);
-      if (HASDP && role == 0) f2[t][q] = *reinterpret_cast<const V8*>(p2 + 32 * q);
+      f2[t][q] = *reinterpret_cast<const V8*>(p2 + 32 * q);
       if (sgn != 1.f) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) f1[t][q][e] = HT::cvt((float)f1[t][q][e] * sgn);
       }
     }
   }
-  // dK dV with a key-padding mask: the value of each tile's key (own row)
-  float kp_own[2] = {0.f, 0.f};
-  if constexpr (KP && DKDV) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t) kp_own[t] = kpmask[(int64_t)z * Nown + own_lo + 16 * t + li];
-  }
-  // dQ: the tiles' row statistics: lse2 = lse in log2 units (+inf for a row
+  // the tiles' row statistics: lse2 = lse in log2 units (+inf for a row
   // that saw nothing, so that P = 0 there), D = dO . O, written out as -D
   // (the dK pass starts its dP accumulators from it)
-  float lse2_own[2] = {0.f, 0.f}, d_own[2] = {0.f, 0.f};
-  if constexpr (!DKDV) {
+  float lse2_own[2], d_own[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int64_t row = zh * Nq + own_lo + 16 * t + li;
-      const float l = lse[row];
-      lse2_own[t] = (l == -INFINITY) ? INFINITY : l * kLog2eW;
-      const u16* po = O + row * D + 8 * g;
-      float acc = 0.f;
+  for (int t = 0; t < 2; ++t) {
+    const int64_t row = zh * Nown + own_lo + 16 * t + li;
+    const float l = lse[row];
+    lse2_own[t] = (l == -INFINITY) ? INFINITY : l * kLog2eW;
+    const u16* po = O + row * D + 8 * g;
+    float acc = 0.f;
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        const V8 ov = *reinterpret_cast<const V8*>(po + 32 * q);
+    for (int q = 0; q < NQ; ++q) {
+      const V8 ov = *reinterpret_cast<const V8*>(po + 32 * q);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc = fmaf((float)f2[t][q][e], (float)ov[e], acc);
-      }
-      d_own[t] = rows4_sum(acc);
-      if (g == 0) Dv[row] = -d_own[t];
+      for (int e = 0; e < 8; ++e) acc = fmaf((float)f2[t][q][e], (float)ov[e], acc);
     }
+    d_own[t] = rows4_sum(acc);
+    if (g == 0) Dv[row] = -d_own[t];
   }
 
   // ---- DMA: instruction i of this wave moves rows (wave + NW i) * RPI .. of
@@ -197,34 +171,15 @@ __global__ __launch_bounds__(BLK * 2 * (MODE == MODE_DKV ? 2 : 1), MODE == MODE_
   }
   const int d_even = (wave & 1) ? dofs[1] : dofs[0];
   const int d_odd = (wave & 1) ? dofs[0] : dofs[1];
-  // the other side's matrices and (dK dV) its row statistics for this
-  // (batch, head) as raw buffer resources (the launch checks that they fit
-  // in 32-bit offsets): each transfer takes a scalar base and offset and a
-  // 32-bit per-lane offset
+  // K and V of this (batch, head) as raw buffer resources (the launch
+  // checks that they fit in 32-bit offsets): each transfer takes a scalar
+  // base and offset and a 32-bit per-lane offset
   const __amdgpu_buffer_rsrc_t x1res = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<u16*>((DKDV ? Q : K) + zh * Noth * D), 0, (int)(unsigned)(Noth * RB), kRsrcWord3W);
+      const_cast<u16*>(K + zh * Noth * D), 0, (int)(unsigned)(Noth * RB), kRsrcWord3W);
   const __amdgpu_buffer_rsrc_t x2res = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<u16*>((DKDV ? dO : V) + zh * Noth * D), 0, (int)(unsigned)(Noth * RB), kRsrcWord3W);
-  const __amdgpu_buffer_rsrc_t lres =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(lse + zh * Nq), 0, (int)(unsigned)(Nq * 4), kRsrcWord3W);
-  const __amdgpu_buffer_rsrc_t dres =
-      __builtin_amdgcn_make_buffer_rsrc(Dv + zh * Nq, 0, (int)(unsigned)(Nq * 4), kRsrcWord3W);
-  auto dma_half = [&](int o, int x, int par) {
+      const_cast<u16*>(V + zh * Noth * D), 0, (int)(unsigned)(Noth * RB), kRsrcWord3W);
+  auto dma_half = [&](int o, int x) {
     const unsigned base = (unsigned)(o * BLK + x * HALF) * (unsigned)RB;
-    if constexpr (DKDV) {
-      if (x == 0 && wave == 0) {
-        // lanes 0 .. BLK/4 - 1: 16-byte chunks of lse; the next BLK/4: of D;
-        // lanes past those (blocks of 64) repeat D's last chunk into the
-        // unused tail of the buffer
-        const int ch = lane < BLK / 2 ? lane : BLK / 2 - 1;
-        const unsigned qofs = (unsigned)(o * BLK) * 4u;
-        if (ch < BLK / 4)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(lres, (lds_u8w*)(&Ss[par][0]), 16, 16u * ch, qofs, 0, 0);
-        else
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(dres, (lds_u8w*)(&Ss[par][0]), 16, 16u * (ch - BLK / 4), qofs, 0,
-                                                   0);
-      }
-    }
 #pragma unroll
     for (int i = 0; i < NIP; ++i) {
       const int I = wave + NW * i;  // uniform
@@ -277,7 +232,7 @@ __global__ __launch_bounds__(BLK * 2 * (MODE == MODE_DKV ? 2 : 1), MODE == MODE_
   // 32 rows of the chunk in the score-register layout (w[t][jt][rr]: row
   // 16 jt + 4 g + rr), rounded to the operand type; both tiles from one
   // pair of transposing reads
-  auto tprod = [&](f32x4 (&acc)[2][NNT], const unsigned char* xb, const f32x4 (&w)[2][2]) {
+  auto tprod = [&](const unsigned char* xb, const f32x4 (&w)[2][2]) {
     V8 pb[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -298,12 +253,17 @@ __global__ __launch_bounds__(BLK * 2 * (MODE == MODE_DKV ? 2 : 1), MODE == MODE_
     }
   };
 
-  if (k0 < k1) dma_half(idx[k0], 0, 0);
-  auto walk = [&](auto mode_c) {
-    constexpr int M = decltype(mode_c)::value;
-    constexpr bool HDP = M != MODE_DV;
+  // S starts from 0, dP from -D: the product then holds dP - D
+  const f32x4 zero[2][2] = {};
+  f32x4 nd[2][2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt) nd[t][jt] = f32x4{-d_own[t], -d_own[t], -d_own[t], -d_own[t]};
+
+  if (k0 < k1) dma_half(idx[k0], 0);
   for (int kk = k0; kk < k1; ++kk) {
-    const int o = idx[kk];  // the other side's block
+    const int o = idx[kk];  // the key block
     // causal: the diagonal block holds keys after queries (every wave of
     // the workgroup computes on it: each has some pair on or below the
     // diagonal)
@@ -314,48 +274,27 @@ __global__ __launch_bounds__(BLK * 2 * (MODE == MODE_DKV ? 2 : 1), MODE == MODE_
       // is done with the half about to be refetched
       __builtin_amdgcn_s_waitcnt(kVmcntZero);
       __syncthreads();
-      auto issue = [&]() {
-        if (x == 0) dma_half(o, 1, 0);
-        else if (kk + 1 < k1) dma_half(idx[kk + 1], 0, (kk + 1 - k0) & 1);
-      };
 #pragma unroll
       for (int ch = 0; ch < NCH; ++ch) {
         const int rofs = x * HALF + 32 * ch;  // first row of the chunk within the block
         const unsigned char* x1 = X1s + rofs * RB;
         const unsigned char* x2 = X2s + rofs * RB;
         f32x4 s[2][2], dp[2][2];
-        // dQ with a key-padding mask: the values of the chunk's keys (read
+        // with a key-padding mask: the values of the chunk's keys (read
         // while the row products run)
-        f32x4 kpv[KP && !DKDV ? 2 : 1];
-        if constexpr (KP && !DKDV) {
+        f32x4 kpv[KP ? 2 : 1];
+        if constexpr (KP) {
 #pragma unroll
           for (int jt = 0; jt < 2; ++jt)
             kpv[jt] = *reinterpret_cast<const f32x4*>(kpmask + (int64_t)z * Noth + o * BLK + rofs + 16 * jt + 4 * g);
         }
-        // element (own row 16 t + li, other row rofs + 16 jt + 4 g + rr);
-        // dK dV: the chunk's lse and -D (read while the row products run)
-        f32x4 l4[2], d4[2];
-        if constexpr (DKDV) {
-          const float* st = &Ss[(kk - k0) & 1][0];
-#pragma unroll
-          for (int jt = 0; jt < 2; ++jt) {
-            l4[jt] = *reinterpret_cast<const f32x4*>(st + rofs + 16 * jt + 4 * g);
-            if constexpr (HDP) d4[jt] = *reinterpret_cast<const f32x4*>(st + BLK + rofs + 16 * jt + 4 * g);
-          }
-        }
-        // S starts from 0, dP from -D: the product then holds dP - D
-        const f32x4 zero[2][2] = {};
-        f32x4 nd[2][2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int jt = 0; jt < 2; ++jt) {
-            if constexpr (DKDV) nd[t][jt] = d4[jt];
-            else nd[t][jt] = f32x4{-d_own[t], -d_own[t], -d_own[t], -d_own[t]};
-          }
         rprod(s, x1, f1, zero);
-        if constexpr (HDP) rprod(dp, x2, f2, nd);
-        if (ch == 0) issue();
+        rprod(dp, x2, f2, nd);
+        if (ch == 0) {
+          if (x == 0) dma_half(o, 1);
+          else if (kk + 1 < k1) dma_half(idx[kk + 1], 0);
+        }
+        // element (query 16 t + li, key rofs + 16 jt + 4 g + rr)
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -363,46 +302,343 @@ __global__ __launch_bounds__(BLK * 2 * (MODE == MODE_DKV ? 2 : 1), MODE == MODE_
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
               float xv = s[t][jt][rr] * cs;
-              if constexpr (KP) xv = fmaf(DKDV ? kp_own[t] : kpv[jt][rr], kLog2eW, xv);
-              float l2;
-              if constexpr (DKDV) {
-                // a row with nothing visible (lse = -inf: P = 0 there) needs
-                // a key-padding mask: without one every query row of a
-                // visited block sees keys of it (causal: its diagonal key)
-                const float l = l4[jt][rr];
-                l2 = (KP && l == -INFINITY) ? INFINITY : l * kLog2eW;
-              } else {
-                l2 = lse2_own[t];
-              }
+              if constexpr (KP) xv = fmaf(kpv[jt][rr], kLog2eW, xv);
               if (CAUSAL && mask_block) {
                 const int own_r = own_lo + 16 * t + li, oth = o * BLK + rofs + 16 * jt + 4 * g + rr;
-                if (DKDV ? (own_r > oth) : (oth > own_r)) xv = -INFINITY;
+                if (oth > own_r) xv = -INFINITY;
               }
-              const float p = __builtin_amdgcn_exp2f(xv - l2);
-              s[t][jt][rr] = p;
-              if constexpr (HDP) dp[t][jt][rr] *= p;  // (dP - D) P = dS / scale
+              const float p = __builtin_amdgcn_exp2f(xv - lse2_own[t]);
+              dp[t][jt][rr] *= p;  // (dP - D) P = dS / scale
             }
-        if constexpr (M == MODE_DV) tprod(acc, x2, s);  // dV^T += dO^T P
-        else tprod(acc, x1, dp);  // dQ^T += K^T dS^T, dK^T += Q^T dS
+        tprod(x1, dp);  // dQ^T += K^T dS^T
+      }
+    }
+  }
+
+  // ---- results: lane (g, li) holds columns 16 nt + 4 g .. of own row
+  // 16 t + li; dQ takes the scale of dS here, once per element
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    u16* pg = G + (zh * Nown + own_lo + 16 * t + li) * D + 4 * g;
+#pragma unroll
+    for (int nt = 0; nt < NNT; ++nt)
+      *reinterpret_cast<V4*>(pg + nt * 16) = V4{HT::cvt(acc[t][nt][0] * scale), HT::cvt(acc[t][nt][1] * scale),
+                                                HT::cvt(acc[t][nt][2] * scale), HT::cvt(acc[t][nt][3] * scale)};
+  }
+}
+
+template <typename E, int BLK, int D>
+int launch_dq(const bs_layout* L, const BwdArgs& a, hipStream_t s) {
+  const bool kp = a.kp != nullptr;
+  const dim3 grid(L->H * L->nbr * a.Z), block(BLK * 2);
+  // head-grouped XCD order with rows of similar length, as the 16-row
+  // kernels (two workgroups per CU)
+  const double per_slot = (double)a.Z * (double)L->nnz / (2.0 * L->num_cus);
+  const int grouped = (4.0 * L->max_row_len <= per_slot) ? 1 : 0;
+  const float c = a.scale * kLog2eW;
+#define BSA_BWDQ_LAUNCH(CA, KPM)                                                                                 \
+  hipLaunchKernelGGL((k_bwd_wide<E, BLK, D, CA, KPM>), grid, block, 0, s, L->row_ptr, L->col_idx, L->row_order,  \
+                     L->row_order_h, grouped, (const u16*)a.Q, (const u16*)a.K, (const u16*)a.V, (const u16*)a.O, \
+                     (const u16*)a.dO, (u16*)a.dQ, a.lse, a.Dws, a.Z, L->H, L->nbr, L->nbc, c, a.scale, a.kp)
+  if (a.causal) {
+    if (kp) BSA_BWDQ_LAUNCH(true, true);
+    else BSA_BWDQ_LAUNCH(true, false);
+  } else {
+    if (kp) BSA_BWDQ_LAUNCH(false, true);
+    else BSA_BWDQ_LAUNCH(false, false);
+  }
+#undef BSA_BWDQ_LAUNCH
+  BSA_HIP(hipGetLastError());
+  return BS_OK;
+}
+
+
+// dK and dV in one workgroup with S formed once: the dV waves (second half
+// of the workgroup) form S and P for each 32-row chunk of a staged half of
+// the row block, pass P (rounded to 16 bits) to the dK waves through LDS,
+// and accumulate dV^T += dO^T P; the dK waves run one half behind: dP - D
+// from their V rows and the staged dO rows, dS / scale = P (dP - D), and
+// dK^T += Q^T dS. The staged halves of Q and dO form a ring of three
+// (the dV waves' half, the dK waves' half, the one in flight), P a ring of
+// two, so that one barrier per half orders every hand-over.
+template <typename E, int BLK, int D, bool CAUSAL, bool KP>
+__global__ __launch_bounds__(BLK * 4, 1) void k_bwd_dkv_pipe(
+    const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx, const int32_t* __restrict__ order,
+    const int32_t* __restrict__ order_h, int grouped, const u16* __restrict__ Q, const u16* __restrict__ K,
+    const u16* __restrict__ V, const u16* __restrict__ dO, u16* __restrict__ dK, u16* __restrict__ dVo,
+    const float* __restrict__ lse, const float* __restrict__ Dv, int Z, int H, int n_own, int n_oth, float c,
+    float scale, const float* __restrict__ kpmask) {
+  using HT = H16<E>;
+  using V8 = typename HT::V8;
+  using V4 = typename HT::V4;
+  constexpr int NWR = BLK / 32;     // waves per role (32 own rows each)
+  constexpr int NW = 2 * NWR;       // waves of the workgroup
+  constexpr int NQ = D / 32;
+  constexpr int NNT = D / 16;
+  constexpr int RB = 2 * D;
+  constexpr int CPR = D / 8;
+  constexpr int RPI = 1024 / RB;
+  constexpr int HALF = BLK / 2;
+  constexpr int PB = HALF * RB;      // bytes per half and matrix
+  constexpr int NIP = PB / 1024 / NW;
+  constexpr int NCH = HALF / 32;
+  constexpr int PT = 2048;           // bytes of one wave's P tile of a chunk (32 x 32, 16 bits)
+  static_assert(NIP >= 1 && PB % (1024 * NW) == 0, "whole DMA instructions per wave");
+  __shared__ __attribute__((aligned(16))) unsigned char X1s[3 * PB];  // Q halves, ring of three
+  __shared__ __attribute__((aligned(16))) unsigned char X2s[3 * PB];  // dO halves
+  __shared__ __attribute__((aligned(16))) unsigned char Ps[2 * NCH * NWR * PT];
+  __shared__ __attribute__((aligned(16))) float Ss[2][256];  // lse and -D of a row block, by parity
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int li = lane & 15, g = lane >> 4;
+  int hu, z;
+  if (grouped) {
+    const int unit = xcd_unit(blockIdx.x, gridDim.x);
+    const int zhu = unit / n_own;
+    z = zhu / H;
+    hu = order_h[(zhu % H) * n_own + unit % n_own];
+  } else {
+    hu = order[blockIdx.x / Z];
+    z = blockIdx.x % Z;
+  }
+  const int h = hu / n_own, u = hu % n_own;
+  int k0 = ptr[hu], k1 = ptr[hu + 1];
+  if constexpr (CAUSAL) trim_causal<true>(idx, u, k0, k1);
+  const int n = k1 - k0;
+  const int64_t zh = (int64_t)z * H + h;
+  const int64_t Nown = (int64_t)n_own * BLK, Noth = (int64_t)n_oth * BLK;
+  const int role = wave / NWR;  // 0: dK, 1: dV
+  const int wr = wave % NWR;
+  const int own_lo = u * BLK + wr * 32;
+
+  // own rows as B fragments: K (dV waves, sign of scale*log2(e) folded in)
+  // or V (dK waves)
+  const float sgn = c > 0.f ? 1.f : (c < 0.f ? -1.f : 0.f);
+  const float cs = (c == 0.f) ? 1.f : fabsf(c);
+  V8 fo[2][NQ];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const u16* p1 = (role ? K : V) + (zh * Nown + own_lo + 16 * t + li) * D + 8 * g;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      fo[t][q] = *reinterpret_cast<const V8*>(p1 + 32 * q);
+      if (role == 1 && sgn != 1.f) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) fo[t][q][e] = HT::cvt((float)fo[t][q][e] * sgn);
+      }
+    }
+  }
+  float kp_own[2] = {0.f, 0.f};
+  if constexpr (KP) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) kp_own[t] = kpmask[(int64_t)z * Nown + own_lo + 16 * t + li];
+  }
+
+  // ---- DMA (as k_bwd_wide): instruction i of this wave moves rows
+  // (wave + NW i) * RPI .. of a half
+  int dofs[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int ri = lane / CPR, slot = lane % CPR;
+    dofs[p] = ri * RB + ((slot ^ swz<D>(p * RPI + ri)) * 16);
+  }
+  const int d_even = (wave & 1) ? dofs[1] : dofs[0];
+  const int d_odd = (wave & 1) ? dofs[0] : dofs[1];
+  const __amdgpu_buffer_rsrc_t x1res = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u16*>(Q + zh * Noth * D), 0, (int)(unsigned)(Noth * RB), kRsrcWord3W);
+  const __amdgpu_buffer_rsrc_t x2res = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u16*>(dO + zh * Noth * D), 0, (int)(unsigned)(Noth * RB), kRsrcWord3W);
+  const __amdgpu_buffer_rsrc_t lres =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(lse + zh * Noth), 0, (int)(unsigned)(Noth * 4), kRsrcWord3W);
+  const __amdgpu_buffer_rsrc_t dres =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(Dv + zh * Noth), 0, (int)(unsigned)(Noth * 4), kRsrcWord3W);
+  // half hh of the walk (block k0 + hh / 2, half hh & 1) into ring slot hh % 3
+  auto dma_half = [&](int hh) {
+    const int o = idx[k0 + (hh >> 1)], x = hh & 1, sl = hh % 3;
+    const unsigned base = (unsigned)(o * BLK + x * HALF) * (unsigned)RB;
+    if (x == 0 && wave == 0) {
+      const int ch = lane < BLK / 2 ? lane : BLK / 2 - 1;
+      const unsigned qofs = (unsigned)(o * BLK) * 4u;
+      float* st = &Ss[(hh >> 1) & 1][0];
+      if (ch < BLK / 4)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(lres, (lds_u8w*)st, 16, 16u * ch, qofs, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(dres, (lds_u8w*)st, 16, 16u * (ch - BLK / 4), qofs, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NIP; ++i) {
+      const int I = wave + NW * i;
+      const unsigned off = (unsigned)(((NW * i) & 1) ? d_odd : d_even);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(x1res, (lds_u8w*)(X1s + sl * PB + I * 1024), 16, off,
+                                               base + I * 1024, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(x2res, (lds_u8w*)(X2s + sl * PB + I * 1024), 16, off,
+                                               base + I * 1024, 0, 0);
+    }
+  };
+
+  int roff[NQ], toff[NNT];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) roff[q] = li * RB + (((4 * q + g) ^ swz<D>(li)) * 16);
+  {
+    const int kk = li >> 2, m = li & 3, vr = 4 * g + kk;
+#pragma unroll
+    for (int nt = 0; nt < NNT; ++nt) toff[nt] = vr * RB + (((2 * nt + (m >> 1)) ^ swz<D>(vr)) * 16) + 8 * (m & 1);
+  }
+  f32x4 acc[2][NNT];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int nt = 0; nt < NNT; ++nt) acc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto rprod = [&](f32x4 (&out)[2][2], const unsigned char* xb, const f32x4 (&init)[2][2]) {
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt) {
+      V8 a[NQ];
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) a[q] = *reinterpret_cast<const V8*>(xb + 16 * jt * RB + roff[q]);
+      __builtin_amdgcn_sched_barrier(0);
+      out[0][jt] = init[0][jt];
+      out[1][jt] = init[1][jt];
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        out[0][jt] = HT::mfma16(a[q], fo[0][q], out[0][jt]);
+        out[1][jt] = HT::mfma16(a[q], fo[1][q], out[1][jt]);
+      }
+    }
+  };
+  // acc += X^T (the chunk's 32 rows) . W, W given as 16-bit B fragments
+  auto tprod = [&](const unsigned char* xb, const V8 (&pb)[2]) {
+    V4 a0[NNT], a1[NNT];
+#pragma unroll
+    for (int nt = 0; nt < NNT; ++nt) {
+      a0[nt] = lds_read_tr16_as<V4>(reinterpret_cast<const u16*>(xb + toff[nt]));
+      a1[nt] = lds_read_tr16_as<V4>(reinterpret_cast<const u16*>(xb + 16 * RB + toff[nt]));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int nt = 0; nt < NNT; ++nt) {
+      const V8 a = {a0[nt][0], a0[nt][1], a0[nt][2], a0[nt][3], a1[nt][0], a1[nt][1], a1[nt][2], a1[nt][3]};
+      acc[0][nt] = HT::mfma16(a, pb[0], acc[0][nt]);
+      acc[1][nt] = HT::mfma16(a, pb[1], acc[1][nt]);
+    }
+  };
+  auto pack = [&](const f32x4 (&w)[2][2], V8 (&pb)[2]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      pb[t] = V8{HT::cvt(w[t][0][0]), HT::cvt(w[t][0][1]), HT::cvt(w[t][0][2]), HT::cvt(w[t][0][3]),
+                 HT::cvt(w[t][1][0]), HT::cvt(w[t][1][1]), HT::cvt(w[t][1][2]), HT::cvt(w[t][1][3])};
+  };
+
+  // ---- the walk: step hs, for hs = 0 .. 2n: the dV waves take half hs,
+  // the dK waves half hs - 1; half hs + 1 is fetched during the step
+  const int last = 2 * n;  // halves 0 .. last - 1
+  if (n > 0) dma_half(0);
+  // one loop per role (the role dispatched outside it), so that registers
+  // are allocated for each role's body alone; both meet the same barriers
+  auto walk = [&](auto role_c) {
+  constexpr int ROLE = decltype(role_c)::value;
+  for (int hs = 0; hs <= last && n > 0; ++hs) {
+    __builtin_amdgcn_s_waitcnt(kVmcntZero);
+    __syncthreads();
+    auto issue = [&]() {
+      if (hs + 1 < last) dma_half(hs + 1);
+    };
+    if constexpr (ROLE == 1) {
+      if (hs < last) {
+        const int o = idx[k0 + (hs >> 1)], x = hs & 1;
+        const unsigned char* q1 = X1s + (hs % 3) * PB;
+        const unsigned char* d2 = X2s + (hs % 3) * PB;
+        const float* st = &Ss[(hs >> 1) & 1][0];
+        const bool mask_block = CAUSAL && o == u;
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch) {
+          const int rofs = x * HALF + 32 * ch;  // first row of the chunk within the block
+          f32x4 l4[2];
+#pragma unroll
+          for (int jt = 0; jt < 2; ++jt) l4[jt] = *reinterpret_cast<const f32x4*>(st + rofs + 16 * jt + 4 * g);
+          const f32x4 zero[2][2] = {};
+          f32x4 s[2][2];
+          rprod(s, q1 + 32 * ch * RB, zero);
+          if (ch == 0) issue();
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr) {
+                float xv = s[t][jt][rr] * cs;
+                if constexpr (KP) xv = fmaf(kp_own[t], kLog2eW, xv);
+                const float l = l4[jt][rr];
+                const float l2 = (KP && l == -INFINITY) ? INFINITY : l * kLog2eW;
+                if (CAUSAL && mask_block) {
+                  const int own_r = own_lo + 16 * t + li, oth = o * BLK + rofs + 16 * jt + 4 * g + rr;
+                  if (own_r > oth) xv = -INFINITY;
+                }
+                s[t][jt][rr] = __builtin_amdgcn_exp2f(xv - l2);
+              }
+          V8 pb[2];
+          pack(s, pb);
+          // hand P to the dK wave of the same keys: two 1 KB rows of 16-byte
+          // lane slots
+          unsigned char* pt = Ps + (((hs & 1) * NCH + ch) * NWR + wr) * PT;
+          *reinterpret_cast<V8*>(pt + 16 * lane) = pb[0];
+          *reinterpret_cast<V8*>(pt + 1024 + 16 * lane) = pb[1];
+          tprod(d2 + 32 * ch * RB, pb);  // dV^T += dO^T P
+        }
+      } else {
+        issue();
+      }
+    } else {
+      if (hs >= 1) {
+        const int hp = hs - 1;
+        const int x = hp & 1;
+        const unsigned char* q1 = X1s + (hp % 3) * PB;
+        const unsigned char* d2 = X2s + (hp % 3) * PB;
+        const float* st = &Ss[(hp >> 1) & 1][0];
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch) {
+          const int rofs = x * HALF + 32 * ch;
+          // dP starts from -D: the product then holds dP - D
+          f32x4 nd[2][2];
+#pragma unroll
+          for (int jt = 0; jt < 2; ++jt) {
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(st + BLK + rofs + 16 * jt + 4 * g);
+            nd[0][jt] = d4;
+            nd[1][jt] = d4;
+          }
+          f32x4 dp[2][2];
+          rprod(dp, d2 + 32 * ch * RB, nd);
+          if (ch == 0) issue();
+          const unsigned char* pt = Ps + (((hp & 1) * NCH + ch) * NWR + wr) * PT;
+          const V8 pb0 = *reinterpret_cast<const V8*>(pt + 16 * lane);
+          const V8 pb1 = *reinterpret_cast<const V8*>(pt + 1024 + 16 * lane);
+#pragma unroll
+          for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              dp[0][jt][rr] *= (float)pb0[4 * jt + rr];
+              dp[1][jt][rr] *= (float)pb1[4 * jt + rr];
+            }
+          V8 sb[2];
+          pack(dp, sb);
+          tprod(q1 + 32 * ch * RB, sb);  // dK^T += Q^T dS
+        }
+      } else {
+        issue();
       }
     }
   }
   };
-  // the whole walk for a wave of mode M: the kernel's mode, or with DUAL
-  // the wave's role (both roles meet at the same barriers)
-  if constexpr (DUAL) {
-    if (role == 0) walk(std::integral_constant<int, MODE_DK>{});
-    else walk(std::integral_constant<int, MODE_DV>{});
-  } else {
-    walk(std::integral_constant<int, MODE>{});
-  }
+  if (role == 1) walk(std::integral_constant<int, 1>{});
+  else walk(std::integral_constant<int, 0>{});
 
-  // ---- results: lane (g, li) holds columns 16 nt + 4 g .. of own row 16 t + li;
-  // dQ and dK take the scale of dS here, once per element
-  const float osc = (DUAL ? role == 0 : MODE != MODE_DV) ? scale : 1.f;
+  // ---- results: dK takes the scale of dS here
+  const float osc = role == 0 ? scale : 1.f;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    u16* pg = (DUAL && role == 1 ? G2 : G) + (zh * Nown + own_lo + 16 * t + li) * D + 4 * g;
+    u16* pg = (role == 1 ? dVo : dK) + (zh * Nown + own_lo + 16 * t + li) * D + 4 * g;
 #pragma unroll
     for (int nt = 0; nt < NNT; ++nt)
       *reinterpret_cast<V4*>(pg + nt * 16) = V4{HT::cvt(acc[t][nt][0] * osc), HT::cvt(acc[t][nt][1] * osc),
@@ -410,43 +646,34 @@ __global__ __launch_bounds__(BLK * 2 * (MODE == MODE_DKV ? 2 : 1), MODE == MODE_
   }
 }
 
-template <typename E, int BLK, int D, int MODE>
-int launch_w(const bs_layout* L, const BwdArgs& a, hipStream_t s) {
+template <typename E, int BLK, int D>
+int launch_dkv_pipe(const bs_layout* L, const BwdArgs& a, hipStream_t s) {
   const bool kp = a.kp != nullptr;
-  constexpr bool DKDV = MODE != MODE_DQ;
-  const int n_own = DKDV ? L->nbc : L->nbr, n_oth = DKDV ? L->nbr : L->nbc;
-  const dim3 grid(L->H * n_own * a.Z), block(BLK * 2 * (MODE == MODE_DKV ? 2 : 1));
-  const int32_t* ptr = DKDV ? L->col_ptr : L->row_ptr;
-  const int32_t* idx = DKDV ? L->row_idx : L->col_idx;
-  const int32_t* order = DKDV ? L->col_order : L->row_order;
-  const int32_t* order_h = DKDV ? L->col_order_h : L->row_order_h;
-  // head-grouped XCD order with rows (columns) of similar length, as the
-  // 16-row kernels (two workgroups per CU)
+  const dim3 grid(L->H * L->nbc * a.Z), block(BLK * 4);
   const double per_slot = (double)a.Z * (double)L->nnz / (2.0 * L->num_cus);
-  const int max_len = DKDV ? L->max_col_len : L->max_row_len;
-  const int grouped = (4.0 * max_len <= per_slot) ? 1 : 0;
+  const int grouped = (4.0 * L->max_col_len <= per_slot) ? 1 : 0;
   const float c = a.scale * kLog2eW;
-  u16* g = (u16*)(MODE == MODE_DQ ? a.dQ : (MODE == MODE_DV ? a.dV : a.dK));
-#define BSA_BWDW_LAUNCH(CA, KPM)                                                                                 \
-  hipLaunchKernelGGL((k_bwd_wide<E, BLK, D, CA, MODE, KPM>), grid, block, 0, s, ptr, idx, order, order_h,        \
-                     grouped, (const u16*)a.Q, (const u16*)a.K, (const u16*)a.V, (const u16*)a.O, (const u16*)a.dO, \
-                     g, a.lse, a.Dws, a.Z, L->H, n_own, n_oth, c, a.scale, a.kp, (u16*)a.dV)
+#define BSA_DKVP_LAUNCH(CA, KPM)                                                                                 \
+  hipLaunchKernelGGL((k_bwd_dkv_pipe<E, BLK, D, CA, KPM>), grid, block, 0, s, L->col_ptr, L->row_idx,             \
+                     L->col_order, L->col_order_h, grouped, (const u16*)a.Q, (const u16*)a.K, (const u16*)a.V,    \
+                     (const u16*)a.dO, (u16*)a.dK, (u16*)a.dV, a.lse, a.Dws, a.Z, L->H, L->nbc, L->nbr, c, a.scale, \
+                     a.kp)
   if (a.causal) {
-    if (kp) BSA_BWDW_LAUNCH(true, true);
-    else BSA_BWDW_LAUNCH(true, false);
+    if (kp) BSA_DKVP_LAUNCH(true, true);
+    else BSA_DKVP_LAUNCH(true, false);
   } else {
-    if (kp) BSA_BWDW_LAUNCH(false, true);
-    else BSA_BWDW_LAUNCH(false, false);
+    if (kp) BSA_DKVP_LAUNCH(false, true);
+    else BSA_DKVP_LAUNCH(false, false);
   }
-#undef BSA_BWDW_LAUNCH
+#undef BSA_DKVP_LAUNCH
   BSA_HIP(hipGetLastError());
   return BS_OK;
 }
 
 template <typename E, int BLK, int D>
 int run_w(const bs_layout* L, const BwdArgs& a, hipStream_t s) {
-  if (int rc = launch_w<E, BLK, D, MODE_DQ>(L, a, s)) return rc;  // dQ and D
-  return launch_w<E, BLK, D, MODE_DKV>(L, a, s);                  // dK and dV (reads D)
+  if (int rc = launch_dq<E, BLK, D>(L, a, s)) return rc;  // dQ and -D
+  return launch_dkv_pipe<E, BLK, D>(L, a, s);             // dK and dV (read -D)
 }
 
 template <typename E>
