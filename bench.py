@@ -279,7 +279,8 @@ def run_workload(w, steps, warmup, with_ops=True, with_cpu=True):
             ops["backward"] = {"ms": round(t_fb, 4), "tflops": round(fb / (t_fb * 1e-3) / 1e12, 3),
                                "flops": "10 b^2 d per stored block",
                                "kernels": "fused: dQ over block rows; dK and dV over block columns "
-                                          "(one kernel for both; with 16-bit operands, half its waves each)"}
+                                          "(one kernel for both; with 16-bit operands S is formed once, "
+                                          "half its waves each)"}
             del o, lse, wsd
             ws = (torch.empty((w.Z, L.nnz, w.block, w.block), dtype=torch.float32, device=dev),
                   torch.empty((w.Z, L.nnz, w.block, w.block), dtype=torch.float32, device=dev))
