@@ -213,18 +213,23 @@ __global__ __launch_bounds__(BLK * 2, 2) void k_bwd_wide(
   // out[t][jt] = init[t][jt] + X rows (16 jt + li of the chunk) . F[t]
   // rows, both tiles from one read of each X operand
   auto rprod = [&](f32x4 (&out)[2][2], const unsigned char* xb, const auto& f, const f32x4 (&init)[2][2]) {
+    // the operands of tile 1 are read while tile 0 is multiplied
+    V8 a[2][NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) a[0][q] = *reinterpret_cast<const V8*>(xb + roff[q]);
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt) {
-      V8 a[NQ];
+      if (jt == 0) {
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) a[q] = *reinterpret_cast<const V8*>(xb + 16 * jt * RB + roff[q]);
+        for (int q = 0; q < NQ; ++q) a[1][q] = *reinterpret_cast<const V8*>(xb + 16 * RB + roff[q]);
+      }
       __builtin_amdgcn_sched_barrier(0);
       out[0][jt] = init[0][jt];
       out[1][jt] = init[1][jt];
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
-        out[0][jt] = HT::mfma16(a[q], f[0][q], out[0][jt]);
-        out[1][jt] = HT::mfma16(a[q], f[1][q], out[1][jt]);
+        out[0][jt] = HT::mfma16(a[jt][q], f[0][q], out[0][jt]);
+        out[1][jt] = HT::mfma16(a[jt][q], f[1][q], out[1][jt]);
       }
     }
   };
@@ -493,18 +498,23 @@ __global__ __launch_bounds__(BLK * 4, 1) void k_bwd_dkv_pipe(
     for (int nt = 0; nt < NNT; ++nt) acc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto rprod = [&](f32x4 (&out)[2][2], const unsigned char* xb, const f32x4 (&init)[2][2]) {
+    // the operands of tile 1 are read while tile 0 is multiplied
+    V8 a[2][NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) a[0][q] = *reinterpret_cast<const V8*>(xb + roff[q]);
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt) {
-      V8 a[NQ];
+      if (jt == 0) {
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) a[q] = *reinterpret_cast<const V8*>(xb + 16 * jt * RB + roff[q]);
+        for (int q = 0; q < NQ; ++q) a[1][q] = *reinterpret_cast<const V8*>(xb + 16 * RB + roff[q]);
+      }
       __builtin_amdgcn_sched_barrier(0);
       out[0][jt] = init[0][jt];
       out[1][jt] = init[1][jt];
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
-        out[0][jt] = HT::mfma16(a[q], fo[0][q], out[0][jt]);
-        out[1][jt] = HT::mfma16(a[q], fo[1][q], out[1][jt]);
+        out[0][jt] = HT::mfma16(a[jt][q], fo[0][q], out[0][jt]);
+        out[1][jt] = HT::mfma16(a[jt][q], fo[1][q], out[1][jt]);
       }
     }
   };
