@@ -411,8 +411,9 @@ def attention_backward_fused(L: Layout, q, k, v, o, lse, do, scale: Optional[flo
     log-sum-exp lse (attention(..., return_lse=True)) and the output
     gradient do, on the fused backward kernels (S and P never reach
     memory). Same scale, causal flag and masks as the forward.
-    workspace: optional float32 [Z, H, Nq] tensor (the D = rowsum(do * o)
-    buffer). out: optional (dq, dk, dv) tensors to write.
+    workspace: optional float32 [Z, H, Nq] tensor, scratch for the rows'
+    D = rowsum(do * o) terms (its contents afterwards are unspecified).
+    out: optional (dq, dk, dv) tensors to write.
     noalloc: call bs_attention_bwd_noalloc, which keeps D in the library's
     static device buffer (at most 2^21 query rows) and allocates nothing;
     with `out` given this call allocates no device memory at all."""

@@ -297,12 +297,14 @@ int bs_attention_backward_masked(bs_layout_t L, const void* Q, const void* K,
    x = scale*S + masks and D = rowsum(dO * O) (which equals rowsum(P * dP)),
    P = exp(x - lse), dS = scale * P * (dO V^T - D), dQ = dS K, dK = dS^T Q,
    dV = P^T dO (the same gradient as bs_attention_backward_masked). Two
-   kernels: one over block rows (dQ, and D into ws_d), one over block
-   columns (dK, dV). Q, O, dO, dQ: [Z][H][nbr*b][d]; K, V, dK, dV:
+   kernels: one over block rows (dQ, and the rows' D terms into ws_d), one
+   over block columns (dK, dV). Q, O, dO, dQ: [Z][H][nbr*b][d]; K, V, dK, dV:
    [Z][H][nbc*b][d], all of dtype dt; d in {64, 128}. lse: float32
    [Z][H][nbr*b] as bs_attention_fwd wrote it, with the same scale, flags
-   and masks. ws_d: caller-owned float32 workspace of Z*H*nbr*b elements.
-   16-bit types: P and dS are rounded to dt for the products. */
+   and masks. ws_d: caller-owned float32 workspace of Z*H*nbr*b elements
+   (its contents afterwards are unspecified). 16-bit types: P and dS (or
+   dS / scale, the scale then applied to dQ and dK) are rounded to dt for
+   the products. */
 int bs_attention_bwd(bs_layout_t L, const void* Q, const void* K,
                      const void* V, const void* O, const float* lse,
                      const void* dO, void* dQ, void* dK, void* dV,

@@ -288,6 +288,35 @@ def test_fused_backward_full_size(idx):
             assert err <= tol, (name, pair, err)
 
 
+@pytest.mark.parametrize("b", [64, 128])
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_fused_backward_16bit_walks_of_zero_and_one_block(b, dt):
+    """The 16-bit kernels with nothing to walk (every column and row empty:
+    zero gradients in outputs prefilled with NaN) and with one stored block
+    per row and column (the dK dV pipeline's shortest walk: two staged
+    halves, the dK waves' half one step behind)."""
+    d, H, nb, Z = 64, 2, 3, 1
+    announce("fused backward 16-bit short walks", b, dt)
+    q, k, v, do = (to_dev(t) for t in _t([(Z, H, nb * b, d)] * 4, 460 + b, dt))
+    empty = np.zeros((H, nb, nb), np.uint8)
+    L = bsa.Layout(torch.from_numpy(empty), b)
+    o, lse = bsa.attention(L, q, k, v, 0.125, return_lse=True)
+    nan = lambda: torch.full_like(q, float("nan"))
+    for g in bsa.attention_backward_fused(L, q, k, v, o, lse, do, 0.125, out=(nan(), nan(), nan())):
+        assert torch.all(g == 0)
+    perm = np.zeros((H, nb, nb), np.uint8)
+    perm[0, np.arange(nb), (np.arange(nb) + 1) % nb] = 1  # one block per row and column
+    perm[1, np.arange(nb), np.arange(nb)] = 1
+    for causal in (False, True):
+        lay = perm if not causal else np.ascontiguousarray(np.broadcast_to(perm[1], perm.shape))
+        L = bsa.Layout(torch.from_numpy(lay), b)
+        o, lse = bsa.attention(L, q, k, v, 0.125, causal, return_lse=True)
+        grads = bsa.attention_backward_fused(L, q, k, v, o, lse, do, 0.125, causal, out=(nan(), nan(), nan()))
+        refs = oracle.attention_backward_dense(*(t.cpu() for t in (q, k, v, do)), lay, b, 0.125, causal)
+        for name, got, ref in zip(("dq", "dk", "dv"), grads, refs):
+            assert max_abs(f64(got), ref) <= _grad_tol(dt, ref), (name, causal)
+
+
 def test_fused_backward_empty_layout_and_empty_batch():
     """No stored block: zero gradients (and -inf lse); Z = 0: nothing to do."""
     b, d, H, nb = 32, 64, 2, 3
