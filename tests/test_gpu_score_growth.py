@@ -6,6 +6,8 @@ against that max reach 2^33 (accepted) or 2^64 and beyond, up to infinity
 scores of block 1 exceed block 0's by about f d scale log2(e) log2 units
 (f = 2: 33; f = 5: 82; f = 40: 650). The expected values are the oracle's
 float64 softmax; the bars are the 16-bit ones of the other parity tests.
+The fp8 score operands (Q, K in OCP FP8 E4M3, V and O bf16) take the same
+path after the score product; the oracle runs on the fp8 values.
 """
 import numpy as np
 import pytest
@@ -19,10 +21,13 @@ import block_sparse_matmul_amd as bsa
 pytestmark = pytest.mark.gpu
 
 DT = {"bf16": torch.bfloat16, "f16": torch.float16}
+F8 = torch.float8_e4m3fn
 
 
-@pytest.mark.parametrize("dt", ["bf16", "f16"])
-@pytest.mark.parametrize("b", [64, 128])
+CASES = [(dt, b) for dt in ("bf16", "f16") for b in (64, 128)] + [("f8", 128)]
+
+
+@pytest.mark.parametrize("dt,b", CASES)
 @pytest.mark.parametrize("f", [2.0, 5.0, 40.0])
 @pytest.mark.parametrize("causal", [False, True])
 def test_scores_far_above_the_running_max(dt, b, f, causal):
@@ -36,7 +41,10 @@ def test_scores_far_above_the_running_max(dt, b, f, causal):
     k = 0.01 * torch.randn((Z, H, N, d), generator=g)
     k[:, :, b:2 * b] = f * u  # block 1
     v = torch.randn((Z, H, N, d), generator=g)
-    q, k, v = (t.to(DT[dt]) for t in (q, k, v))
+    if dt == "f8":
+        q, k, v = q.to(F8), k.to(F8), v.to(torch.bfloat16)
+    else:
+        q, k, v = (t.to(DT[dt]) for t in (q, k, v))
     lay = np.zeros((H, nb, nb), np.uint8)
     lay[:, :, 0] = 1          # every row sees block 0 first
     lay[:, 1:, 1] = 1         # rows 1, 2 then block 1 (on or below the diagonal)
@@ -48,6 +56,6 @@ def test_scores_far_above_the_running_max(dt, b, f, causal):
     ref_o = oracle.attention_dense(q, k, v, lay, b, scale, causal)
     ref_l = oracle.attention_lse(q, k, lay, b, scale, causal)
     assert torch.isfinite(o).all()
-    assert max_abs(f64(o), ref_o) <= TOL[dt] * max(1.0, float(np.abs(ref_o).max()))
-    bar = 4e-3 if dt == "bf16" else 1e-3
+    assert max_abs(f64(o), ref_o) <= TOL["bf16" if dt == "f8" else dt] * max(1.0, float(np.abs(ref_o).max()))
+    bar = 1e-3 if dt == "f16" else 4e-3
     assert max_abs(f64(lse), ref_l) <= bar * max(1.0, float(np.abs(ref_l).max()))
